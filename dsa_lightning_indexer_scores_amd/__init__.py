@@ -1,0 +1,258 @@
+"""Thin Python binding of libdsa.so (DSA lightning indexer -> top-k -> sparse MLA
+attention with IndexShare, hand-written HIP kernels for gfx950).
+
+Argument marshalling only: every step of the path runs in the library's kernels.
+PyTorch provides device memory and the current stream.  There is no CPU fallback:
+if libdsa.so has not been built (``python -m dsa_lightning_indexer_scores_amd.build_lib``)
+or no GPU is present, the calls raise.
+
+Function names follow include/dsa.h.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
+    "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
+    "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
+    "sparse_attn", "layer_group", "Workspace",
+]
+
+DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
+DSA_OP_TOPK, DSA_OP_INDEXER_TOPK, DSA_OP_SPARSE_ATTN, DSA_OP_LAYER_GROUP = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def library_path():
+    return os.path.join(_HERE, "libdsa.so")
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+class _IndexerIn(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("q_scale", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("w", ctypes.c_void_p), ("H_I", ctypes.c_int32),
+                ("d_I", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _AttnIn(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("k_row_stride", ctypes.c_int64),
+                ("v", ctypes.c_void_p), ("v_row_stride", ctypes.c_int64), ("out", ctypes.c_void_p),
+                ("lse", ctypes.c_void_p), ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+                ("Dqk", ctypes.c_int32), ("Dv", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load libdsa.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with "
+                           "`python -m dsa_lightning_indexer_scores_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+    lib.dsa_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.dsa_workspace_size.restype = sz
+    lib.dsa_indexer_scores.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, vp]
+    lib.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_topk.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, i32, vp, vp, sz, vp]
+    lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
+    lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
+                                    i32, i32, vp, vp, sz, vp]
+    lib.dsa_status_string.argtypes = [i32]
+    lib.dsa_status_string.restype = ctypes.c_char_p
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_layer_group"):
+        getattr(lib, fn).restype = i32
+    _lib = lib
+    return lib
+
+
+def status_string(status):
+    return load_library().dsa_status_string(int(status)).decode()
+
+
+def workspace_size(op, dtype, B, Lq, Lk, k, heads=0):
+    return int(load_library().dsa_workspace_size(op, dtype, B, Lq, Lk, k, heads))
+
+
+def _check(fn, st):
+    if st != 0:
+        raise DsaError(fn, st)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous and on the GPU")
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return DSA_F32
+    if t.dtype == torch.bfloat16:
+        return DSA_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DSA_FP8_E4M3
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+class Workspace:
+    """A growable device workspace (allocated by torch, handed to the library)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes, device):
+        if nbytes == 0:
+            return None, 0
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf, self.buf.numel()
+
+
+def _indexer_struct(q, k, w, q_scale, k_scale):
+    _require_cuda(q, k, w, q_scale, k_scale)
+    dt = _dtype_code(q)
+    B, Lq, H_I, d_I = q.shape
+    s = _IndexerIn(_ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), H_I, d_I, dt)
+    return s, B, Lq, k.shape[1]
+
+
+def indexer_scores(q, k, w, q_scale=None, k_scale=None, out=None, stream=None):
+    """Materialised scores [B, Lq, Lk] fp32 (-inf for non-causal keys)."""
+    s, B, Lq, Lk = _indexer_struct(q, k, w, q_scale, k_scale)
+    if out is None:
+        out = torch.empty((B, Lq, Lk), dtype=torch.float32, device=q.device)
+    _check("dsa_indexer_scores", load_library().dsa_indexer_scores(
+        ctypes.byref(s), B, Lq, Lk, _ptr(out), _stream(stream)))
+    return out
+
+
+def topk(scores, k, n_valid=None, return_vals=False, stream=None):
+    """Deterministic top-k over the rows of a 2-D (or batched) fp32 score tensor."""
+    _require_cuda(scores, n_valid)
+    n = scores.shape[-1]
+    rows = scores.numel() // n
+    idx = torch.empty(scores.shape[:-1] + (k,), dtype=torch.int32, device=scores.device)
+    vals = torch.empty(idx.shape, dtype=torch.float32, device=scores.device) if return_vals else None
+    _check("dsa_topk", load_library().dsa_topk(
+        _ptr(scores), n, rows, n, _ptr(n_valid), k, _ptr(idx), _ptr(vals), None, 0, _stream(stream)))
+    return (idx, vals) if return_vals else idx
+
+
+def indexer_topk(q, k, w, topk_k, q_scale=None, k_scale=None, ws=None, out=None, stream=None):
+    """Fused indexer + top-k: idx [B, Lq, topk_k] int32."""
+    s, B, Lq, Lk = _indexer_struct(q, k, w, q_scale, k_scale)
+    need = workspace_size(DSA_OP_INDEXER_TOPK, s.dtype, B, Lq, Lk, topk_k)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(need, q.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=q.device)
+    _check("dsa_indexer_topk", load_library().dsa_indexer_topk(
+        ctypes.byref(s), B, Lq, Lk, topk_k, _ptr(out), _ptr(buf), nbytes, _stream(stream)))
+    return out
+
+
+def _attn_struct(layer, out, lse):
+    q = layer["q"]
+    if "kv" in layer:                        # MLA latent: k = v = kv rows, V = first Dv dims
+        kk = vv = layer["kv"]
+        Hkv, Dqk = 1, q.shape[-1]
+        Dv = layer.get("Dv", 512)
+        ks = vs = kk.shape[-1]
+    else:
+        kk, vv = layer["k"], layer["v"]
+        Hkv, Dqk = kk.shape[-2], kk.shape[-1]
+        Dv = vv.shape[-1]
+        ks, vs = Hkv * Dqk, Hkv * Dv
+    _require_cuda(q, kk, vv, out, lse)
+    H = q.shape[2]
+    return _AttnIn(_ptr(q), _ptr(kk), ks, _ptr(vv), vs, _ptr(out), _ptr(lse), H, Hkv, Dqk, Dv,
+                   float(layer["sm_scale"]), _dtype_code(q), _dtype_code(out)), kk.shape[1], Dv
+
+
+def sparse_attn(layer, idx, idx_q_stride=None, return_lse=False, ws=None, out=None, out_dtype=None,
+                stream=None):
+    """Sparse attention of one layer over the positions in idx.
+
+    layer: dict with q [B,Lq,H,Dqk], sm_scale, and either kv [B,Lk,576] (MLA latent, V = first
+    512 dims) or k [B,Lk,Hkv,Dqk] and v [B,Lk,Hkv,Dv].  idx: [B,Lq,k] int32, or [B,1,k] with
+    idx_q_stride=0 (all queries share the row, the MTP-draft case).  out_dtype: torch.float32
+    keeps the fp32 result; default is q's dtype.
+    """
+    q = layer["q"]
+    B, Lq, H = q.shape[0], q.shape[1], q.shape[2]
+    k = idx.shape[-1]
+    if idx_q_stride is None:
+        idx_q_stride = 0 if idx.shape[1] == 1 and Lq > 1 else k
+    Dv = layer.get("Dv", 512) if "kv" in layer else layer["v"].shape[-1]
+    if out is None:
+        out = torch.empty((B, Lq, H, Dv), dtype=out_dtype or q.dtype, device=q.device)
+    lse = torch.empty((B, Lq, H), dtype=torch.float32, device=q.device) if return_lse else None
+    s, Lk, _ = _attn_struct(layer, out, lse)
+    _require_cuda(idx)
+    need = workspace_size(DSA_OP_SPARSE_ATTN, s.dtype, B, Lq, Lk, k, H)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(need, q.device)
+    _check("dsa_sparse_attn", load_library().dsa_sparse_attn(
+        ctypes.byref(s), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _ptr(buf), nbytes, _stream(stream)))
+    return (out, lse) if return_lse else out
+
+
+def layer_group(full, layers, topk_k, ws=None, return_lse=False, outs=None, idx_out=None, out_dtype=None,
+                stream=None):
+    """One IndexShare group: the Full layer's indexer + top-k once, then every layer's
+    sparse attention with that index set.  full: dict(q, k, w, q_scale, k_scale);
+    layers: list of attention dicts as for sparse_attn.  Returns (idx, [out per layer])."""
+    s, B, Lq, Lk = _indexer_struct(full["q"], full["k"], full["w"], full.get("q_scale"), full.get("k_scale"))
+    n = len(layers)
+    structs = (_AttnIn * max(n, 1))()
+    keep = []
+    if outs is None:
+        outs = []
+        for lay in layers:
+            q = lay["q"]
+            Dv = lay.get("Dv", 512) if "kv" in lay else lay["v"].shape[-1]
+            outs.append(torch.empty((q.shape[0], q.shape[1], q.shape[2], Dv), dtype=out_dtype or q.dtype,
+                                    device=q.device))
+    lses = [torch.empty(lay["q"].shape[:3], dtype=torch.float32, device=lay["q"].device) if return_lse else None
+            for lay in layers]
+    for i, lay in enumerate(layers):
+        st, _, _ = _attn_struct(lay, outs[i], lses[i])
+        structs[i] = st
+        keep.append(st)
+    if idx_out is None:
+        idx_out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=full["q"].device)
+    heads = layers[0]["q"].shape[2] if n else 16
+    need = workspace_size(DSA_OP_LAYER_GROUP, s.dtype, B, Lq, Lk, topk_k, heads)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(need, full["q"].device)
+    _check("dsa_layer_group", load_library().dsa_layer_group(
+        ctypes.byref(s), structs, n, B, Lq, Lk, topk_k, _ptr(idx_out), _ptr(buf), nbytes, _stream(stream)))
+    if return_lse:
+        return idx_out, outs, lses
+    return idx_out, outs

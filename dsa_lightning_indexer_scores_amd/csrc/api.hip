@@ -1,0 +1,253 @@
+// C ABI of libdsa.so: argument validation, workspace planning and dispatch.
+// Every check runs on the host before anything is enqueued; see include/dsa.h.
+#include "../../include/dsa.h"
+#include "dsa_launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int kMaxFusedK = 4096;
+constexpr int kMaxTopkK = 65536;
+constexpr int kMinFusedLq = 16;   // fewer queries per sequence: score rows + row top-k
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+size_t round_up(size_t x) { return (x + 255) / 256 * 256; }
+
+bool use_materialised(int dtype, int Lq) { return dtype == DSA_F32 || Lq < kMinFusedLq; }
+
+int check_indexer(const dsa_indexer_in* in, int B, int Lq, int Lk) {
+  if (!in || !in->q || !in->k || !in->w) return DSA_ERR_ARG;
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || Lq > Lk) return DSA_ERR_ARG;
+  switch (in->dtype) {
+    case DSA_F32:
+      if (in->H_I <= 0 || in->H_I > 64 || in->d_I <= 0 || (int64_t)in->H_I * in->d_I > 8192) return DSA_ERR_SHAPE;
+      if (!aligned(in->q, 4) || !aligned(in->k, 4) || !aligned(in->w, 4)) return DSA_ERR_ALIGN;
+      break;
+    case DSA_BF16:
+    case DSA_FP8_E4M3:
+      if (in->H_I < 16 || in->H_I > 64 || (in->H_I % 16) != 0 || in->d_I != 128) return DSA_ERR_SHAPE;
+      if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->w, 16)) return DSA_ERR_ALIGN;
+      if (in->dtype == DSA_FP8_E4M3 && (!in->q_scale || !in->k_scale)) return DSA_ERR_ARG;
+      break;
+    default:
+      return DSA_ERR_DTYPE;
+  }
+  return DSA_OK;
+}
+
+int check_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx, int64_t idx_q_stride, int k) {
+  if (!in || !in->q || !in->k || !in->v || !in->out || !idx) return DSA_ERR_ARG;
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0) return DSA_ERR_ARG;
+  if (idx_q_stride != 0 && idx_q_stride < k) return DSA_ERR_ARG;
+  if (!aligned(idx, 4) || (in->lse && !aligned(in->lse, 4))) return DSA_ERR_ALIGN;
+  if (in->out_dtype != DSA_F32 && in->out_dtype != in->dtype) return DSA_ERR_DTYPE;
+  switch (in->dtype) {
+    case DSA_BF16:
+      if (in->H < 16 || in->H > 128 || (in->H % 16) != 0 || in->Hkv != 1 || in->Dqk != 576 || in->Dv != 512)
+        return DSA_ERR_SHAPE;
+      if (in->v != in->k || in->v_row_stride != in->k_row_stride) return DSA_ERR_SHAPE;
+      if (in->k_row_stride < 576 || (in->k_row_stride % 8) != 0) return DSA_ERR_ALIGN;
+      if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->out, 16)) return DSA_ERR_ALIGN;
+      break;
+    case DSA_F32:
+      if (in->H <= 0 || in->Hkv <= 0 || (in->H % in->Hkv) != 0 || in->Dqk <= 0 || in->Dv <= 0 ||
+          in->Dqk > 256 || in->Dv > 256 || k > 8192)
+        return DSA_ERR_SHAPE;
+      if (in->k_row_stride < (int64_t)in->Hkv * in->Dqk || in->v_row_stride < (int64_t)in->Hkv * in->Dv)
+        return DSA_ERR_SHAPE;
+      if (!aligned(in->q, 4) || !aligned(in->k, 4) || !aligned(in->v, 4) || !aligned(in->out, 4)) return DSA_ERR_ALIGN;
+      break;
+    default:
+      return DSA_ERR_DTYPE;
+  }
+  return DSA_OK;
+}
+
+dsa::IndexerArgs make_indexer_args(const dsa_indexer_in* in, int B, int Lq, int Lk) {
+  dsa::IndexerArgs a;
+  a.q = in->q;
+  a.q_scale = in->q_scale;
+  a.k = in->k;
+  a.k_scale = in->k_scale;
+  a.w = in->w;
+  a.H_I = in->H_I;
+  a.d_I = in->d_I;
+  a.dtype = in->dtype;
+  a.B = B;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  return a;
+}
+
+dsa::AttnArgs make_attn_args(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx,
+                             int64_t idx_q_stride, int k) {
+  dsa::AttnArgs a;
+  a.q = in->q;
+  a.k = in->k;
+  a.k_row_stride = in->k_row_stride;
+  a.v = in->v;
+  a.v_row_stride = in->v_row_stride;
+  a.out = in->out;
+  a.lse = in->lse;
+  a.H = in->H;
+  a.Hkv = in->Hkv;
+  a.Dqk = in->Dqk;
+  a.Dv = in->Dv;
+  a.sm_scale = in->sm_scale;
+  a.dtype = in->dtype;
+  a.out_dtype = in->out_dtype;
+  a.B = B;
+  a.Lq = Lq;
+  a.Lk = Lk;
+  a.idx = idx;
+  a.idx_q_stride = idx_q_stride;
+  a.topk = k;
+  return a;
+}
+
+size_t indexer_topk_ws(int dtype, int B, int Lq, int Lk, int k) {
+  if (use_materialised(dtype, Lq)) return round_up((size_t)B * Lq * Lk * sizeof(float));
+  return dsa::indexer_topk_fused_ws(B, Lq, Lk, k, dtype);
+}
+
+size_t attn_ws(int dtype, int B, int Lq, int k, int H) {
+  const size_t a = dsa::sparse_attn_ws(B, Lq, k, H, (int64_t)k, dtype);
+  const size_t b = dsa::sparse_attn_ws(B, Lq, k, H, 0, dtype);
+  return a > b ? a : b;
+}
+
+int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int32_t* idx, void* ws,
+                     size_t ws_bytes, hipStream_t s) {
+  const dsa::IndexerArgs a = make_indexer_args(in, B, Lq, Lk);
+  hipError_t e;
+  if (use_materialised(in->dtype, Lq)) {
+    float* scores = static_cast<float*>(ws);
+    e = dsa::launch_indexer_scores(a, scores, s);
+    if (e == hipSuccess)
+      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, k, idx, nullptr, s);
+  } else {
+    e = dsa::launch_indexer_topk_fused(a, k, idx, ws, ws_bytes, s);
+  }
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dsa_workspace_size(int op, int dtype, int B, int Lq, int Lk, int k, int heads) {
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0) return 0;
+  switch (op) {
+    case DSA_OP_TOPK:
+      return 0;
+    case DSA_OP_INDEXER_TOPK:
+      if (dtype < DSA_F32 || dtype > DSA_FP8_E4M3 || k > kMaxFusedK || Lq > Lk) return 0;
+      return indexer_topk_ws(dtype, B, Lq, Lk, k);
+    case DSA_OP_SPARSE_ATTN:
+      if (heads <= 0 || (dtype != DSA_F32 && dtype != DSA_BF16)) return 0;
+      return attn_ws(dtype, B, Lq, k, heads);
+    case DSA_OP_LAYER_GROUP: {
+      if (dtype < DSA_F32 || dtype > DSA_FP8_E4M3 || k > kMaxFusedK || Lq > Lk || heads <= 0) return 0;
+      const size_t a = indexer_topk_ws(dtype, B, Lq, Lk, k);
+      // attention dtype follows the layers; bf16 needs the (larger) split workspace
+      const size_t b = attn_ws(DSA_BF16, B, Lq, k, heads);
+      return a > b ? a : b;
+    }
+    default:
+      return 0;
+  }
+}
+
+int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* scores, void* stream) {
+  int st = check_indexer(in, B, Lq, Lk);
+  if (st != DSA_OK) return st;
+  if (!scores) return DSA_ERR_ARG;
+  if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_indexer_scores(make_indexer_args(in, B, Lq, Lk), scores,
+                                                  static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_topk(const float* scores, int64_t row_stride, int rows, int n, const int32_t* n_valid, int k,
+             int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!scores || !idx) return DSA_ERR_ARG;
+  if (rows <= 0 || n <= 0 || k <= 0 || k > kMaxTopkK || row_stride < n) return DSA_ERR_ARG;
+  if (!aligned(scores, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)) || (n_valid && !aligned(n_valid, 4)))
+    return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_topk_rows(scores, row_stride, rows, n, n_valid, 0, 0, k, idx, vals,
+                                             static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int32_t* idx, void* ws,
+                     size_t ws_bytes, void* stream) {
+  int st = check_indexer(in, B, Lq, Lk);
+  if (st != DSA_OK) return st;
+  if (!idx || k <= 0 || k > kMaxFusedK) return DSA_ERR_ARG;
+  if (!aligned(idx, 4)) return DSA_ERR_ALIGN;
+  const size_t need = indexer_topk_ws(in->dtype, B, Lq, Lk, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
+  return run_indexer_topk(in, B, Lq, Lk, k, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx, int64_t idx_q_stride, int k,
+                    void* ws, size_t ws_bytes, void* stream) {
+  int st = check_attn(in, B, Lq, Lk, idx, idx_q_stride, k);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::sparse_attn_ws(B, Lq, k, in->H, idx_q_stride, in->dtype);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_sparse_attn(make_attn_args(in, B, Lq, Lk, idx, idx_q_stride, k), ws, ws_bytes,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n_layers, int B, int Lq, int Lk,
+                    int k, int32_t* idx_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_indexer(full, B, Lq, Lk);
+  if (st != DSA_OK) return st;
+  if (!idx_out || k <= 0 || k > kMaxFusedK || n_layers < 0 || (n_layers > 0 && !layers)) return DSA_ERR_ARG;
+  if (!aligned(idx_out, 4)) return DSA_ERR_ALIGN;
+  for (int l = 0; l < n_layers; ++l) {
+    st = check_attn(&layers[l], B, Lq, Lk, idx_out, (int64_t)k, k);
+    if (st != DSA_OK) return st;
+    if (layers[l].dtype != layers[0].dtype || layers[l].H != layers[0].H || layers[l].Dqk != layers[0].Dqk ||
+        layers[l].Dv != layers[0].Dv)
+      return DSA_ERR_SHAPE;
+  }
+  size_t need = indexer_topk_ws(full->dtype, B, Lq, Lk, k);
+  for (int l = 0; l < n_layers; ++l) {
+    const size_t a = dsa::sparse_attn_ws(B, Lq, k, layers[l].H, (int64_t)k, layers[l].dtype);
+    if (a > need) need = a;
+  }
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = run_indexer_topk(full, B, Lq, Lk, k, idx_out, ws, ws_bytes, s);
+  if (st != DSA_OK) return st;
+  for (int l = 0; l < n_layers; ++l) {
+    const hipError_t e =
+        dsa::launch_sparse_attn(make_attn_args(&layers[l], B, Lq, Lk, idx_out, (int64_t)k, k), ws, ws_bytes, s);
+    if (e != hipSuccess) return DSA_ERR_HIP;
+  }
+  return DSA_OK;
+}
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "DSA_OK";
+    case DSA_ERR_ARG: return "DSA_ERR_ARG: null pointer, non-positive size or k out of range";
+    case DSA_ERR_DTYPE: return "DSA_ERR_DTYPE: dtype not supported for this operation";
+    case DSA_ERR_SHAPE: return "DSA_ERR_SHAPE: head count, head dim or stride combination not supported";
+    case DSA_ERR_ALIGN: return "DSA_ERR_ALIGN: pointer or stride not aligned as required";
+    case DSA_ERR_WORKSPACE: return "DSA_ERR_WORKSPACE: workspace missing or too small";
+    case DSA_ERR_HIP: return "DSA_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown dsa_status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Device-side building blocks shared by the DSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// MFMA wrappers.  Lane layouts (verified on gfx950):
+//  16x16xK: A lane l holds row (l % 16), a contiguous K-slice chosen by (l / 16);
+//           B lane l holds column (l % 16) with the same K-slice; A and B pair their
+//           K elements position by position, so any K permutation applied to both
+//           operands gives the same dot products.
+//           D lane l holds column (l % 16), rows 4 * (l / 16) + i, i = 0..3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// OCP E4M3 x OCP E4M3, 16x16x128 (format code 0 for both operands, unit scales).
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving map float -> uint32 (larger float -> larger key); -0 maps to +0 so
+// that signed zeros tie.  Key 0 is never produced by a finite or infinite float, so
+// "key > 0" admits every candidate.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---------------------------------------------------------------------------
+// Wave helpers.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+// number of set bits of m below this lane
+__device__ __forceinline__ uint32_t rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+__device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
+
+template <typename T>
+__device__ __forceinline__ T uniform(T v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ float wave_max16x4(float v) {  // max over lanes {l, l^16, l^32, l^48}
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum16x4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Reduce-scatter of four per-lane partial sums p[0..3] over the four 16-lane groups:
+// afterwards lane l holds sum over groups g of p[l / 16] taken at lane (l % 16) + 16 g.
+// Uses the gfx950 cross-half (32) and cross-row (16) lane swaps.
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+  // Step 1: lanes 0-31 keep blocks 0,1 and lanes 32-63 keep blocks 2,3.
+  // permlane32_swap(a, b) returns {[a_lo, b_lo], [a_hi, b_hi]} (halves of 32 lanes).
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p2), false, false);
+  auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(p1), __float_as_uint(p3), false, false);
+  float q0 = __uint_as_float(x[0]) + __uint_as_float(x[1]);  // lo: block 0, hi: block 2
+  float q1 = __uint_as_float(y[0]) + __uint_as_float(y[1]);  // lo: block 1, hi: block 3
+  // Step 2: within each half, row 0 keeps the first block and row 1 the second.
+  // permlane16_swap(a, b) returns {[a_r0, b_r0], [a_r1, b_r1]} per 32-lane half.
+  auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(q0), __float_as_uint(q1), false, false);
+  return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+}  // namespace dsa

@@ -1,0 +1,59 @@
+// Host-side launchers of the DSA kernels (internal to libdsa.so).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dsa {
+
+struct IndexerArgs {
+  const void* q;         // [B, Lq, H_I, d_I]
+  const float* q_scale;  // [B, Lq] or null
+  const void* k;         // [B, Lk, d_I]
+  const float* k_scale;  // [B, Lk] or null
+  const float* w;        // [B, Lq, H_I]
+  int H_I, d_I, dtype;
+  int B, Lq, Lk;
+};
+
+// Capacity (entries) of the per-row streaming candidate buffer of the fused kernel.
+inline int topk_buffer_capacity(int k) {
+  int cap = 2 * k;
+  if (cap < k + 512) cap = k + 512;
+  return (cap + 63) / 64 * 64;
+}
+
+// --- indexer ---------------------------------------------------------------
+hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, hipStream_t s);
+// Fused streaming indexer + top-k for query counts large enough to fill the GPU.
+size_t indexer_topk_fused_ws(int B, int Lq, int Lk, int k, int dtype);
+hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, void* ws,
+                                     size_t ws_bytes, hipStream_t s);
+
+// --- top-k over materialised rows -------------------------------------------
+hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, int n,
+                            const int32_t* n_valid, int causal_Lq, int causal_Lk, int k,
+                            int32_t* idx, float* vals, hipStream_t s);
+
+// --- sparse attention --------------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  int64_t k_row_stride;
+  const void* v;
+  int64_t v_row_stride;
+  void* out;
+  float* lse;
+  int H, Hkv, Dqk, Dv;
+  float sm_scale;
+  int dtype;
+  int out_dtype;
+  int B, Lq, Lk;
+  const int32_t* idx;
+  int64_t idx_q_stride;
+  int topk;          // entries per idx row
+};
+size_t sparse_attn_ws(int B, int Lq, int k, int H, int64_t idx_q_stride, int dtype);
+hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace dsa

@@ -1,0 +1,217 @@
+/*
+ * dsa.h -- C ABI of libdsa.so: DeepSeek-Sparse-Attention token selection with
+ * IndexShare cross-layer index reuse, hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * The operations follow the statement of the problem on these pages:
+ *  [A] GLM-5.2 技术报告速览：IndexShare 与 critic-based PPO (mloasisblog), section
+ *      "IndexShare": lightning-indexer score I[t,s] = sum_j w[t,j] ReLU(q^I[t,j] . k^I[s])
+ *      over causal s <= t, then top-k (k = 2048) position IDs; groups of 4 layers with
+ *      1 Full layer (runs the indexer) and 3 Shared layers (inherit its index set).
+ *  [B] GLM 5.2: Built for Long Horizon Tasks (papers.chlience.com), section 5.2 (FSSS
+ *      pattern; Shared layers read their own KV cache at the shared positions) and the
+ *      discussion section "DSA 与 IndexShare 的组合数据流" (sparse core attention reads
+ *      the selected positions' K/V of its own layer and recomputes score, softmax and
+ *      value aggregation; only top-k position IDs cross layers; MLA decode uses the
+ *      576-d latent: 512-d compressed KV + 64-d RoPE key).
+ *  [C] GLM-5 technical report, section 3.2 "DSA 强化学习洞察": the top-k operator must
+ *      be deterministic.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer argument is DEVICE memory owned by the caller, except the struct
+ *    pointers (dsa_indexer_in*, dsa_attn_in*), which are host memory read during the
+ *    call only.  The library allocates no device memory and keeps no pointer after
+ *    the call returns.
+ *  - stream is a hipStream_t passed as void* (NULL = the default stream).  Calls only
+ *    enqueue work on it; none synchronises the host.
+ *  - Arguments are validated before anything is enqueued.  A negative return value
+ *    (dsa_status) means nothing was enqueued.  DSA_ERR_HIP means a HIP launch error
+ *    (work enqueued before the failing launch may have run).  No C++ exception crosses
+ *    the ABI.  Entry points are reentrant and hold no mutable global state.
+ *  - Layout: tensors are dense, row-major, innermost dimension last.  A query i of a
+ *    call with Lq queries and Lk keys sits at position p_i = Lk - Lq + i and sees the
+ *    keys s <= p_i (causality of [A]).
+ *  - Index sets (top-k) are int32 position IDs s in [0, Lk), listed in ascending order;
+ *    a row with fewer than k causal keys lists all of them followed by -1 padding; ties
+ *    in score go to the lower position (reading of [C]'s determinism requirement).
+ *  - FP8 operands are OCP E4M3 ("e4m3fn") codes with one fp32 scale per token; the
+ *    dequantised value is code * scale.  Scales must be > 0 (the kernels factor them
+ *    out of the ReLU, which is exact only for positive scales).
+ *  - Scores must be finite; NaN or infinite scores make the selected set unspecified.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_ARG = -1,        /* null pointer, non-positive size, k out of range        */
+  DSA_ERR_DTYPE = -2,      /* dtype not supported for this operation                  */
+  DSA_ERR_SHAPE = -3,      /* head count / head dim / stride combination unsupported  */
+  DSA_ERR_ALIGN = -4,      /* a pointer or stride is not aligned as required          */
+  DSA_ERR_WORKSPACE = -5,  /* workspace missing or smaller than dsa_workspace_size()  */
+  DSA_ERR_HIP = -6         /* a HIP call or kernel launch failed                      */
+} dsa_status;
+
+typedef enum { DSA_F32 = 0, DSA_BF16 = 1, DSA_FP8_E4M3 = 2 } dsa_dtype;
+
+/* Operations that take a workspace (argument `op` of dsa_workspace_size). */
+typedef enum {
+  DSA_OP_TOPK = 0,
+  DSA_OP_INDEXER_TOPK = 1,
+  DSA_OP_SPARSE_ATTN = 2,
+  DSA_OP_LAYER_GROUP = 3
+} dsa_op;
+
+/*
+ * Indexer operands of one Full layer ([A], indexer-score equation; [B] the indexer has
+ * its own light W_Q^I / W_K^I projections and a per-layer index-key cache).
+ *   q       [B, Lq, H_I, d_I]  dtype    query heads q^I
+ *   q_scale [B, Lq] fp32                per-token scale (DSA_FP8_E4M3 only, else NULL)
+ *   k       [B, Lk, d_I]       dtype    index-key cache k^I
+ *   k_scale [B, Lk] fp32                per-token scale (DSA_FP8_E4M3 only, else NULL)
+ *   w       [B, Lq, H_I] fp32           per-head gating weights w^I (any sign)
+ * Supported: DSA_F32 with H_I <= 64 and H_I * d_I <= 8192 (reference-size path);
+ *            DSA_BF16 / DSA_FP8_E4M3 with H_I in {16, 32, 48, 64} and d_I == 128.
+ * q and k must be 16-byte aligned.
+ */
+typedef struct {
+  const void* q;
+  const float* q_scale;
+  const void* k;
+  const float* k_scale;
+  const float* w;
+  int32_t H_I;
+  int32_t d_I;
+  int32_t dtype; /* dsa_dtype */
+} dsa_indexer_in;
+
+/*
+ * Operands of one layer's sparse core attention ([B], combined data-flow section).
+ *   q    [B, Lq, H, Dqk]                       query heads (MLA: already absorbed, Dqk=576)
+ *   k    [B, Lk, k_row_stride] elements        key rows: head g at offset g*Dqk
+ *   v    [B, Lk, v_row_stride] elements        value rows: head g at offset g*Dv
+ *                                              (MLA: v == k, Dv = 512 = the c_kv part)
+ *   out  [B, Lq, H, Dv]                        written, dtype out_dtype (DSA_F32, or the
+ *                                              input dtype; DSA_F32 keeps the fp32 result)
+ *   lse  [B, Lq, H] fp32 or NULL               natural-log sum of exp(scaled logits);
+ *                                              -inf for a query with no selected key
+ * Query head h reads KV head h / (H / Hkv).  sm_scale multiplies q.k before softmax.
+ * Supported: DSA_BF16 MLA latent form: H % 16 == 0, 16 <= H <= 128, Hkv == 1,
+ *            Dqk == 576, Dv == 512, v == k with v_row_stride == k_row_stride (the value
+ *            is the first 512 dims of the latent row), k_row_stride a multiple of 8
+ *            elements >= 576, q/k/out 16-byte aligned;
+ *            DSA_F32 with Dqk, Dv <= 256, H % Hkv == 0, k <= 8192 (reference-size path;
+ *            k and v may be separate, k_row_stride >= Hkv*Dqk, v_row_stride >= Hkv*Dv).
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  int64_t k_row_stride;
+  const void* v;
+  int64_t v_row_stride;
+  void* out;
+  float* lse;
+  int32_t H;
+  int32_t Hkv;
+  int32_t Dqk;
+  int32_t Dv;
+  float sm_scale;
+  int32_t dtype;     /* dsa_dtype of q, k, v */
+  int32_t out_dtype; /* dsa_dtype of out: DSA_F32 or equal to dtype */
+} dsa_attn_in;
+
+/*
+ * Bytes of device workspace needed by `op` (a dsa_op) for these sizes; 0 if none.
+ * dtype is the indexer dtype for DSA_OP_INDEXER_TOPK / DSA_OP_LAYER_GROUP and the
+ * attention dtype for DSA_OP_SPARSE_ATTN; `heads` is the attention head count H for
+ * DSA_OP_SPARSE_ATTN and DSA_OP_LAYER_GROUP (0 elsewhere).  The value covers both
+ * idx_q_stride conventions of dsa_sparse_attn.  Pure host arithmetic, no device call;
+ * returns 0 for invalid arguments (the entry point then reports them).
+ */
+size_t dsa_workspace_size(int op, int dtype, int B, int Lq, int Lk, int k, int heads);
+
+/*
+ * Materialised indexer scores ([A], indexer-score equation; ReLU and the head-weighted
+ * sum are fused after the dot products):
+ *   scores[b, i, s] = sum_j w[b,i,j] * ReLU(q[b,i,j,:] . k[b,s,:])   for s <= p_i,
+ *   scores[b, i, s] = -inf                                           for s >  p_i.
+ * scores: [B, Lq, Lk] fp32, written completely.  Used for short query counts (decode)
+ * and for testing; the prefill path uses dsa_indexer_topk, which never writes the
+ * Lq x Lk matrix.
+ */
+int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* scores,
+                       void* stream);
+
+/*
+ * Deterministic top-k over materialised rows ([A] top-k; [C] determinism):
+ * row r holds n fp32 scores at scores + r * row_stride; only the first n_valid[r]
+ * entries are candidates (n_valid == NULL means n for every row).  Writes idx[r, 0..k)
+ * (ascending positions, -1 padding, ties to the lower position) and, if vals != NULL,
+ * vals[r, j] = score of idx[r, j] (-inf for padding).  Requires 1 <= k <= 65536,
+ * n >= 1, row_stride >= n.  Needs no workspace: ws may be NULL (ws_bytes ignored).
+ */
+int dsa_topk(const float* scores, int64_t row_stride, int rows, int n,
+             const int32_t* n_valid, int k, int32_t* idx, float* vals, void* ws,
+             size_t ws_bytes, void* stream);
+
+/*
+ * Fused indexer + top-k ([A]; the score tiles are filtered against a running per-query
+ * threshold as they are produced, so the Lq x Lk score matrix is never written):
+ * idx[b, i, 0..k) = top-k positions of scores[b, i, :] as defined by dsa_indexer_scores
+ * and dsa_topk.  Requires 1 <= k <= 4096.  For DSA_F32, and for fewer than 16 queries
+ * per sequence (decode), the scores of each query row are written to the workspace
+ * (one row of Lk floats per query, never Lq x Lk for prefill) and selected by the dsa_topk
+ * kernel; otherwise the fused streaming kernel runs.
+ * ws: dsa_workspace_size(DSA_OP_INDEXER_TOPK, in->dtype, B, Lq, Lk, k, 0) bytes.
+ */
+int dsa_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k,
+                     int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Sparse core attention over selected positions ([B], combined data-flow section):
+ * for query (b, i), head h, with S = the entries of its idx row that lie in [0, Lk)
+ * (-1 and out-of-range entries are skipped):
+ *   out[b,i,h,:] = sum_{s in S} softmax_s(sm_scale * q[b,i,h,:] . K_g[s]) * V_g[s],
+ *   g = h / (H / Hkv).  The idx row of (b, i) is idx + b * (idx_q_stride ? Lq *
+ *   idx_q_stride : k) + i * idx_q_stride: idx_q_stride = k is one row per query,
+ *   idx_q_stride = 0 makes all Lq queries of a sequence share one row (the MTP-draft
+ *   reuse of the first draft step's index set, [B] section 5.3).
+ * Causality is not re-applied here: attention reads exactly the listed positions, which
+ * must be distinct within a row (as top-k rows are); a repeated position would be
+ * weighted once per occurrence.
+ * idx_q_stride must be 0 or >= k.  When few query rows are given (decode) the keys are
+ * split across workgroups and combined; the partial results live in
+ * ws: dsa_workspace_size(DSA_OP_SPARSE_ATTN, in->dtype, B, Lq, Lk, k, in->H) bytes.
+ */
+int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx,
+                    int64_t idx_q_stride, int k, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * One IndexShare group ([A] section "IndexShare"; [B] section 5.2): the Full layer's
+ * indexer + top-k runs once (dsa_indexer_topk with `full`), writing idx_out [B, Lq, k];
+ * then layers[0..n_layers) each run dsa_sparse_attn with that same idx (layer 0 is the
+ * Full layer's own attention, layers 1.. are the Shared layers).  n_layers = 0 is
+ * dsa_indexer_topk alone.  The all-Full comparator is n_layers = 1 called once per layer
+ * with each layer's own indexer operands.
+ * All layers must share dtype, H, Dqk and Dv.  The attention runs with idx_q_stride = k.
+ * ws: dsa_workspace_size(DSA_OP_LAYER_GROUP, full->dtype, B, Lq, Lk, k, layers[0].H)
+ * bytes (covers the indexer and the attention, which run one after the other).
+ */
+int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n_layers,
+                    int B, int Lq, int Lk, int k, int32_t* idx_out, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* Static string naming a status code. */
+const char* dsa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

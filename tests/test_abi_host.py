@@ -1,0 +1,129 @@
+"""CPU-side checks of the C ABI: the library loads, exports every declared entry point,
+sizes workspaces with pure host arithmetic, and rejects invalid arguments before
+touching the GPU (these calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_lightning_indexer_scores_amd as dsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+
+import torch
+
+pytestmark = pytest.mark.skipif(not os.path.exists(dsa.library_path()),
+                                reason="libdsa.so not built (run __graft_entry__.build())")
+
+# The error-path tests hand the library fake device addresses and rely on validation
+# rejecting the call before any launch; they run only where no GPU is visible.
+host_only = pytest.mark.skipif(torch.cuda.device_count() > 0,
+                               reason="fake-pointer validation tests run on GPU-less hosts only")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = dsa.load_library()
+    names = declared_functions()
+    assert set(names) >= {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_layer_group",
+                          "dsa_indexer_topk", "dsa_workspace_size", "dsa_status_string"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(0, -7, -1):
+        assert dsa.status_string(code).startswith("DSA_")
+    assert dsa.status_string(-99) == "unknown dsa_status"
+
+
+def test_workspace_sizes_are_host_arithmetic():
+    ws = dsa.workspace_size
+    assert ws(dsa.DSA_OP_TOPK, dsa.DSA_F32, 1, 16, 1000, 64) == 0
+    # fp32 / decode: one score row per query
+    assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_F32, 1, 1024, 1024, 64) >= 1024 * 1024 * 4
+    assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_FP8_E4M3, 64, 1, 200001, 2048) >= 64 * 200001 * 4
+    # fused: bounded per-workgroup candidate buffers, not Lq x Lk
+    big = ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_FP8_E4M3, 1, 131072, 131072, 2048)
+    assert 0 < big < 131072 * 131072 * 4 // 16
+    # decode attention splits the keys: partial results need a workspace
+    assert ws(dsa.DSA_OP_SPARSE_ATTN, dsa.DSA_BF16, 64, 1, 200001, 2048, 32) > 0
+    assert ws(dsa.DSA_OP_LAYER_GROUP, dsa.DSA_FP8_E4M3, 64, 1, 200001, 2048, 32) >= \
+        ws(dsa.DSA_OP_SPARSE_ATTN, dsa.DSA_BF16, 64, 1, 200001, 2048, 32)
+    assert ws(dsa.DSA_OP_INDEXER_TOPK, 7, 1, 16, 16, 4) == 0          # bad dtype
+    assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_BF16, 1, 32, 16, 4) == 0  # Lq > Lk
+
+
+def _indexer_struct(dtype=dsa.DSA_BF16, H_I=64, d_I=128, q=0x1000, k=0x2000, w=0x3000, qs=0, ks=0):
+    return dsa._IndexerIn(q, qs, k, ks, w, H_I, d_I, dtype)
+
+
+def _call_indexer_topk(s, B=1, Lq=64, Lk=64, k=16, idx=0x4000, ws=0x10000, nbytes=1 << 40):
+    lib = dsa.load_library()
+    return lib.dsa_indexer_topk(ctypes.byref(s), B, Lq, Lk, k, idx, ws, nbytes, None)
+
+
+@host_only
+def test_indexer_argument_errors():
+    E = {"arg": -1, "dtype": -2, "shape": -3, "align": -4, "ws": -5}
+    assert _call_indexer_topk(_indexer_struct(q=0)) == E["arg"]
+    assert _call_indexer_topk(_indexer_struct(dtype=9)) == E["dtype"]
+    assert _call_indexer_topk(_indexer_struct(H_I=40)) == E["shape"]
+    assert _call_indexer_topk(_indexer_struct(d_I=64)) == E["shape"]
+    assert _call_indexer_topk(_indexer_struct(q=0x1004)) == E["align"]
+    assert _call_indexer_topk(_indexer_struct(dtype=dsa.DSA_FP8_E4M3)) == E["arg"]   # scales missing
+    assert _call_indexer_topk(_indexer_struct(), Lq=65, Lk=64) == E["arg"]          # Lq > Lk
+    assert _call_indexer_topk(_indexer_struct(), k=0) == E["arg"]
+    assert _call_indexer_topk(_indexer_struct(), k=5000) == E["arg"]
+    assert _call_indexer_topk(_indexer_struct(), ws=0) == E["ws"]
+    assert _call_indexer_topk(_indexer_struct(), nbytes=16) == E["ws"]
+    lib = dsa.load_library()
+    assert lib.dsa_indexer_scores(ctypes.byref(_indexer_struct()), 1, 4, 4, None, None) == E["arg"]
+    assert lib.dsa_topk(None, 8, 1, 8, None, 4, 0x1000, None, None, 0, None) == E["arg"]
+    assert lib.dsa_topk(0x1000, 4, 1, 8, None, 4, 0x2000, None, None, 0, None) == E["arg"]  # stride < n
+    assert lib.dsa_topk(0x1002, 8, 1, 8, None, 4, 0x2000, None, None, 0, None) == E["align"]
+
+
+def _attn_struct(dtype=dsa.DSA_BF16, H=32, Hkv=1, Dqk=576, Dv=512, q=0x1000, k=0x2000, v=0x2000,
+                 ks=576, vs=576, out=0x3000):
+    return dsa._AttnIn(q, k, ks, v, vs, out, None, H, Hkv, Dqk, Dv, 0.04, dtype)
+
+
+@host_only
+def test_attention_argument_errors():
+    lib = dsa.load_library()
+
+    def call(s, idx=0x5000, qstride=16, k=16, ws=0x100000, nbytes=1 << 40, B=1, Lq=4, Lk=64):
+        return lib.dsa_sparse_attn(ctypes.byref(s), B, Lq, Lk, idx, qstride, k, ws, nbytes, None)
+
+    assert call(_attn_struct(), idx=0) == -1
+    assert call(_attn_struct(), qstride=8) == -1               # 0 < stride < k
+    assert call(_attn_struct(H=40)) == -3
+    assert call(_attn_struct(Hkv=2)) == -3
+    assert call(_attn_struct(Dqk=512)) == -3
+    assert call(_attn_struct(v=0x9000)) == -3                   # MLA needs v == k
+    assert call(_attn_struct(ks=580, vs=580)) == -4             # stride not multiple of 8
+    assert call(_attn_struct(q=0x1008)) == -4
+    assert call(_attn_struct(dtype=dsa.DSA_FP8_E4M3)) == -2
+    assert call(_attn_struct(dtype=dsa.DSA_F32, H=4, Hkv=4, Dqk=64, Dv=64, ks=256, vs=256), k=9000,
+                qstride=9000) == -3
+    # decode (few rows) needs the split workspace
+    assert call(_attn_struct(), ws=0, nbytes=0, B=2, Lq=1, k=2048, qstride=2048) == -5
+
+
+@host_only
+def test_layer_group_argument_errors():
+    lib = dsa.load_library()
+    full = _indexer_struct()
+    layers = (dsa._AttnIn * 2)(_attn_struct(), _attn_struct(H=16))
+    st = lib.dsa_layer_group(ctypes.byref(full), layers, 2, 1, 64, 64, 16, 0x4000, 0x100000, 1 << 40, None)
+    assert st == -3                                             # layers disagree on H
+    st = lib.dsa_layer_group(ctypes.byref(full), None, 1, 1, 64, 64, 16, 0x4000, 0x100000, 1 << 40, None)
+    assert st == -1

@@ -1,0 +1,287 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars (see the design notes for their derivation):
+* dsa_topk fed the oracle's fp32 scores: bit-exact (same idx array, order, padding).
+* materialised scores: |gpu - oracle| <= rtol * max|row| (rtol 1e-5 fp32, 1e-4 bf16,
+  3e-3 fp8: fp32 accumulation of exact bf16/fp8 products; the fp8 MFMA accumulates
+  with ~1e-4 relative error).
+* fused indexer + top-k: bit-identical to dsa_topk(dsa_indexer_scores) (same score
+  bits), and index sets equal to the oracle's except for positions whose oracle score
+  lies within tau*|theta| of the row's k-th score (tau 1e-3 bf16, 2e-2 fp8), sizes exact.
+* sparse attention: max |err| <= 1e-2 * RMS(oracle output) with the GPU's idx.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import dsa_lightning_indexer_scores_amd as dsa
+from tests._helpers import to_f64, indexer_to_oracle, attn_to_oracle, index_sets_agree
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TAU = {"bf16": 1e-3, "fp8": 2e-2, "f32": 1e-5}
+SCORE_RTOL = {"f32": 1e-5, "bf16": 1e-4, "fp8": 3e-3}
+
+
+def _cfg(dtype, L, k, **kw):
+    base = "prefill16k" if dtype == "bf16" else ("prefill128k" if dtype == "fp8" else "tiny")
+    return synth.get_config(base, L=L, Lq=kw.pop("Lq", L), topk=k, **kw)
+
+
+def _ind_args(ind):
+    return dict(q_scale=ind["q_scale"], k_scale=ind["k_scale"])
+
+
+def _oracle_rows(ora, b, rows, Lq, Lk):
+    return oracle.indexer_scores_rows(
+        ora["q"][b], ora["k"][b], ora["w"][b], rows, Lk,
+        None if ora["q_scale"] is None else ora["q_scale"][b],
+        None if ora["k_scale"] is None else ora["k_scale"][b], Lq)
+
+
+# ---------------------------------------------------------------------------
+# top-k on the oracle's fp32 scores: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_topk_bitexact_on_oracle_scores_tiny():
+    cfg = synth.get_config("tiny")
+    ind = synth.indexer_inputs(cfg, device="cpu")
+    ora = indexer_to_oracle(ind)
+    sc64 = oracle.indexer_scores(ora["q"], ora["k"], ora["w"])[0]        # [L, L]
+    sc32 = sc64.astype(np.float32)
+    L, k = cfg.L, cfg.topk
+    n_valid = np.arange(1, L + 1, dtype=np.int32)
+    ref = oracle.topk_rows(sc32.astype(np.float64), n_valid, k)
+    got = dsa.topk(torch.from_numpy(sc32).to(DEV), k,
+                   n_valid=torch.from_numpy(n_valid).to(DEV)).cpu().numpy()
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("case", ["gauss", "ties", "signed_zero", "k1", "k_ge_n", "long"])
+def test_topk_bitexact_edge_cases(case):
+    rng = np.random.default_rng(hash(case) % 2 ** 32)
+    if case == "gauss":
+        rows, n, k = 37, 5003, 2048
+        x = rng.standard_normal((rows, n)).astype(np.float32)
+        nv = rng.integers(1, n + 1, rows).astype(np.int32)
+        nv[:3] = [1, 2047, 2049]
+    elif case == "ties":
+        rows, n, k = 16, 3001, 100
+        x = rng.integers(0, 4, (rows, n)).astype(np.float32)
+        nv = np.full(rows, n, dtype=np.int32)
+    elif case == "signed_zero":
+        rows, n, k = 8, 700, 300
+        x = rng.choice(np.array([0.0, -0.0, -1.0, 1.0, -2.5], dtype=np.float32), (rows, n))
+        nv = np.full(rows, n, dtype=np.int32)
+    elif case == "k1":
+        rows, n, k = 9, 1000, 1
+        x = rng.integers(0, 3, (rows, n)).astype(np.float32)
+        nv = rng.integers(1, n + 1, rows).astype(np.int32)
+    elif case == "k_ge_n":
+        rows, n, k = 5, 300, 512
+        x = rng.standard_normal((rows, n)).astype(np.float32)
+        nv = np.array([300, 1, 299, 17, 0], dtype=np.int32)
+    else:
+        rows, n, k = 2, 200001, 2048
+        x = (rng.standard_normal((rows, n)) * 3).astype(np.float32)
+        nv = np.array([n, 150000], dtype=np.int32)
+    ref = oracle.topk_rows(x.astype(np.float64), nv, k)
+    got_idx, got_val = dsa.topk(torch.from_numpy(x).to(DEV), k, n_valid=torch.from_numpy(nv).to(DEV),
+                                return_vals=True)
+    got_idx = got_idx.cpu().numpy()
+    assert np.array_equal(got_idx, ref)
+    gv = got_val.cpu().numpy()
+    for r in range(rows):
+        sel = ref[r] >= 0
+        assert np.array_equal(gv[r][sel], x[r][ref[r][sel]])
+        assert np.all(np.isneginf(gv[r][~sel]))
+
+
+# ---------------------------------------------------------------------------
+# materialised scores
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,L,Lq,B", [("f32", 1024, 1024, 1), ("bf16", 600, 600, 1),
+                                          ("fp8", 520, 520, 1), ("fp8", 5000, 3, 2), ("bf16", 777, 5, 2)])
+def test_indexer_scores_parity(dtype, L, Lq, B):
+    cfg = _cfg(dtype, L, 64, Lq=Lq, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    got = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind)).cpu().numpy()
+    ora = indexer_to_oracle(ind)
+    rng = np.random.default_rng(0)
+    rows = sorted(set([0, 1, Lq - 1] + rng.integers(0, Lq, 12).tolist()))
+    for b in range(B):
+        ref = _oracle_rows(ora, b, rows, Lq, L)
+        g = got[b][rows]
+        assert np.array_equal(np.isneginf(g), np.isneginf(ref))
+        fin = np.isfinite(ref)
+        scale = np.abs(np.where(fin, ref, 0)).max(axis=1, keepdims=True) + 1e-30
+        err = np.abs(np.where(fin, g - ref, 0)) / scale
+        assert err.max() <= SCORE_RTOL[dtype], (dtype, err.max())
+
+
+# ---------------------------------------------------------------------------
+# fused indexer + top-k
+# ---------------------------------------------------------------------------
+
+FUSED_CASES = [
+    # dtype, B, Lq, Lk, k
+    ("bf16", 1, 2048, 2048, 256),      # many compactions per row
+    ("fp8", 1, 2048, 2048, 256),
+    ("fp8", 1, 1000, 1000, 2048),      # every row shorter than k: all causal keys
+    ("bf16", 2, 333, 333, 64),         # ragged tail, batch
+    ("fp8", 2, 64, 32768, 512),        # few queries, long keys: key segments + merge
+    ("bf16", 1, 48, 20000, 1),         # k = 1
+]
+
+
+@pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES)
+def test_fused_topk_equals_scores_then_topk(dtype, B, Lq, Lk, k):
+    cfg = _cfg(dtype, Lk, k, Lq=Lq, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind))
+    nv = (torch.arange(Lq, device=DEV, dtype=torch.int32) + (Lk - Lq + 1)).repeat(B)
+    ref = dsa.topk(sc.reshape(B * Lq, Lk), k, n_valid=nv).reshape(B, Lq, k)
+    assert torch.equal(idx, ref)
+    idx2 = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    assert torch.equal(idx, idx2)                                     # run twice: identical
+
+
+@pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES[:5])
+def test_fused_topk_matches_oracle_sets(dtype, B, Lq, Lk, k):
+    cfg = _cfg(dtype, Lk, k, Lq=Lq, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind)).cpu().numpy()
+    ora = indexer_to_oracle(ind)
+    rng = np.random.default_rng(1)
+    rows = sorted(set([0, min(k, Lq) - 1, min(k, Lq - 1), Lq - 1] + rng.integers(0, Lq, 10).tolist()))
+    for b in range(B):
+        sc = _oracle_rows(ora, b, rows, Lq, Lk)
+        nv = [Lk - Lq + r + 1 for r in rows]
+        ref = oracle.topk_rows(sc, nv, k)
+        ok, nbad, msg = index_sets_agree(idx[b][rows], ref, sc, nv, k, TAU[dtype])
+        assert ok, msg
+
+
+def test_rows_shorter_than_k_select_every_causal_key():
+    cfg = _cfg("fp8", 3000, 2048)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], 2048, **_ind_args(ind)).cpu().numpy()[0]
+    for t in (0, 1, 100, 2046, 2047):
+        assert idx[t, : t + 1].tolist() == list(range(t + 1))
+        assert np.all(idx[t, t + 1:] == -1)
+    assert np.all(idx[2048:] >= 0)
+
+
+# ---------------------------------------------------------------------------
+# sparse attention
+# ---------------------------------------------------------------------------
+
+def _attn_check(lay, idx_np, out, lse, rows, b=0, idx_rows_override=None):
+    ol = attn_to_oracle(lay)
+    ir = idx_np[b][rows] if idx_rows_override is None else idx_rows_override
+    ref, ref_lse = oracle.sparse_attention_rows(ol["q"][b][rows], ol["k"][b], ol["v"][b], ir,
+                                                ol["sm_scale"], ol["Hkv"])
+    g = to_f64(out[b][rows])
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = np.abs(g - ref).max()
+    assert err <= 1e-2 * rms, (err, rms)
+    if lse is not None:
+        gl = lse[b][rows].cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isneginf(gl), np.isneginf(ref_lse))
+        fin = np.isfinite(ref_lse)
+        assert np.abs(gl[fin] - ref_lse[fin]).max() <= 2e-3 * (1 + np.abs(ref_lse[fin]).max())
+
+
+def test_mla_prefill_attention_parity():
+    L, k = 1500, 256
+    cfg = _cfg("bf16", L, k)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    lay = synth.attention_inputs(cfg, layer=1, device=DEV)
+    out, lse = dsa.sparse_attn(lay, idx, return_lse=True, out_dtype=torch.float32)
+    rows = [0, 1, 5, 255, 256, 700, 1499]
+    _attn_check(lay, idx.cpu().numpy(), out, lse, rows)
+    out2 = dsa.sparse_attn(lay, idx, out_dtype=torch.float32)
+    assert torch.equal(out, out2)                                   # run twice: identical
+    out_bf = dsa.sparse_attn(lay, idx)                               # bf16 output = RNE(fp32 result)
+    assert out_bf.dtype == torch.bfloat16 and torch.equal(out_bf, out.to(torch.bfloat16))
+
+
+def test_mla_attention_invalid_and_padded_entries():
+    cfg = _cfg("bf16", 300, 40)
+    lay = synth.attention_inputs(cfg, layer=0, device=DEV)
+    rng = np.random.default_rng(3)
+    idx = np.stack([np.sort(rng.permutation(300)[:40]) for _ in range(300)])[None].astype(np.int32)
+    idx[0, 0] = -1                         # no key at all: zeros, lse = -inf
+    idx[0, 1, 5:] = -1                     # padded row
+    idx[0, 2, ::3] = 1000                  # out of range: skipped
+    idx[0, 3] = -1
+    idx[0, 3, 17] = 7                      # one key: out = V[7]
+    out, lse = dsa.sparse_attn(lay, torch.from_numpy(idx).to(DEV), return_lse=True, out_dtype=torch.float32)
+    ol_idx = idx.copy()
+    ol_idx[ol_idx >= 300] = -1
+    rows = [1, 2, 3, 4, 299]
+    _attn_check(lay, ol_idx, out, lse, rows)
+    assert torch.all(out[0, 0] == 0) and torch.all(torch.isneginf(lse[0, 0]))
+    v7 = lay["kv"][0, 7, :512].float()
+    assert torch.equal(out[0, 3], v7.expand(32, 512))
+
+
+def test_mla_decode_split_and_mtp_shared_rows():
+    B, Lk, k = 3, 5000, 2048
+    cfg = synth.get_config("decode200k", L=Lk, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))    # [B, 1, k]
+    lay = synth.attention_inputs(cfg, layer=2, device=DEV)                       # Lq = 1
+    out, lse = dsa.sparse_attn(lay, idx, return_lse=True, out_dtype=torch.float32)
+    for b in range(B):
+        _attn_check(lay, idx.cpu().numpy(), out, lse, [0], b=b)
+    # MTP draft: 4 queries per sequence share the first step's index row
+    lay4 = synth.attention_inputs(cfg, layer=3, device=DEV, Lq=4)
+    out4, lse4 = dsa.sparse_attn(lay4, idx, idx_q_stride=0, return_lse=True, out_dtype=torch.float32)
+    shared = idx.cpu().numpy()[:, 0]
+    for b in range(B):
+        _attn_check(lay4, None, out4, lse4, [0, 1, 2, 3], b=b,
+                    idx_rows_override=np.repeat(shared[b][None], 4, axis=0))
+
+
+def test_tiny_mha_fp32_attention_parity():
+    cfg = synth.get_config("tiny")
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], cfg.topk, **_ind_args(ind))
+    lay = synth.attention_inputs(cfg, layer=0, device=DEV)
+    out, lse = dsa.sparse_attn(lay, idx, return_lse=True)
+    _attn_check(lay, idx.cpu().numpy(), out, lse, [0, 3, 63, 64, 500, 1023])
+
+
+# ---------------------------------------------------------------------------
+# IndexShare group
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,L,k", [("tiny", 1024, 64), ("prefill16k", 1200, 256), ("prefill128k", 2500, 2048)])
+def test_layer_group_shares_full_index_set(name, L, k):
+    cfg = synth.get_config(name, L=L, Lq=L, topk=k)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(4)]
+    idx, outs = dsa.layer_group(ind, layers, k, out_dtype=torch.float32)
+    idx_alone = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    assert torch.equal(idx, idx_alone)
+    for l in range(4):                                                # Shared = standalone on idx_full
+        assert torch.equal(outs[l], dsa.sparse_attn(layers[l], idx, out_dtype=torch.float32))
+    # oracle on sampled rows: index sets within the band, attention within the bar
+    ora = indexer_to_oracle(ind)
+    rows = [0, k - 1, min(k, L - 1), L // 2, L - 1]
+    sc = _oracle_rows(ora, 0, rows, L, L)
+    ref = oracle.topk_rows(sc, [r + 1 for r in rows], k)
+    ok, _, msg = index_sets_agree(idx.cpu().numpy()[0][rows], ref, sc, [r + 1 for r in rows], k,
+                                  TAU[cfg.idx_dtype])
+    assert ok, msg
+    for l in (0, 3):
+        _attn_check(layers[l], idx.cpu().numpy(), outs[l], None, rows)
