@@ -44,7 +44,7 @@ int check_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx,
   if (in->out_dtype != DSA_F32 && in->out_dtype != in->dtype) return DSA_ERR_DTYPE;
   switch (in->dtype) {
     case DSA_BF16:
-      if (in->H < 16 || in->H > 128 || (in->H % 16) != 0 || in->Hkv != 1 || in->Dqk != 576 || in->Dv != 512)
+      if (in->H < 16 || in->H > 64 || (in->H % 16) != 0 || in->Hkv != 1 || in->Dqk != 576 || in->Dv != 512)
         return DSA_ERR_SHAPE;
       if (in->v != in->k || in->v_row_stride != in->k_row_stride) return DSA_ERR_SHAPE;
       if (in->k_row_stride < 576 || (in->k_row_stride % 8) != 0) return DSA_ERR_ALIGN;

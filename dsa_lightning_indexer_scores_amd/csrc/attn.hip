@@ -9,12 +9,19 @@
 //
 // MLA kernel: one workgroup per (query row group, key split); a row group is the nq
 // queries that share one idx row (nq = 1, or the MTP draft queries).  Each wave owns
-// 16 heads of one query.  Per 32-key block the workgroup gathers the 32 selected latent
-// rows (1152 B each) into LDS once; every wave then computes
-//   S^T[key, head] = K . Q^T  (bf16 MFMA 16x16x32, K from LDS, Q^T in registers),
-// an online softmax per head (each lane owns one head), and
-//   O^T[dv, head] += V^T . P^T  (V^T read from the row-major LDS tile with the gfx950
-// transposing LDS load; P^T straight from the S^T accumulators).
+// 16 heads of one query.  Keys are processed in blocks of 16 selected positions: the
+// block's 16 latent rows (18 KB) are gathered straight into LDS with direct-to-LDS loads
+// (global_load_lds_dwordx4), double-buffered so that block n+1 is in flight while block n
+// is computed; the idx row is read two blocks ahead.  Per block every wave computes
+//   S^T[key, head] = K . Q^T  (bf16 MFMA 16x16x32, K from LDS, Q^T held in registers),
+// an online softmax per head (each lane owns one head; the running maximum is only
+// raised when it grows by more than 2^8, so the O rescale is rare), and
+//   O^T[dv, head] += V^T . P^T  (one 16x16x32 MFMA per 16 dims: the K=32 slots carry the
+// 16 keys twice, once with bf16(p) and once with the bf16 residual p - bf16(p), so P
+// enters with ~16 bits; V^T comes from the row-major LDS tile through the transposing
+// LDS read ds_read_b64_tr_b16).
+// LDS rows are stored with the 16-byte chunks of each group of 8 XOR-swizzled by
+// (row/2) % 8, so the 16 rows read by one MFMA operand fall in distinct banks.
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
 #include "../../include/dsa.h"
@@ -23,15 +30,35 @@ namespace dsa {
 
 constexpr int kMlaD = 576;
 constexpr int kMlaDv = 512;
-constexpr int kBlk = 32;                       // keys per block
-constexpr int kLdsRow = kMlaD * 2 + 16;        // padded LDS row (bytes)
-constexpr int kPieces = kMlaD * 2 / 16;        // 72 x 16 B per row
+constexpr int kBlk = 16;                        // keys per block
+constexpr int kRowBytes = kMlaD * 2;            // 1152
+constexpr int kChunks = kRowBytes / 16;         // 72 chunks of 16 B per row
+constexpr int kBlkBytes = kBlk * kRowBytes;     // 18432
+constexpr int kDmaPerBlk = kBlkBytes / 1024;    // 18 wave-wide 1 KB direct-to-LDS loads
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
+
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's bytes land at
+// lds + size * l.  Issued through asm so that the compiler neither tracks their LDS
+// writes (it would otherwise wait for them before unrelated LDS reads of the other
+// buffer) nor counts them; the kernel waits for them explicitly with s_waitcnt vmcnt(0).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+__device__ __forceinline__ void dma_16(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory");
+}
+__device__ __forceinline__ void dma_4(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory");
+}
+
+// LDS chunk slot of global 16-byte chunk c of block row r (an involution).
+__device__ __forceinline__ int swz(int r, int c) { return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7)); }
 
 struct MlaParams {
   AttnArgs a;
@@ -43,30 +70,80 @@ struct MlaParams {
   float* part_ml;    // [n_groups*nq*H][n_split][2]
 };
 
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaParams P) {
-  __shared__ __attribute__((aligned(16))) uint8_t kv[kBlk * kLdsRow];
+// NW waves per workgroup; DVS = slices of the 512 value dims per (query, head tile):
+// DVS = 2 halves the output accumulators a wave holds (16 heads x 256 dims) so that two
+// or three waves fit per SIMD without spills; the S^T tile is then computed by both
+// slices.  WPE = minimum waves per SIMD the register allocation must allow.
+template <int NW, int DVS, int WPE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
+void mla_attn_kernel(MlaParams P) {
+  constexpr int kDvPer = kMlaDv / DVS;          // value dims per wave
+  constexpr int kDt = kDvPer / 16;              // 16-dim output tiles per wave
+  constexpr int kSlotsPerWave = (kDmaPerBlk + NW - 1) / NW;
+  constexpr int kDummy = kSlotsPerWave * NW - kDmaPerBlk;   // padding slots (fixed counts)
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kBlkBytes + kDummy * 1024];
+  __shared__ int keyring[3][64];            // idx entries of blocks (ring of 3)
   const AttnArgs& a = P.a;
-  const int NT = NW * 64;
-  const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6, g = lane >> 4, r16 = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv_id = uniform(tid >> 6);      // wave index, kept in a scalar register
   const int hpq = a.H / 16;                 // head tiles per query
-  const int grp = blockIdx.x;
+  const int wpq = hpq * DVS;                // waves per query
+  // XCD-aware order: consecutive workgroup ids go to different XCDs; give each XCD a
+  // contiguous range of row groups (neighbouring queries share many selected rows).
+  const int ng = P.n_groups;
+  int grp;
+  {
+    const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+    const int per = ng >> 3, rem = ng & 7;
+    grp = (xcd < rem) ? xcd * (per + 1) + j : rem * (per + 1) + (xcd - rem) * per + j;
+  }
   const int split = blockIdx.y;
   const int qpl = a.Lq / P.nq;              // row groups per sequence
   const int b = grp / qpl;
-  const int qi = wv_id / hpq;               // query of this wave within the group
-  const int ht = wv_id - qi * hpq;
-  const int i = (grp - b * qpl) * P.nq + qi;  // query index within the sequence
-  const bool wave_active = wv_id < P.nq * hpq;
+  const int qi = wv_id / wpq;
+  const int wr = wv_id - qi * wpq;
+  const int ht = wr % hpq;                  // head tile
+  const int ds = wr / hpq;                  // value-dim slice
+  const int i = (grp - b * qpl) * P.nq + qi;
+  const bool wave_active = wv_id < P.nq * wpq;
   const int32_t* idx_row = a.idx_q_stride
                                ? a.idx + (size_t)b * a.Lq * a.idx_q_stride + (size_t)((grp - b * qpl) * P.nq) * a.idx_q_stride
                                : a.idx + (size_t)b * a.topk;
-  // (with a per-query idx row, nq == 1 so the group's first query is the query itself)
-  const int blk_begin = split * P.blocks_per_split;
   const int n_blk_total = (a.topk + kBlk - 1) / kBlk;
+  const int blk_begin = split * P.blocks_per_split;
   const int blk_end = min(n_blk_total, blk_begin + P.blocks_per_split);
+  const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride * 2;
+  const size_t row_bytes = (size_t)a.k_row_stride * 2;
 
-  const uint16_t* kvbase = reinterpret_cast<const uint16_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride;
+  // key of entry r of a block (from the LDS ring); -1 if padding / out of range
+  auto block_key = [&](int blk, int r) -> int {
+    const int pos = blk * kBlk + r;
+    const int key = keyring[(blk - blk_begin) % 3][r];
+    return (pos < a.topk && key >= 0 && key < a.Lk) ? key : -1;
+  };
+  // idx entries of a block into its ring slot (one wave; lanes past the block read
+  // clamped in-range positions that are never used)
+  auto issue_keys = [&](int blk) {
+    if (wv_id == 0) {
+      const int pos = min(blk * kBlk + lane, a.topk - 1);
+      dma_4(idx_row + pos, lds_offset(&keyring[(blk - blk_begin) % 3][0]));
+    }
+  };
+  // the block's 16 latent rows into kvs[buf] (invalid rows read row 0 and are masked).
+  // Every wave issues the same number of loads; padding slots fill a dummy area.
+  auto issue_rows = [&](int blk, int buf) {
+#pragma unroll
+    for (int u = 0; u < kSlotsPerWave; ++u) {
+      const int j = wv_id + u * NW;
+      const int piece = j * 64 + lane;
+      const int r = min(piece / kChunks, kBlk - 1);
+      const int cs = piece - (piece / kChunks) * kChunks;
+      int key = block_key(blk, r);
+      key = key < 0 ? 0 : key;
+      const uint8_t* src = kvbase + (size_t)key * row_bytes + (j < kDmaPerBlk ? 16 * swz(r, cs) : 0);
+      dma_16(src, lds_offset(&kvs[buf][j * 1024]));
+    }
+  };
 
   // Q^T operand: head h, dims [32 ks + 8 g, +8)
   const int h = ht * 16 + r16;
@@ -78,124 +155,105 @@ __global__ __launch_bounds__(NW * 64) void mla_attn_kernel(MlaParams P) {
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) qop[ks] = qrow[4 * ks + g];
   }
-  f32x4 o[32];
+  f32x4 o[kDt];
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_use = -INFINITY, l_lane = 0.f;
   const float sl2 = a.sm_scale * kLog2e;
+  // Complete the operand loads here: otherwise the compiler waits for them inside the
+  // loop, where the counter also covers the in-flight row gather.
+  __builtin_amdgcn_s_waitcnt(0);
+
+  if (blk_begin < blk_end) {
+    issue_keys(blk_begin);
+    if (blk_begin + 1 < blk_end) issue_keys(blk_begin + 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    issue_rows(blk_begin, 0);
+  }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
-    const int kb0 = blk * kBlk;
-    // gather the block's latent rows (invalid entries read row 0 and are masked below)
-#pragma unroll 2
-    for (int p0 = 0; p0 < kBlk * kPieces; p0 += NT * 6) {
-      i32x4 tmp[6];
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        const int p = p0 + u * NT + tid;
-        tmp[u] = i32x4{0, 0, 0, 0};
-        if (p < kBlk * kPieces) {
-          const int rr = p / kPieces, c = p - rr * kPieces;
-          const int pos = kb0 + rr;
-          int key = pos < a.topk ? idx_row[pos] : -1;
-          if (key < 0 || key >= a.Lk) key = 0;
-          tmp[u] = *reinterpret_cast<const i32x4*>(kvbase + (size_t)key * a.k_row_stride + 8 * c);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 6; ++u) {
-        const int p = p0 + u * NT + tid;
-        if (p < kBlk * kPieces) {
-          const int rr = p / kPieces, c = p - rr * kPieces;
-          *reinterpret_cast<i32x4*>(&kv[rr * kLdsRow + 16 * c]) = tmp[u];
-        }
-      }
-    }
-    __syncthreads();
+    const int buf = (blk - blk_begin) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of blk, keys of blk+1
+    __syncthreads();                                     // visible to all; buffers free
+    if (blk + 2 < blk_end) issue_keys(blk + 2);
+    if (blk + 1 < blk_end) issue_rows(blk + 1, buf ^ 1);
 
     if (wave_active) {
-      // S^T for keys [0,16) and [16,32) of the block
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      const uint8_t* kb = kvs[buf];
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(&kv[r16 * kLdsRow + (32 * ks + 8 * g) * 2]);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(&kv[(16 + r16) * kLdsRow + (32 * ks + 8 * g) * 2]);
-        s0 = mfma_bf16_16x16x32(k0, qop[ks], s0);
-        s1 = mfma_bf16_16x16x32(k1, qop[ks], s1);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + r16 * kRowBytes + 16 * swz(r16, 4 * ks + g));
+        s = mfma_bf16_16x16x32(kop, qop[ks], s);
       }
-      // lane holds head h, keys 4g+i (s0) and 16+4g+i (s1)
-      float sv[8];
+      // lane holds head h, keys 4g+j of the block
+      float sv[4];
       float bmax = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = (j < 4) ? (4 * g + j) : (16 + 4 * g + j - 4);
-        const int pos = kb0 + kk;
-        const int key = pos < a.topk ? idx_row[pos] : -1;
-        const bool valid = key >= 0 && key < a.Lk;
-        const float raw = (j < 4) ? s0[j] : s1[j - 4];
-        sv[j] = valid ? raw * sl2 : -INFINITY;
+      for (int j = 0; j < 4; ++j) {
+        const bool valid = block_key(blk, 4 * g + j) >= 0;
+        sv[j] = valid ? s[j] * sl2 : -INFINITY;
         bmax = fmaxf(bmax, sv[j]);
       }
       bmax = wave_max16x4(bmax);
-      const float m_new = fmaxf(m_run, bmax);
-      const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
-      // P is applied as bf16 hi + lo parts (p = hi + lo + O(2^-16 p)): a single bf16
-      // rounding of p would cost up to 2^-8 relative on the dominant keys.
-      float psum = 0.f;
-      bf16x8 pb, pl;
+      const bool need = bmax > m_use + kRescaleGap;
+      if (ballot(need)) {
+        const float alpha = need ? (m_use == -INFINITY ? 0.f : exp2f(m_use - bmax)) : 1.f;
+        if (need) m_use = bmax;
+        l_lane *= alpha;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float pj = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - m_new);
-        psum += pj;
+        for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
+      }
+      bf16x8 pb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pj = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - m_use);
+        l_lane += pj;
         const __bf16 hi = (__bf16)pj;
         pb[j] = hi;
-        pl[j] = (__bf16)(pj - (float)hi);
+        pb[j + 4] = (__bf16)(pj - (float)hi);
       }
-      psum = wave_sum16x4(psum);
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
+      // O^T += V^T . P^T over the block's 16 keys (each key twice: hi and lo part of p)
+      const int vrow = 4 * g + (r16 >> 2);
+      const uint8_t* vbase = kb + vrow * kRowBytes + 8 * (r16 & 1);
+      const int c0 = 2 * kDt * ds + ((r16 & 3) >> 1);
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) o[dt] *= alpha;
-      // O^T += V^T . P^T ; V^T operand via transposing LDS reads
-      const int vrow0 = 4 * g + (r16 >> 2);
-      const int vcol = 4 * (r16 & 3);
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
-        const bf16x4 lo = lds_read_tr16(&kv[vrow0 * kLdsRow + (16 * dt + vcol) * 2]);
-        const bf16x4 hi = lds_read_tr16(&kv[(16 + vrow0) * kLdsRow + (16 * dt + vcol) * 2]);
-        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      for (int dt = 0; dt < kDt; ++dt) {
+        const bf16x4 v = lds_read_tr16(vbase + 16 * swz(vrow, c0 + 2 * dt));
+        const bf16x8 va = {v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]};
         o[dt] = mfma_bf16_16x16x32(va, pb, o[dt]);
-        o[dt] = mfma_bf16_16x16x32(va, pl, o[dt]);
       }
     }
-    __syncthreads();
   }
 
   if (!wave_active) return;
+  const float l_run = wave_sum16x4(l_lane);
   const size_t qh = ((size_t)b * a.Lq + i) * a.H + h;   // (query, head) row
+  const int d0 = kDvPer * ds;
   if (P.n_split == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (a.out_dtype == DSA_F32) {
-      float* orow = reinterpret_cast<float*>(a.out) + qh * kMlaDv;
+      float* orow = reinterpret_cast<float*>(a.out) + qh * kMlaDv + d0;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = o[dt] * inv;
+      for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = o[dt] * inv;
     } else {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qh * kMlaDv;
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qh * kMlaDv + d0;
 #pragma unroll
-      for (int dt = 0; dt < 32; ++dt) {
+      for (int dt = 0; dt < kDt; ++dt) {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][e] * inv);
         *reinterpret_cast<bf16x4*>(orow + 16 * dt + 4 * g) = v;
       }
     }
-    if (a.lse && g == 0) a.lse[qh] = l_run > 0.f ? (m_run + log2f(l_run)) / kLog2e : -INFINITY;
+    if (a.lse && g == 0 && ds == 0) a.lse[qh] = l_run > 0.f ? (m_use + log2f(l_run)) / kLog2e : -INFINITY;
   } else {
-    float* po = P.part_o + (qh * P.n_split + split) * kMlaDv;
+    float* po = P.part_o + (qh * P.n_split + split) * kMlaDv + d0;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
-    if (g == 0) {
-      P.part_ml[(qh * P.n_split + split) * 2 + 0] = m_run;
+    for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+    if (g == 0 && ds == 0) {
+      P.part_ml[(qh * P.n_split + split) * 2 + 0] = m_use;
       P.part_ml[(qh * P.n_split + split) * 2 + 1] = l_run;
     }
   }
@@ -290,7 +348,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }
 
 struct MlaPlan {
-  int nq, n_groups, n_split, bps;
+  int nq, dvs, nw, n_groups, n_split, bps;
   size_t off_o, off_ml, total;
 };
 
@@ -299,8 +357,11 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   p.nq = 1;
   if (idx_q_stride == 0) {  // queries of a sequence share one row: batch them per workgroup
     p.nq = Lq;
-    while (p.nq > 1 && (p.nq * (H / 16) > 8 || Lq % p.nq)) --p.nq;
+    while (p.nq > 1 && (p.nq * (H / 16) * 2 > 8 || Lq % p.nq)) --p.nq;
   }
+  // each wave holds 16 heads x 256 value dims; at most 8 waves per workgroup
+  p.dvs = 2;
+  p.nw = p.nq * (H / 16) * p.dvs;
   p.n_groups = B * (Lq / p.nq);
   const int n_blk = (k + kBlk - 1) / kBlk;
   int split = 1;
@@ -344,11 +405,9 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   P.blocks_per_split = pl.bps;
   P.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_o);
   P.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_ml);
-  const int nw = pl.nq * (a.H / 16);
   dim3 grid(pl.n_groups, pl.n_split);
-  if (nw <= 2) mla_attn_kernel<2><<<grid, 128, 0, s>>>(P);
-  else if (nw <= 4) mla_attn_kernel<4><<<grid, 256, 0, s>>>(P);
-  else mla_attn_kernel<8><<<grid, 512, 0, s>>>(P);
+  if (pl.nw <= 4) mla_attn_kernel<4, 2, 2><<<grid, 256, 0, s>>>(P);
+  else mla_attn_kernel<8, 2, 2><<<grid, 512, 0, s>>>(P);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_split == 1) return e;
   mla_combine_kernel<<<a.B * a.Lq * a.H, 128, 0, s>>>(P.part_o, P.part_ml, pl.n_split, a.out, a.out_dtype, a.lse);

@@ -102,7 +102,7 @@ typedef struct {
  *   lse  [B, Lq, H] fp32 or NULL               natural-log sum of exp(scaled logits);
  *                                              -inf for a query with no selected key
  * Query head h reads KV head h / (H / Hkv).  sm_scale multiplies q.k before softmax.
- * Supported: DSA_BF16 MLA latent form: H % 16 == 0, 16 <= H <= 128, Hkv == 1,
+ * Supported: DSA_BF16 MLA latent form: H % 16 == 0, 16 <= H <= 64, Hkv == 1,
  *            Dqk == 576, Dv == 512, v == k with v_row_stride == k_row_stride (the value
  *            is the first 512 dims of the latent row), k_row_stride a multiple of 8
  *            elements >= 576, q/k/out 16-byte aligned;
