@@ -27,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def library_path():
-    return os.path.join(_HERE, "libdsa.so")
+    """libdsa.so next to this file, or the file named by the DSA_LIBRARY variable."""
+    return os.environ.get("DSA_LIBRARY") or os.path.join(_HERE, "libdsa.so")
 
 
 class DsaError(RuntimeError):

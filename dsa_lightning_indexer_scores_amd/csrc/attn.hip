@@ -43,20 +43,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
-// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's bytes land at
-// lds + size * l.  Issued through asm so that the compiler neither tracks their LDS
-// writes (it would otherwise wait for them before unrelated LDS reads of the other
-// buffer) nor counts them; the kernel waits for them explicitly with s_waitcnt vmcnt(0).
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
-}
-__device__ __forceinline__ void dma_16(const void* gsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory");
-}
-__device__ __forceinline__ void dma_4(const void* gsrc, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory");
-}
-
 // LDS chunk slot of global 16-byte chunk c of block row r (an involution).
 __device__ __forceinline__ int swz(int r, int c) { return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7)); }
 

@@ -87,6 +87,20 @@ __device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, f
   return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
+// Direct-to-LDS loads (global_load_lds_dword / _dwordx4): lane l's bytes land at
+// lds + size * l.  Issued through asm so that the compiler neither tracks their LDS
+// writes (it would otherwise wait for them before unrelated LDS reads of the other
+// buffer) nor counts them; the kernel waits for them explicitly with s_waitcnt vmcnt(0).
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
+}
+__device__ __forceinline__ void dma_16(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory");
+}
+__device__ __forceinline__ void dma_4(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory");
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();

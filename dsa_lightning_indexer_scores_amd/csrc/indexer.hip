@@ -30,14 +30,14 @@ constexpr int kPersistentGrid = 1024;  // fixed so that workspace sizes are pure
 template <int DT> struct IdxTraits;
 template <> struct IdxTraits<DSA_BF16> {
   static constexpr int kRowBytes = 256;   // d_I = 128 bf16
-  static constexpr int kLdsStride = 272;  // +16 B: 16 consecutive rows hit distinct banks
-  static constexpr int kTokensPerWave = 2;
+  static constexpr int kTokensPerWave = 1;
 };
 template <> struct IdxTraits<DSA_FP8_E4M3> {
   static constexpr int kRowBytes = 128;   // d_I = 128 E4M3
-  static constexpr int kLdsStride = 144;
-  static constexpr int kTokensPerWave = 4;
+  static constexpr int kTokensPerWave = 2;
 };
+
+
 
 // Per-lane operand slice of one 16-row block of a d_I = 128 row: lane group g = lane/16
 // takes bytes [g * kRowBytes/4, (g+1) * kRowBytes/4).  A (queries) and B (keys) use the
@@ -62,6 +62,33 @@ __device__ __forceinline__ Op<DSA_BF16> load_op<DSA_BF16>(const uint8_t* row, in
   Op<DSA_BF16> o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) o.v[i] = p[i];
+  return o;
+}
+
+// Key tiles sit in LDS unpadded; the 16-byte chunks of a row are XOR-swizzled so that
+// the 16 rows one MFMA operand reads start in distinct banks.
+template <int DT>
+__device__ __forceinline__ int tile_chunk(int r, int c) {
+  return DT == DSA_FP8_E4M3 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+}
+// B operand (16 keys x d_I) of lane (r16, g) from a swizzled LDS key tile.
+template <int DT>
+__device__ __forceinline__ Op<DT> load_op_tile(const uint8_t* tile, int row, int g);
+template <>
+__device__ __forceinline__ Op<DSA_FP8_E4M3> load_op_tile<DSA_FP8_E4M3>(const uint8_t* tile, int row, int g) {
+  const uint8_t* r = tile + row * 128;
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, 2 * g));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, 2 * g + 1));
+  Op<DSA_FP8_E4M3> o;
+  o.v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return o;
+}
+template <>
+__device__ __forceinline__ Op<DSA_BF16> load_op_tile<DSA_BF16>(const uint8_t* tile, int row, int g) {
+  const uint8_t* r = tile + row * 256;
+  Op<DSA_BF16> o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o.v[i] = *reinterpret_cast<const bf16x8*>(r + 16 * tile_chunk<DSA_BF16>(row, 4 * g + i));
   return o;
 }
 
@@ -185,74 +212,182 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* 
 }
 
 // ---------------------------------------------------------------------------
-// Wave-level exact selection on a candidate array (global memory, ascending positions).
+// Wave-level selection on a candidate list held as two arrays in global memory:
+// keys[0..n) (uint32 order keys) and pos[0..n) (positions, ascending).  Loads are
+// issued 8 per lane at a time so that one wave keeps 512 entries in flight.
 // ---------------------------------------------------------------------------
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;          // 2048 LDS bins per wave
+constexpr int kBinsPerLane = kBins / 64;
 
-// Radix-select the k-th largest order key among buf[0..n) (n > k), 8 bits per pass.
-// Returns theta (the k-th key) and need_eq (how many entries equal to theta belong to
-// the top k: the first need_eq of them in array order).
-__device__ void wave_select(const uint2* buf, uint32_t n, uint32_t k, uint32_t* hist,
-                            uint32_t& theta, uint32_t& need_eq) {
+// Histogram of bits [shift, shift + nbits) of the keys whose higher bits equal prefix.
+__device__ void hist_pass(const uint32_t* keys, uint32_t n, uint32_t prefix, uint32_t pmask, int shift,
+                          int nbits, uint32_t* hist) {
   const int lane = lane_id();
-  uint32_t prefix = 0, pmask = 0, krem = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  const uint32_t dmask = (1u << nbits) - 1u;
+  for (int b = lane; b < kBins; b += 64) hist[b] = 0;
+  wave_lds_fence();
+  for (uint32_t base = 0; base < n; base += 512) {
+    uint32_t kk[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) hist[4 * lane + j] = 0;
-    wave_lds_fence();
-    for (uint32_t e = lane; e < n; e += 64) {
-      const uint32_t key = buf[e].x;
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      kk[j] = e < n ? keys[e] : 0u;
     }
-    wave_lds_fence();
-    const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                   h3 = hist[4 * lane + 3];
-    const uint32_t tot = h0 + h1 + h2 + h3;
-    uint32_t S = tot;  // inclusive suffix sum over lanes >= this lane
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t o = __shfl_down(S, d);
-      if (lane + d < 64) S += o;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      if (e < n && (kk[j] & pmask) == prefix) atomicAdd(&hist[(kk[j] >> shift) & dmask], 1u);
     }
-    const uint32_t above = S - tot;  // entries whose digit lies in higher lanes' bins
-    const bool here = (above < krem) && (S >= krem);
-    const uint64_t m = ballot(here);
-    const int src = __ffsll((long long)m) - 1;
-    uint32_t c = above, d;
-    if (c + h3 >= krem) d = 4 * lane + 3;
-    else { c += h3;
-      if (c + h2 >= krem) d = 4 * lane + 2;
-      else { c += h2;
-        if (c + h1 >= krem) d = 4 * lane + 1;
-        else { c += h1; d = 4 * lane; } } }
-    d = __shfl(d, src);
-    c = __shfl(c, src);
-    prefix |= d << shift;
-    pmask |= 255u << shift;
-    krem -= c;
-    wave_lds_fence();
   }
-  theta = prefix;
-  need_eq = krem;
+  wave_lds_fence();
+}
+
+// Digit d of the krem-th largest key: count(digit > d) < krem <= count(digit >= d).
+// Returns d, above = count(digit > d) and at = count(digit == d).
+__device__ void find_digit(const uint32_t* hist, uint32_t krem, uint32_t& d, uint32_t& above, uint32_t& at) {
+  const int lane = lane_id();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int j = 0; j < kBinsPerLane; ++j) tot += hist[lane * kBinsPerLane + j];
+  uint32_t S = tot;  // inclusive suffix sum over lanes >= this lane
+#pragma unroll
+  for (int dd = 1; dd < 64; dd <<= 1) {
+    const uint32_t o = __shfl_down(S, dd);
+    if (lane + dd < 64) S += o;
+  }
+  const uint32_t above_lane = S - tot;
+  const bool here = (above_lane < krem) && (S >= krem);
+  const int src = __ffsll((long long)ballot(here)) - 1;
+  uint32_t c = above_lane, dig = 0, h = 0;
+  for (int j = kBinsPerLane - 1; j >= 0; --j) {
+    h = hist[lane * kBinsPerLane + j];
+    dig = lane * kBinsPerLane + j;
+    if (c + h >= krem) break;
+    c += h;
+  }
+  d = __shfl(dig, src);
+  above = __shfl(c, src);
+  at = __shfl(h, src);
+  wave_lds_fence();
+}
+
+// Exact k-th largest key theta among keys[0..n) (n > k) and need_eq, the number of
+// entries equal to theta in the top k (the first need_eq of them in array order).
+__device__ void select_exact(const uint32_t* keys, uint32_t n, uint32_t k, uint32_t* hist, uint32_t& theta,
+                             uint32_t& need_eq) {
+  uint32_t prefix = 0, pmask = 0, krem = k, d, above, at;
+  hist_pass(keys, n, prefix, pmask, 21, 11, hist);
+  find_digit(hist, krem, d, above, at);
+  prefix = d << 21; pmask = 0x7FFu << 21; krem -= above;
+  hist_pass(keys, n, prefix, pmask, 10, 11, hist);
+  find_digit(hist, krem, d, above, at);
+  prefix |= d << 10; pmask |= 0x7FFu << 10; krem -= above;
+  hist_pass(keys, n, prefix, pmask, 0, 10, hist);
+  find_digit(hist, krem, d, above, at);
+  theta = prefix | d;
+  need_eq = krem - above;
 }
 
 // In-place stable compaction keeping keys > theta and the first need_eq keys == theta.
-__device__ uint32_t wave_compact(uint2* buf, uint32_t n, uint32_t theta, uint32_t need_eq) {
+__device__ uint32_t compact_exact(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, uint32_t need_eq) {
   const int lane = lane_id();
   uint32_t out = 0, eq_seen = 0;
-  for (uint32_t base = 0; base < n; base += 64) {
-    const uint32_t e = base + lane;
-    const bool v = e < n;
-    const uint2 x = v ? buf[e] : make_uint2(0u, 0u);
-    const bool gt = v && x.x > theta;
-    const bool eq = v && x.x == theta;
-    const uint64_t meq = ballot(eq);
-    const bool take = gt || (eq && eq_seen + rank_below(meq) < need_eq);
-    const uint64_t mt = ballot(take);
-    if (take) buf[out + rank_below(mt)] = x;  // destination <= e: never ahead of reads
-    out += popc64(mt);
-    eq_seen += popc64(meq);
+  for (uint32_t base = 0; base < n; base += 512) {
+    uint32_t kk[8], pp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      kk[j] = e < n ? keys[e] : 0u;
+      pp[j] = e < n ? pos[e] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      const bool v = e < n;
+      const bool gt = v && kk[j] > theta;
+      const bool eq = v && kk[j] == theta;
+      const uint64_t meq = ballot(eq);
+      const bool take = gt || (eq && eq_seen + rank_below(meq) < need_eq);
+      const uint64_t mt = ballot(take);
+      if (take) {  // destination <= e: never ahead of the entries still to be read
+        keys[out + rank_below(mt)] = kk[j];
+        pos[out + rank_below(mt)] = pp[j];
+      }
+      out += popc64(mt);
+      eq_seen += popc64(meq);
+    }
   }
   return out;
+}
+
+// In-place stable compaction keeping every key >= th.
+__device__ uint32_t compact_ge(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t th) {
+  const int lane = lane_id();
+  uint32_t out = 0;
+  for (uint32_t base = 0; base < n; base += 512) {
+    uint32_t kk[8], pp[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      kk[j] = e < n ? keys[e] : 0u;
+      pp[j] = e < n ? pos[e] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t e = base + j * 64 + lane;
+      const bool take = e < n && kk[j] >= th;
+      const uint64_t mt = ballot(take);
+      if (take) {
+        keys[out + rank_below(mt)] = kk[j];
+        pos[out + rank_below(mt)] = pp[j];
+      }
+      out += popc64(mt);
+    }
+  }
+  return out;
+}
+
+// Exact top-k of a candidate list: afterwards keys/pos[0..min(n,k)) hold the k largest
+// keys (ties to the earlier entry), in their original order.
+__device__ uint32_t reduce_to_k(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t k, uint32_t* hist) {
+  if (n <= k) return n;
+  __threadfence_block();
+  uint32_t th, ne;
+  select_exact(keys, n, k, hist, th, ne);
+  const uint32_t r = compact_exact(keys, pos, n, th, ne);
+  __threadfence_block();
+  return r;
+}
+
+// Make room in a streaming candidate list that holds n > k entries: drop every key below
+// a lower bound of the k-th largest key.  The bound is the lower edge of the 22-bit key
+// prefix that contains the k-th largest key (two histogram passes, one filtering pass);
+// when that prefix holds too many keys the exact selection is used.  Returns the new
+// count; theta receives the bound (the streaming filter then admits keys > theta: the
+// list keeps at least k keys >= theta that precede any later one, so a later key equal
+// to theta cannot enter the top k).
+__device__ uint32_t shrink_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t k, uint32_t keep_max,
+                                uint32_t* hist, uint32_t& theta) {
+  __threadfence_block();
+  uint32_t d1, a1, h1, d2, a2, h2;
+  hist_pass(keys, n, 0u, 0u, 21, 11, hist);
+  find_digit(hist, k, d1, a1, h1);
+  hist_pass(keys, n, d1 << 21, 0x7FFu << 21, 10, 11, hist);
+  find_digit(hist, k - a1, d2, a2, h2);
+  uint32_t r;
+  if (a1 + a2 + h2 <= keep_max) {
+    theta = (d1 << 21) | (d2 << 10);
+    r = compact_ge(keys, pos, n, theta);
+  } else {
+    uint32_t prefix = (d1 << 21) | (d2 << 10), krem = k - a1 - a2, d3, a3, h3;
+    hist_pass(keys, n, prefix, 0x3FFFFFu << 10, 0, 10, hist);
+    find_digit(hist, krem, d3, a3, h3);
+    theta = prefix | d3;
+    r = compact_exact(keys, pos, n, theta, krem - a3);
+  }
+  __threadfence_block();
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -265,29 +400,33 @@ struct FusedParams {
   IndexerArgs a;
   int k, cap, S, seg_len, nqb, n_items;
   int32_t* idx;
-  uint2* rowbuf;
-  uint2* seg_out;
-  int32_t* seg_cnt;
+  uint32_t* row_keys;   // [grid * TQ * cap]
+  uint32_t* row_pos;
+  uint32_t* seg_keys;   // [B * Lq * S * k]   (S > 1)
+  uint32_t* seg_pos;
+  int32_t* seg_cnt;     // [B * Lq * S]
   int* counter;
 };
 
 template <int DT, int HB>
-__global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void indexer_topk_kernel(FusedParams P) {
   constexpr int RB = IdxTraits<DT>::kRowBytes;
-  constexpr int LS = IdxTraits<DT>::kLdsStride;
   constexpr int TW = IdxTraits<DT>::kTokensPerWave;
   constexpr int TQ = 4 * TW;
   constexpr int H_I = HB * 16;
-  constexpr int kChunks = RB / 16;                 // 16-byte pieces per key row
-  constexpr int kPerThread = 64 * kChunks / 256;   // pieces each thread stages per tile
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileKeys * LS];
-  __shared__ float kscl[2][kTileKeys];
+  constexpr int kChunks = RB / 16;                 // 16-byte chunks per key row
+  constexpr int kTileBytes = kTileKeys * RB;
+  constexpr int kDmaPerWave = kTileBytes / 1024 / 4;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float kscl[2][kTileKeys];
   __shared__ __attribute__((aligned(16))) float wsh[TQ * H_I];
-  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t hist[4][kBins];
   __shared__ int item_sh;
 
   const IndexerArgs& a = P.a;
-  const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6, g = lane >> 4;
+  const int lane = threadIdx.x & 63, g = lane >> 4;
+  const int wv_id = uniform((int)(threadIdx.x >> 6));
   const bool fp8 = (DT == DSA_FP8_E4M3);
 
   for (;;) {
@@ -306,6 +445,23 @@ __global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
     const int s_lo = seg * P.seg_len;
     const int s_hi = min(min(a.Lk, s_lo + P.seg_len), p_max + 1);
     const int n_tiles = s_hi > s_lo ? (s_hi - s_lo + kTileKeys - 1) / kTileKeys : 0;
+
+    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * RB;
+    const float* kscale = fp8 ? a.k_scale + (size_t)b * a.Lk : nullptr;
+    // key tile [s0, s0 + 64) into ktile[buf] by direct-to-LDS loads (rows past Lk read
+    // the last key; they are never admitted)
+    auto issue_tile = [&](int s0, int buf) {
+#pragma unroll
+      for (int u = 0; u < kDmaPerWave; ++u) {
+        const int j = wv_id + 4 * u;
+        const int piece = j * 64 + lane;
+        const int row = piece / kChunks;
+        const int cs = piece - row * kChunks;
+        const int key = min(s0 + row, a.Lk - 1);
+        dma_16(kbase + (size_t)key * RB + 16 * tile_chunk<DT>(row, cs), lds_offset(&ktile[buf][j * 1024]));
+      }
+      if (fp8 && wv_id == 0) dma_4(kscale + min(s0 + lane, a.Lk - 1), lds_offset(&kscl[buf][0]));
+    };
 
     // query operands of this wave's tokens (rows past Lq reuse row t0; never appended)
     Op<DT> A[TW][HB];
@@ -329,53 +485,32 @@ __global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
       }
       wsh[e] = v;
     }
-
-    const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * RB;
-    const float* kscale = fp8 ? a.k_scale + (size_t)b * a.Lk : nullptr;
-    auto load_piece = [&](int s0, int piece) -> i32x4 {
-      const int key = piece / kChunks, c = piece - key * kChunks;
-      const int s = min(s0 + key, a.Lk - 1);
-      return *reinterpret_cast<const i32x4*>(kbase + (size_t)s * RB + 16 * c);
-    };
-    auto store_piece = [&](int buf, int piece, i32x4 v) {
-      const int key = piece / kChunks, c = piece - key * kChunks;
-      *reinterpret_cast<i32x4*>(&ktile[buf][key * LS + 16 * c]) = v;
-    };
+    // complete these loads here, not inside the tile loop where the counter also
+    // covers the in-flight tile loads
+    __builtin_amdgcn_s_waitcnt(0);
 
     uint32_t theta[TW], cnt[TW];
-    uint2* rb[TW];
+    uint32_t* rk[TW];
+    uint32_t* rp[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
       theta[tt] = 0u;
       cnt[tt] = 0u;
-      rb[tt] = P.rowbuf + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
+      rk[tt] = P.row_keys + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
+      rp[tt] = P.row_pos + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
     }
 
-    if (n_tiles > 0) {
-#pragma unroll
-      for (int j = 0; j < kPerThread; ++j) {
-        const int piece = threadIdx.x + 256 * j;
-        store_piece(0, piece, load_piece(s_lo, piece));
-      }
-      if (fp8 && threadIdx.x < kTileKeys) kscl[0][threadIdx.x] = kscale[min(s_lo + (int)threadIdx.x, a.Lk - 1)];
-    }
-    __syncthreads();
-
+    if (n_tiles > 0) issue_tile(s_lo, 0);
     for (int it = 0; it < n_tiles; ++it) {
       const int s0 = s_lo + it * kTileKeys;
       const int cur = it & 1;
-      const bool more = it + 1 < n_tiles;
-      i32x4 pre[kPerThread];
-      float pre_sc = 0.f;
-      if (more) {
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) pre[j] = load_piece(s0 + kTileKeys, threadIdx.x + 256 * j);
-        if (fp8 && threadIdx.x < kTileKeys) pre_sc = kscale[min(s0 + kTileKeys + (int)threadIdx.x, a.Lk - 1)];
-      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile has landed
+      __syncthreads();                                     // ... for every wave; other buffer free
+      if (it + 1 < n_tiles) issue_tile(s0 + kTileKeys, cur ^ 1);
 
       Op<DT> Bk[4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) Bk[kb] = load_op<DT>(&ktile[cur][(kb * 16 + (lane & 15)) * LS], g);
+      for (int kb = 0; kb < 4; ++kb) Bk[kb] = load_op_tile<DT>(ktile[cur], kb * 16 + (lane & 15), g);
       const float ks = fp8 ? kscl[cur][lane] : 1.f;
       const int s = s0 + lane;
 
@@ -391,25 +526,16 @@ __global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
         const bool pred = (s <= p_t[tt]) && (s < s_hi) && (key > theta[tt]);
         const uint64_t m = ballot(pred);
         if (m) {
-          if (pred) rb[tt][cnt[tt] + rank_below(m)] = make_uint2(key, (uint32_t)s);
-          cnt[tt] += popc64(m);
-          if (cnt[tt] > (uint32_t)(P.cap - kTileKeys)) {
-            __threadfence_block();
-            uint32_t th, ne;
-            wave_select(rb[tt], cnt[tt], (uint32_t)P.k, hist[wv_id], th, ne);
-            cnt[tt] = wave_compact(rb[tt], cnt[tt], th, ne);
-            theta[tt] = th;
-            __threadfence_block();
+          if (pred) {
+            rk[tt][cnt[tt] + rank_below(m)] = key;
+            rp[tt][cnt[tt] + rank_below(m)] = (uint32_t)s;
           }
+          cnt[tt] += popc64(m);
+          if (cnt[tt] > (uint32_t)(P.cap - kTileKeys))
+            cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
+                                  hist[wv_id], theta[tt]);
         }
       }
-
-      if (more) {
-#pragma unroll
-        for (int j = 0; j < kPerThread; ++j) store_piece(cur ^ 1, threadIdx.x + 256 * j, pre[j]);
-        if (fp8 && threadIdx.x < kTileKeys) kscl[cur ^ 1][threadIdx.x] = pre_sc;
-      }
-      __syncthreads();
     }
 
     // finalize this wave's rows
@@ -418,19 +544,18 @@ __global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
     for (int tt = 0; tt < TW; ++tt) {
       const int t = t0 + wv_id * TW + tt;
       if (t >= a.Lq) continue;
-      if (cnt[tt] > (uint32_t)P.k) {
-        uint32_t th, ne;
-        wave_select(rb[tt], cnt[tt], (uint32_t)P.k, hist[wv_id], th, ne);
-        cnt[tt] = wave_compact(rb[tt], cnt[tt], th, ne);
-        __threadfence_block();
-      }
+      cnt[tt] = reduce_to_k(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id]);
       const size_t row = (size_t)b * a.Lq + t;
       if (P.S == 1) {
         int32_t* out = P.idx + row * P.k;
-        for (int j = lane; j < P.k; j += 64) out[j] = j < (int)cnt[tt] ? (int32_t)rb[tt][j].y : -1;
+        for (int j = lane; j < P.k; j += 64) out[j] = j < (int)cnt[tt] ? (int32_t)rp[tt][j] : -1;
       } else {
-        uint2* out = P.seg_out + (row * P.S + seg) * P.k;
-        for (int j = lane; j < (int)cnt[tt]; j += 64) out[j] = rb[tt][j];
+        uint32_t* ok = P.seg_keys + (row * P.S + seg) * P.k;
+        uint32_t* op = P.seg_pos + (row * P.S + seg) * P.k;
+        for (int j = lane; j < (int)cnt[tt]; j += 64) {
+          ok[j] = rk[tt][j];
+          op[j] = rp[tt][j];
+        }
         if (lane == 0) P.seg_cnt[row * P.S + seg] = (int32_t)cnt[tt];
       }
     }
@@ -439,35 +564,36 @@ __global__ __launch_bounds__(256) void indexer_topk_kernel(FusedParams P) {
 
 // Merge of per-segment top-k lists (segments are in position order, so their
 // concatenation is in ascending position order).  One wave per query row.
-__global__ __launch_bounds__(256) void merge_segments_kernel(uint2* seg_out, const int32_t* seg_cnt,
-                                                             int rows, int S, int k, int32_t* idx) {
-  __shared__ uint32_t hist[4][256];
+__global__ __launch_bounds__(256) void merge_segments_kernel(uint32_t* seg_keys, uint32_t* seg_pos,
+                                                             const int32_t* seg_cnt, int rows, int S, int k,
+                                                             int32_t* idx) {
+  __shared__ uint32_t hist[4][kBins];
   const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wv_id;
   if (row >= rows) return;
-  uint2* base = seg_out + (size_t)row * S * k;
+  uint32_t* bk = seg_keys + (size_t)row * S * k;
+  uint32_t* bp = seg_pos + (size_t)row * S * k;
   // pack the lists contiguously at the start of the row's region (moves only downwards)
   uint32_t n = 0;
   for (int sg = 0; sg < S; ++sg) {
     const uint32_t c = (uint32_t)seg_cnt[(size_t)row * S + sg];
-    const uint2* src = base + (size_t)sg * k;
     for (uint32_t j0 = 0; j0 < c; j0 += 64) {
       const uint32_t j = j0 + lane;
-      uint2 v = make_uint2(0u, 0u);
-      if (j < c) v = src[j];
-      if (j < c) base[n + j] = v;
+      uint32_t kk = 0, pp = 0;
+      if (j < c) {
+        kk = bk[(size_t)sg * k + j];
+        pp = bp[(size_t)sg * k + j];
+      }
+      if (j < c) {
+        bk[n + j] = kk;
+        bp[n + j] = pp;
+      }
     }
     n += c;
   }
-  __threadfence_block();
-  if (n > (uint32_t)k) {
-    uint32_t th, ne;
-    wave_select(base, n, (uint32_t)k, hist[wv_id], th, ne);
-    n = wave_compact(base, n, th, ne);
-    __threadfence_block();
-  }
+  n = reduce_to_k(bk, bp, n, (uint32_t)k, hist[wv_id]);
   int32_t* out = idx + (size_t)row * k;
-  for (int j = lane; j < k; j += 64) out[j] = j < (int)n ? (int32_t)base[j].y : -1;
+  for (int j = lane; j < k; j += 64) out[j] = j < (int)n ? (int32_t)bp[j] : -1;
 }
 
 __global__ void zero_ints_kernel(int* p, int n) {
@@ -528,10 +654,10 @@ static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
   p.cap = topk_buffer_capacity(k);
   size_t off = 256;  // work counter
   p.off_rowbuf = off;
-  off += (size_t)p.grid * p.TQ * p.cap * sizeof(uint2);
+  off += (size_t)p.grid * p.TQ * p.cap * sizeof(uint32_t) * 2;
   off = (off + 255) / 256 * 256;
   p.off_seg = off;
-  if (S > 1) off += (size_t)B * Lq * S * k * sizeof(uint2);
+  if (S > 1) off += (size_t)B * Lq * S * k * sizeof(uint32_t) * 2;
   off = (off + 255) / 256 * 256;
   p.off_cnt = off;
   if (S > 1) off += (size_t)B * Lq * S * sizeof(int32_t);
@@ -567,8 +693,10 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.nqb = pl.nqb;
   P.n_items = pl.n_items;
   P.idx = idx;
-  P.rowbuf = reinterpret_cast<uint2*>(w8 + pl.off_rowbuf);
-  P.seg_out = reinterpret_cast<uint2*>(w8 + pl.off_seg);
+  P.row_keys = reinterpret_cast<uint32_t*>(w8 + pl.off_rowbuf);
+  P.row_pos = P.row_keys + (size_t)pl.grid * pl.TQ * pl.cap;
+  P.seg_keys = reinterpret_cast<uint32_t*>(w8 + pl.off_seg);
+  P.seg_pos = P.seg_keys + (size_t)a.B * a.Lq * pl.S * k;
   P.seg_cnt = reinterpret_cast<int32_t*>(w8 + pl.off_cnt);
   P.counter = reinterpret_cast<int*>(w8);
   zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 1);
@@ -578,7 +706,7 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   if (e != hipSuccess) return e;
   if (pl.S > 1) {
     const int rows = a.B * a.Lq;
-    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_out, P.seg_cnt, rows, pl.S, k, idx);
+    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k, idx);
     e = hipGetLastError();
   }
   return e;
