@@ -21,6 +21,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",
     "-Wno-unused-function",
+    # scores and logits are finite by contract: max/min need no NaN canonicalisation
+    # (infinities keep their IEEE meaning; the softmax relies on -inf)
+    "-fno-honor-nans",
     # packed fp32 VALU forms are kept out of the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", os.path.join(HERE, "..", "include"),

@@ -37,6 +37,8 @@ constexpr int kBlkBytes = kBlk * kRowBytes;     // 18432
 constexpr int kDmaPerBlk = kBlkBytes / 1024;    // 18 wave-wide 1 KB direct-to-LDS loads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
+constexpr int kRowBufs = 3;                     // row blocks: computing, landing, issued
+constexpr int kKeyBufs = 4;                     // idx blocks held: j .. j+3
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -67,8 +69,8 @@ void mla_attn_kernel(MlaParams P) {
   constexpr int kDt = kDvPer / 16;              // 16-dim output tiles per wave
   constexpr int kSlotsPerWave = (kDmaPerBlk + NW - 1) / NW;
   constexpr int kDummy = kSlotsPerWave * NW - kDmaPerBlk;   // padding slots (fixed counts)
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kBlkBytes + kDummy * 1024];
-  __shared__ int keyring[3][64];            // idx entries of blocks (ring of 3)
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[kRowBufs][kBlkBytes + kDummy * 1024];
+  __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs][64];   // idx entries of blocks
   const AttnArgs& a = P.a;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wv_id = uniform(tid >> 6);      // wave index, kept in a scalar register
@@ -104,16 +106,15 @@ void mla_attn_kernel(MlaParams P) {
   // key of entry r of a block (from the LDS ring); -1 if padding / out of range
   auto block_key = [&](int blk, int r) -> int {
     const int pos = blk * kBlk + r;
-    const int key = keyring[(blk - blk_begin) % 3][r];
+    const int key = keyring[(blk - blk_begin) % kKeyBufs][r];
     return (pos < a.topk && key >= 0 && key < a.Lk) ? key : -1;
   };
-  // idx entries of a block into its ring slot (one wave; lanes past the block read
-  // clamped in-range positions that are never used)
+  // idx entries of a block into its ring slot.  Every wave issues the same load (same
+  // bytes to the same place) so that all waves count the same number of loads; lanes past
+  // the block read clamped in-range positions that are never used.
   auto issue_keys = [&](int blk) {
-    if (wv_id == 0) {
-      const int pos = min(blk * kBlk + lane, a.topk - 1);
-      dma_4(idx_row + pos, lds_offset(&keyring[(blk - blk_begin) % 3][0]));
-    }
+    const int pos = min(blk * kBlk + lane, a.topk - 1);
+    dma_4(idx_row + pos, lds_offset(&keyring[(blk - blk_begin) % kKeyBufs][0]));
   };
   // the block's 16 latent rows into kvs[buf] (invalid rows read row 0 and are masked).
   // Every wave issues the same number of loads; padding slots fill a dummy area.
@@ -146,46 +147,70 @@ void mla_attn_kernel(MlaParams P) {
   for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_use = -INFINITY, l_lane = 0.f;
   const float sl2 = a.sm_scale * kLog2e;
+  // loop-invariant LDS offsets (bytes within a row buffer)
+  const int k_off0 = r16 * kRowBytes + 16 * swz(r16, g);
+  const int k_off1 = r16 * kRowBytes + 16 * swz(r16, 4 + g);
+  int v_off[4];
+  {
+    const int vrow = 4 * g + (r16 >> 2);
+    const int c0 = 2 * kDt * ds + ((r16 & 3) >> 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v_off[u] = vrow * kRowBytes + 16 * swz(vrow, c0 + 2 * u) + 8 * (r16 & 1);
+  }
   // Complete the operand loads here: otherwise the compiler waits for them inside the
   // loop, where the counter also covers the in-flight row gather.
   __builtin_amdgcn_s_waitcnt(0);
 
+  // Pipeline: before computing block j, the last loads issued were [idx of j+2, rows of
+  // j+1] (kSlotsPerWave row loads last), so s_waitcnt vmcnt(kSlotsPerWave) guarantees
+  // that the rows of j and the idx of j+2 have landed while rows j+1 stay in flight.
   if (blk_begin < blk_end) {
     issue_keys(blk_begin);
     if (blk_begin + 1 < blk_end) issue_keys(blk_begin + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     issue_rows(blk_begin, 0);
+    if (blk_begin + 2 < blk_end) issue_keys(blk_begin + 2);
+    if (blk_begin + 1 < blk_end) issue_rows(blk_begin + 1, 1);
   }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
-    const int buf = (blk - blk_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of blk, keys of blk+1
-    __syncthreads();                                     // visible to all; buffers free
-    if (blk + 2 < blk_end) issue_keys(blk + 2);
-    if (blk + 1 < blk_end) issue_rows(blk + 1, buf ^ 1);
+    const int j = blk - blk_begin;
+    const int buf = j % kRowBufs;
+    if (blk + 2 < blk_end) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSlotsPerWave) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                     // landed for all; oldest buffers free
+    if (blk + 3 < blk_end) issue_keys(blk + 3);
+    if (blk + 2 < blk_end) issue_rows(blk + 2, (j + 2) % kRowBufs);
 
     if (wave_active) {
       const uint8_t* kb = kvs[buf];
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      // chunk 4ks+g of row r16 sits at 128*(ks/2) + 16*(((ks&1)*4 + g) ^ ((r16/2)&7)):
+      // two per-lane bases plus immediate offsets
+      const uint8_t* kq0 = kb + k_off0;
+      const uint8_t* kq1 = kb + k_off1;
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kb + r16 * kRowBytes + 16 * swz(r16, 4 * ks + g));
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>((ks & 1 ? kq1 : kq0) + 128 * (ks >> 1));
         s = mfma_bf16_16x16x32(kop, qop[ks], s);
       }
       // lane holds head h, keys 4g+j of the block
       float sv[4];
       float bmax = -INFINITY;
+      const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j % kKeyBufs][4 * g]);
+      const int kkv[4] = {kk4.x, kk4.y, kk4.z, kk4.w};
+      const int pos0 = blk * kBlk + 4 * g;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool valid = block_key(blk, 4 * g + j) >= 0;
-        sv[j] = valid ? s[j] * sl2 : -INFINITY;
-        bmax = fmaxf(bmax, sv[j]);
+      for (int jj = 0; jj < 4; ++jj) {
+        const bool valid = (pos0 + jj < a.topk) & ((unsigned)kkv[jj] < (unsigned)a.Lk);
+        sv[jj] = valid ? s[jj] * sl2 : -INFINITY;
+        bmax = fmaxf(bmax, sv[jj]);
       }
       bmax = wave_max16x4(bmax);
       const bool need = bmax > m_use + kRescaleGap;
       if (ballot(need)) {
-        const float alpha = need ? (m_use == -INFINITY ? 0.f : exp2f(m_use - bmax)) : 1.f;
+        const float alpha = need ? (m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_use - bmax)) : 1.f;
         if (need) m_use = bmax;
         l_lane *= alpha;
 #pragma unroll
@@ -194,20 +219,22 @@ void mla_attn_kernel(MlaParams P) {
       bf16x8 pb;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pj = (sv[j] == -INFINITY) ? 0.f : exp2f(sv[j] - m_use);
+        const float pj = (sv[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_use);
         l_lane += pj;
         const __bf16 hi = (__bf16)pj;
         pb[j] = hi;
         pb[j + 4] = (__bf16)(pj - (float)hi);
       }
       // O^T += V^T . P^T over the block's 16 keys (each key twice: hi and lo part of p)
-      const int vrow = 4 * g + (r16 >> 2);
-      const uint8_t* vbase = kb + vrow * kRowBytes + 8 * (r16 & 1);
-      const int c0 = 2 * kDt * ds + ((r16 & 3) >> 1);
+      // V^T rows for dims 16dt..16dt+15: chunk c0 + 2dt of row vrow, at
+      // v_off[dt % 4] + 128 * (dt / 4).  Each key enters twice (hi and lo part of p), so
+      // the same transposed read fills both halves of the operand.
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        const bf16x4 v = lds_read_tr16(vbase + 16 * swz(vrow, c0 + 2 * dt));
-        const bf16x8 va = {v[0], v[1], v[2], v[3], v[0], v[1], v[2], v[3]};
+        const uint8_t* vp = kb + v_off[dt & 3] + 128 * (dt >> 2);
+        const bf16x4 v0 = lds_read_tr16(vp);
+        const bf16x4 v1 = lds_read_tr16(vp);
+        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = mfma_bf16_16x16x32(va, pb, o[dt]);
       }
     }
