@@ -106,8 +106,11 @@ dsa::AttnArgs make_attn_args(const dsa_attn_in* in, int B, int Lq, int Lk, const
   return a;
 }
 
+size_t materialised_scores_bytes(int B, int Lq, int Lk) { return round_up((size_t)B * Lq * Lk * sizeof(float)); }
+size_t materialised_hist_bytes(int B, int Lq) { return round_up((size_t)B * Lq * dsa::kRowHistBins * sizeof(uint32_t)); }
+
 size_t indexer_topk_ws(int dtype, int B, int Lq, int Lk, int k) {
-  if (use_materialised(dtype, Lq)) return round_up((size_t)B * Lq * Lk * sizeof(float));
+  if (use_materialised(dtype, Lq)) return materialised_scores_bytes(B, Lq, Lk) + materialised_hist_bytes(B, Lq);
   return dsa::indexer_topk_fused_ws(B, Lq, Lk, k, dtype);
 }
 
@@ -123,9 +126,11 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
   hipError_t e;
   if (use_materialised(in->dtype, Lq)) {
     float* scores = static_cast<float*>(ws);
-    e = dsa::launch_indexer_scores(a, scores, s);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + materialised_scores_bytes(B, Lq, Lk));
+    e = dsa::launch_zero(hist, materialised_hist_bytes(B, Lq), s);
+    if (e == hipSuccess) e = dsa::launch_indexer_scores(a, scores, hist, s);
     if (e == hipSuccess)
-      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, k, idx, nullptr, s);
+      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, hist, k, idx, nullptr, s);
   } else {
     e = dsa::launch_indexer_topk_fused(a, k, idx, ws, ws_bytes, s);
   }
@@ -164,7 +169,7 @@ int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* s
   if (st != DSA_OK) return st;
   if (!scores) return DSA_ERR_ARG;
   if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
-  const hipError_t e = dsa::launch_indexer_scores(make_indexer_args(in, B, Lq, Lk), scores,
+  const hipError_t e = dsa::launch_indexer_scores(make_indexer_args(in, B, Lq, Lk), scores, nullptr,
                                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
@@ -177,7 +182,7 @@ int dsa_topk(const float* scores, int64_t row_stride, int rows, int n, const int
   if (rows <= 0 || n <= 0 || k <= 0 || k > kMaxTopkK || row_stride < n) return DSA_ERR_ARG;
   if (!aligned(scores, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)) || (n_valid && !aligned(n_valid, 4)))
     return DSA_ERR_ALIGN;
-  const hipError_t e = dsa::launch_topk_rows(scores, row_stride, rows, n, n_valid, 0, 0, k, idx, vals,
+  const hipError_t e = dsa::launch_topk_rows(scores, row_stride, rows, n, n_valid, 0, 0, nullptr, k, idx, vals,
                                              static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

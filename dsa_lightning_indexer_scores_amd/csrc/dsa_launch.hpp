@@ -24,7 +24,11 @@ inline int topk_buffer_capacity(int k) {
 }
 
 // --- indexer ---------------------------------------------------------------
-hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, hipStream_t s);
+// row_hist (optional, [B*Lq][2048] uint32, zeroed by the caller): per-row histogram of
+// the top 11 bits of the order keys of the causal scores.
+hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s);
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+constexpr int kRowHistBins = 2048;
 // Fused streaming indexer + top-k for query counts large enough to fill the GPU.
 size_t indexer_topk_fused_ws(int B, int Lq, int Lk, int k, int dtype);
 hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, void* ws,
@@ -32,8 +36,8 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
 
 // --- top-k over materialised rows -------------------------------------------
 hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, int n,
-                            const int32_t* n_valid, int causal_Lq, int causal_Lk, int k,
-                            int32_t* idx, float* vals, hipStream_t s);
+                            const int32_t* n_valid, int causal_Lq, int causal_Lk, const uint32_t* row_hist,
+                            int k, int32_t* idx, float* vals, hipStream_t s);
 
 // --- sparse attention --------------------------------------------------------
 struct AttnArgs {

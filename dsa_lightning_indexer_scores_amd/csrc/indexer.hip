@@ -137,7 +137,9 @@ __device__ __forceinline__ float tile_score(const Op<DT> (&a)[HB], const Op<DT> 
 constexpr int kRowscanChunk = 4096;
 
 template <int DT, int HB>
-__global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, float* __restrict__ scores) {
+__global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, float* __restrict__ scores,
+                                                              uint32_t* __restrict__ row_hist) {
+  __shared__ uint32_t lhist[kRowHistBins];
   constexpr int RB = IdxTraits<DT>::kRowBytes;
   const int n_chunks = (a.Lk + kRowscanChunk - 1) / kRowscanChunk;
   const int qrow = blockIdx.x / n_chunks;
@@ -162,26 +164,49 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
 
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * RB;
   const float* ksc = (DT == DSA_FP8_E4M3) ? a.k_scale + (size_t)b * a.Lk : nullptr;
-  for (int s0 = s_begin + wv_id * kTileKeys; s0 < s_end; s0 += 4 * kTileKeys) {
-    const int s = s0 + lane;
-    if (s0 > p) {  // whole tile is non-causal for this query
-      if (s < s_end) out[s] = -INFINITY;
-      continue;
-    }
-    Op<DT> Bk[4];
+  if (row_hist) {
+    for (int j = threadIdx.x; j < kRowHistBins; j += 256) lhist[j] = 0;
+    __syncthreads();
+  }
+  // software pipeline: the next tile's key operands are loaded before this tile is scored
+  auto load_tile = [&](int s0, Op<DT> (&Bk)[4]) {
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int key = min(s0 + kb * 16 + (lane & 15), a.Lk - 1);
       Bk[kb] = load_op<DT>(kbase + (size_t)key * RB, g);
     }
+  };
+  const int s_first = s_begin + wv_id * kTileKeys;
+  const int s_causal_end = min(s_end, p + 1);      // tiles starting here are all -inf
+  Op<DT> Bn[4];
+  if (s_first < s_causal_end) load_tile(s_first, Bn);
+  for (int s0 = s_first; s0 < s_end; s0 += 4 * kTileKeys) {
+    const int s = s0 + lane;
+    if (s0 >= s_causal_end) {  // whole tile is non-causal for this query
+      if (s < s_end) out[s] = -INFINITY;
+      continue;
+    }
+    Op<DT> Bk[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) Bk[kb] = Bn[kb];
+    if (s0 + 4 * kTileKeys < s_causal_end) load_tile(s0 + 4 * kTileKeys, Bn);
     float val = tile_score<DT, HB>(A, Bk, W);
     if (DT == DSA_FP8_E4M3) val *= ksc[min(s, a.Lk - 1)];
-    if (s < s_end) out[s] = (s <= p) ? val : -INFINITY;
+    const bool causal = s <= p && s < s_end;
+    if (s < s_end) out[s] = causal ? val : -INFINITY;
+    if (row_hist && causal) atomicAdd(&lhist[order_key(val) >> 21], 1u);
+  }
+  if (row_hist) {
+    __syncthreads();
+    uint32_t* rh = row_hist + (size_t)qrow * kRowHistBins;
+    for (int j = threadIdx.x; j < kRowHistBins; j += 256)
+      if (lhist[j]) atomicAdd(&rh[j], lhist[j]);
   }
 }
 
 // Reference-size fp32 path: one thread per (query, key); q row and weights in LDS.
-__global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* __restrict__ scores) {
+__global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* __restrict__ scores,
+                                                          uint32_t* __restrict__ row_hist) {
   extern __shared__ float smem[];
   const int n_chunks = (a.Lk + 255) / 256;
   const int qrow = blockIdx.x / n_chunks;
@@ -207,6 +232,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* 
       acc = fmaf(ws[j], fmaxf(d, 0.f), acc);
     }
     val = acc;
+    if (row_hist) atomicAdd(&row_hist[(size_t)qrow * kRowHistBins + (order_key(val) >> 21)], 1u);
   }
   scores[(size_t)qrow * a.Lk + s] = val;
 }
@@ -605,26 +631,38 @@ __global__ void zero_ints_kernel(int* p, int n) {
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <int DT>
-static hipError_t rowscan_dispatch(const IndexerArgs& a, float* scores, hipStream_t s) {
+static hipError_t rowscan_dispatch(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s) {
   dim3 grid((unsigned)((a.Lk + kRowscanChunk - 1) / kRowscanChunk) * (unsigned)(a.B * a.Lq));
   switch (a.H_I / 16) {
-    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores); break;
-    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores); break;
-    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores); break;
-    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores); break;
+    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
+    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
+    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
+    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, hipStream_t s) {
+__global__ void zero_words_kernel(uint32_t* p, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  zero_words_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(static_cast<uint32_t*>(p), n);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s) {
   if (a.dtype == DSA_F32) {
     dim3 grid((unsigned)((a.Lk + 255) / 256) * (unsigned)(a.B * a.Lq));
     const size_t smem = (size_t)(a.H_I * a.d_I + a.H_I) * sizeof(float);
-    indexer_f32_kernel<<<grid, 256, smem, s>>>(a, scores);
+    indexer_f32_kernel<<<grid, 256, smem, s>>>(a, scores, row_hist);
     return hipGetLastError();
   }
-  if (a.dtype == DSA_BF16) return rowscan_dispatch<DSA_BF16>(a, scores, s);
-  return rowscan_dispatch<DSA_FP8_E4M3>(a, scores, s);
+  if (a.dtype == DSA_BF16) return rowscan_dispatch<DSA_BF16>(a, scores, row_hist, s);
+  return rowscan_dispatch<DSA_FP8_E4M3>(a, scores, row_hist, s);
 }
 
 struct FusedPlan {

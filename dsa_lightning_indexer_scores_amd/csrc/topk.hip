@@ -2,28 +2,92 @@
 //
 // GLM-5.2 技术报告速览, section "IndexShare": keep the k highest indexer scores of each
 // query; GLM-5 technical report, section 3.2: the top-k operator must be deterministic.
-// One workgroup per row: an MSB-first radix select (8-bit digits, LDS histogram) finds
-// the k-th largest order key theta and how many keys equal to theta are needed; a final
-// pass in position order emits keys > theta and the first needed keys == theta, using
-// wave ballots plus a cross-wave prefix, so the output is in ascending position order
-// and identical from run to run.
+//
+// One workgroup per row.  Scores are mapped to order-preserving uint32 keys.  From a
+// 2048-bin histogram of the top 11 key bits (built by the score kernel, or by one pass
+// here) the workgroup finds the digit d1 of the k-th largest key.  A single streaming
+// read of the row then compacts, in position order, every entry whose digit is >= d1
+// into an LDS list (block-wide prefix sums keep the order); the exact k-th key theta is
+// radix-selected on the list's lower 21 bits in LDS, and a final ordered pass emits the
+// keys > theta plus the first needed keys == theta.  The output is therefore in
+// ascending position order and identical from run to run.  When the digit's bin is too
+// large for LDS, the row is processed with the same selection rule directly in global
+// memory (radix passes over the row, then an ordered emitting pass).
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
 #include "../../include/dsa.h"
 
 namespace dsa {
 
-template <int BS>
-__global__ __launch_bounds__(BS) void topk_rows_kernel(const float* __restrict__ scores, int64_t row_stride,
-                                                       int n, const int32_t* __restrict__ n_valid,
-                                                       int causal_Lq, int causal_Lk, int k,
-                                                       int32_t* __restrict__ idx, float* __restrict__ vals) {
-  constexpr int NWV = BS / 64;
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sel[2];
-  __shared__ uint32_t wsum[NWV][2];
+constexpr int kTopBins = 2048;          // histogram of key bits [31:21]
+constexpr int kTopBS = 1024;            // threads per row
+constexpr int kListCap = 8192;          // LDS candidate list (keys + positions: 64 KB)
+
+// Block-wide exclusive prefix of v (position order = thread order); returns the prefix
+// and writes the block total.  sh: scratch of kTopBS/64 words.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* sh, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) sh[w] = incl;
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTopBS / 64; ++i) {
+    const uint32_t c = sh[i];
+    if (i < w) before += c;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
+}
+
+// Digit d (0..nb-1) of the krem-th largest entry of an LDS histogram: count(> d) < krem
+// <= count(>= d).  Block-wide; returns d and count(> d).
+__device__ void block_find_digit(const uint32_t* hist, int nb, uint32_t krem, uint32_t* sh, uint32_t& d,
+                                 uint32_t& above) {
+  // each thread owns bins [tid*per, tid*per + per) ; suffix sums over threads
+  const int per = nb / kTopBS;  // 2 for 2048 bins, 1 for 1024
+  const int tid = threadIdx.x;
+  uint32_t tot = 0;
+  for (int j = 0; j < per; ++j) tot += hist[tid * per + j];
+  // suffix = total - inclusive prefix + tot
+  uint32_t all;
+  const uint32_t excl = block_excl_scan(tot, sh, all);
+  const uint32_t above_thread = all - excl - tot;   // entries in bins of higher threads
+  if (above_thread < krem && above_thread + tot >= krem) {
+    uint32_t c = above_thread;
+    int dd = tid * per;
+    for (int j = per - 1; j >= 0; --j) {
+      const uint32_t h = hist[tid * per + j];
+      if (c + h >= krem) { dd = tid * per + j; break; }
+      c += h;
+    }
+    sh[kTopBS / 64] = (uint32_t)dd;
+    sh[kTopBS / 64 + 1] = c;
+  }
+  __syncthreads();
+  d = sh[kTopBS / 64];
+  above = sh[kTopBS / 64 + 1];
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kTopBS) void topk_rows_kernel(const float* __restrict__ scores, int64_t row_stride,
+                                                          int n, const int32_t* __restrict__ n_valid,
+                                                          int causal_Lq, int causal_Lk,
+                                                          const uint32_t* __restrict__ row_hist, int k,
+                                                          int32_t* __restrict__ idx, float* __restrict__ vals) {
+  __shared__ uint32_t hist[kTopBins];
+  __shared__ uint32_t lkeys[kListCap];
+  __shared__ uint32_t lpos[kListCap];
+  __shared__ uint32_t sh[kTopBS / 64 + 2];
   const int row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6;
+  const int tid = threadIdx.x;
   const float* x = scores + (size_t)row * row_stride;
   int nv = n;
   if (n_valid) nv = n_valid[row];
@@ -33,97 +97,143 @@ __global__ __launch_bounds__(BS) void topk_rows_kernel(const float* __restrict__
   float* vout = vals ? vals + (size_t)row * k : nullptr;
 
   if (nv <= k) {
-    for (int j = tid; j < k; j += BS) {
+    for (int j = tid; j < k; j += kTopBS) {
       out[j] = j < nv ? j : -1;
       if (vout) vout[j] = j < nv ? x[j] : -INFINITY;
     }
     return;
   }
 
-  uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int j = tid; j < 256; j += BS) hist[j] = 0;
+  // histogram of the top 11 key bits
+  if (row_hist) {
+    for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = row_hist[(size_t)row * kTopBins + j];
+  } else {
+    for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = 0;
     __syncthreads();
-    for (int e = tid; e < nv; e += BS) {
-      const uint32_t key = order_key(x[e]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wv_id == 0) {
-      const uint32_t h0 = hist[4 * lane], h1 = hist[4 * lane + 1], h2 = hist[4 * lane + 2],
-                     h3 = hist[4 * lane + 3];
-      const uint32_t tot = h0 + h1 + h2 + h3;
-      uint32_t S = tot;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_down(S, d);
-        if (lane + d < 64) S += o;
-      }
-      const uint32_t above = S - tot;
-      if (above < krem && S >= krem) {  // exactly one lane
-        uint32_t c = above, d;
-        if (c + h3 >= krem) d = 4 * lane + 3;
-        else { c += h3;
-          if (c + h2 >= krem) d = 4 * lane + 2;
-          else { c += h2;
-            if (c + h1 >= krem) d = 4 * lane + 1;
-            else { c += h1; d = 4 * lane; } } }
-        sel[0] = d;
-        sel[1] = c;
-      }
-    }
-    __syncthreads();
-    prefix |= sel[0] << shift;
-    pmask |= 255u << shift;
-    krem -= sel[1];
-    __syncthreads();
+    for (int e = tid; e < nv; e += kTopBS) atomicAdd(&hist[order_key(x[e]) >> 21], 1u);
   }
-  const uint32_t theta = prefix, need_eq = krem;
+  __syncthreads();
+  uint32_t d1, a1;
+  block_find_digit(hist, kTopBins, (uint32_t)k, sh, d1, a1);
+  const uint32_t h1 = hist[d1];
 
+  uint32_t theta, need_eq;
+  if (a1 + h1 <= (uint32_t)kListCap) {
+    // ---- one streaming pass: candidates with digit >= d1 into the LDS list ----------
+    const uint32_t kmin = d1 << 21;
+    uint32_t base = 0;
+    for (int c0 = 0; c0 < nv; c0 += kTopBS * 4) {
+      const int e0 = c0 + tid * 4;
+      uint32_t kk[4];
+      uint32_t cnt = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = e0 + u;
+        kk[u] = e < nv ? order_key(x[e]) : 0u;
+        cnt += kk[u] >= kmin ? 1u : 0u;
+      }
+      uint32_t tot;
+      uint32_t o = base + block_excl_scan(cnt, sh, tot);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (kk[u] >= kmin) {
+          if (o < (uint32_t)kListCap) {   // holds by construction (o < a1 + h1)
+            lkeys[o] = kk[u];
+            lpos[o] = (uint32_t)(e0 + u);
+          }
+          ++o;
+        }
+      base += tot;
+    }
+    __syncthreads();
+    const uint32_t nl = min(base, (uint32_t)kListCap);  // == a1 + h1
+    // ---- exact selection of the remaining k - a1 among digit d1 (bits [20:0]) --------
+    uint32_t krem = (uint32_t)k - a1, d2, a2, d3, a3;
+    for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < nl; e += kTopBS)
+      if ((lkeys[e] >> 21) == d1) atomicAdd(&hist[(lkeys[e] >> 10) & 0x7FFu], 1u);
+    __syncthreads();
+    block_find_digit(hist, kTopBins, krem, sh, d2, a2);
+    krem -= a2;
+    const uint32_t pre = (d1 << 21) | (d2 << 10);
+    for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = 0;
+    __syncthreads();
+    for (uint32_t e = tid; e < nl; e += kTopBS)
+      if ((lkeys[e] >> 10) == (pre >> 10)) atomicAdd(&hist[lkeys[e] & 0x3FFu], 1u);
+    __syncthreads();
+    block_find_digit(hist, kTopBins, krem, sh, d3, a3);
+    theta = pre | d3;
+    need_eq = krem - a3;
+    // ---- ordered emit from the list ---------------------------------------------------
+    uint32_t out_n = 0, eq_seen = 0;
+    for (uint32_t c0 = 0; c0 < nl; c0 += kTopBS) {
+      const uint32_t e = c0 + tid;
+      const bool v = e < nl;
+      const uint32_t key = v ? lkeys[e] : 0u;
+      const bool gt = v && key > theta, eq = v && key == theta;
+      uint32_t eq_tot;
+      const uint32_t eq_before = eq_seen + block_excl_scan(eq ? 1u : 0u, sh, eq_tot);
+      const bool take = gt || (eq && eq_before < need_eq);
+      uint32_t t_tot;
+      const uint32_t pos = out_n + block_excl_scan(take ? 1u : 0u, sh, t_tot);
+      if (take) {
+        out[pos] = (int32_t)lpos[e];
+        if (vout) vout[pos] = x[lpos[e]];
+      }
+      out_n += t_tot;
+      eq_seen += eq_tot;
+    }
+    return;
+  }
+
+  // ---- fallback: the selection rule applied directly on the row -----------------------
+  {
+    uint32_t prefix = d1 << 21, pmask = 0x7FFu << 21, krem = (uint32_t)k - a1, d, above;
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 10 : 0;
+      const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
+      for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = 0;
+      __syncthreads();
+      for (int e = tid; e < nv; e += kTopBS) {
+        const uint32_t key = order_key(x[e]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      }
+      __syncthreads();
+      block_find_digit(hist, kTopBins, krem, sh, d, above);
+      prefix |= d << shift;
+      pmask |= dmask << shift;
+      krem -= above;
+    }
+    theta = prefix;
+    need_eq = krem;
+  }
   uint32_t out_n = 0, eq_seen = 0;
-  for (int base = 0; base < nv && out_n < (uint32_t)k; base += BS) {
-    const int e = base + tid;
+  for (int c0 = 0; c0 < nv && out_n < (uint32_t)k; c0 += kTopBS) {
+    const int e = c0 + tid;
     const bool v = e < nv;
     const float xv = v ? x[e] : 0.f;
     const uint32_t key = v ? order_key(xv) : 0u;
-    const bool gt = v && key > theta;
-    const bool eq = v && key == theta;
-    const uint64_t meq = ballot(eq);
-    if (lane == 0) wsum[wv_id][0] = popc64(meq);
-    __syncthreads();
-    uint32_t eq_before = eq_seen + rank_below(meq), eq_tot = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const uint32_t c = wsum[w][0];
-      if (w < wv_id) eq_before += c;
-      eq_tot += c;
-    }
+    const bool gt = v && key > theta, eq = v && key == theta;
+    uint32_t eq_tot;
+    const uint32_t eq_before = eq_seen + block_excl_scan(eq ? 1u : 0u, sh, eq_tot);
     const bool take = gt || (eq && eq_before < need_eq);
-    const uint64_t mt = ballot(take);
-    if (lane == 0) wsum[wv_id][1] = popc64(mt);
-    __syncthreads();
-    uint32_t pos = out_n + rank_below(mt), t_tot = 0;
-#pragma unroll
-    for (int w = 0; w < NWV; ++w) {
-      const uint32_t c = wsum[w][1];
-      if (w < wv_id) pos += c;
-      t_tot += c;
-    }
+    uint32_t t_tot;
+    const uint32_t pos = out_n + block_excl_scan(take ? 1u : 0u, sh, t_tot);
     if (take) {
       out[pos] = e;
       if (vout) vout[pos] = xv;
     }
     out_n += t_tot;
     eq_seen += eq_tot;
-    __syncthreads();
   }
 }
 
 hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, int n,
-                            const int32_t* n_valid, int causal_Lq, int causal_Lk, int k,
-                            int32_t* idx, float* vals, hipStream_t s) {
-  if (n >= 65536) topk_rows_kernel<1024><<<rows, 1024, 0, s>>>(scores, row_stride, n, n_valid, causal_Lq, causal_Lk, k, idx, vals);
-  else topk_rows_kernel<512><<<rows, 512, 0, s>>>(scores, row_stride, n, n_valid, causal_Lq, causal_Lk, k, idx, vals);
+                            const int32_t* n_valid, int causal_Lq, int causal_Lk, const uint32_t* row_hist,
+                            int k, int32_t* idx, float* vals, hipStream_t s) {
+  topk_rows_kernel<<<rows, kTopBS, 0, s>>>(scores, row_stride, n, n_valid, causal_Lq, causal_Lk, row_hist, k,
+                                           idx, vals);
   return hipGetLastError();
 }
 
