@@ -37,13 +37,16 @@ constexpr int kBlkBytes = kBlk * kRowBytes;     // 18432
 constexpr int kDmaPerBlk = kBlkBytes / 1024;    // 18 wave-wide 1 KB direct-to-LDS loads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
-constexpr int kRowBufs = 3;                     // row blocks: computing, landing, issued
-constexpr int kKeyBufs = 4;                     // idx blocks held: j .. j+3
+constexpr int kRowBufs = 2;                     // row blocks: computing, in flight
+constexpr int kKeyBufs = 3;                     // idx blocks held: j .. j+2
+constexpr int kQSteps = 18 / 2;                 // 32-dim MFMA steps per wave (half of 576)
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
+
+__device__ __forceinline__ f32x4 sp_plus(f32x4 lo_half, f32x4 hi_half) { return lo_half + hi_half; }
 
 // LDS chunk slot of global 16-byte chunk c of block row r (an involution).
 __device__ __forceinline__ int swz(int r, int c) { return (c & ~7) | ((c & 7) ^ ((r >> 1) & 7)); }
@@ -59,9 +62,11 @@ struct MlaParams {
 };
 
 // NW waves per workgroup; DVS = slices of the 512 value dims per (query, head tile):
-// DVS = 2 halves the output accumulators a wave holds (16 heads x 256 dims) so that two
-// or three waves fit per SIMD without spills; the S^T tile is then computed by both
-// slices.  WPE = minimum waves per SIMD the register allocation must allow.
+// DVS = 2 halves the output accumulators a wave holds (16 heads x 256 dims).  The two
+// slices of a head tile also split the S^T reduction: each multiplies over 288 of the 576
+// latent dims, the partial tiles are exchanged through LDS, and both add them in the same
+// order (so both hold bitwise the same S^T).  WPE = minimum waves per SIMD the register
+// allocation must allow.
 template <int NW, int DVS, int WPE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void mla_attn_kernel(MlaParams P) {
@@ -71,6 +76,7 @@ void mla_attn_kernel(MlaParams P) {
   constexpr int kDummy = kSlotsPerWave * NW - kDmaPerBlk;   // padding slots (fixed counts)
   __shared__ __attribute__((aligned(16))) uint8_t kvs[kRowBufs][kBlkBytes + kDummy * 1024];
   __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs][64];   // idx entries of blocks
+  __shared__ __attribute__((aligned(16))) f32x4 xch[2][NW][64];         // partial S^T tiles
   const AttnArgs& a = P.a;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wv_id = uniform(tid >> 6);      // wave index, kept in a scalar register
@@ -132,24 +138,28 @@ void mla_attn_kernel(MlaParams P) {
     }
   };
 
-  // Q^T operand: head h, dims [32 ks + 8 g, +8)
+  // Q^T operand: head h, dims [32 (ks + kQSteps ds) + 8 g, +8) for this wave's half
   const int h = ht * 16 + r16;
-  bf16x8 qop[18];
+  bf16x8 qop[kQSteps];
   {
     const int qq = wave_active ? i : 0;
     const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
         reinterpret_cast<const uint16_t*>(a.q) + (((size_t)b * a.Lq + qq) * a.H + (wave_active ? h : 0)) * kMlaD);
 #pragma unroll
-    for (int ks = 0; ks < 18; ++ks) qop[ks] = qrow[4 * ks + g];
+    for (int ks = 0; ks < kQSteps; ++ks) qop[ks] = qrow[4 * (ks + kQSteps * ds) + g];
   }
+  const int partner = wv_id + (ds == 0 ? hpq : -hpq);   // same head tile, other half
   f32x4 o[kDt];
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_use = -INFINITY, l_lane = 0.f;
   const float sl2 = a.sm_scale * kLog2e;
   // loop-invariant LDS offsets (bytes within a row buffer)
-  const int k_off0 = r16 * kRowBytes + 16 * swz(r16, g);
-  const int k_off1 = r16 * kRowBytes + 16 * swz(r16, 4 + g);
+  // this wave's half starts at 32-dim step kQSteps*ds (chunk 4*kQSteps*ds; kQSteps is odd,
+  // so the parity of the step index flips between the halves)
+  const int ks0 = kQSteps * ds;
+  const int k_off0 = r16 * kRowBytes + 16 * swz(r16, 4 * (ks0 & 1) + g) + 128 * (ks0 >> 1);
+  const int k_off1 = r16 * kRowBytes + 16 * swz(r16, 4 * ((ks0 + 1) & 1) + g) + 128 * ((ks0 + 1) >> 1);
   int v_off[4];
   {
     const int vrow = 4 * g + (r16 >> 2);
@@ -161,40 +171,43 @@ void mla_attn_kernel(MlaParams P) {
   // loop, where the counter also covers the in-flight row gather.
   __builtin_amdgcn_s_waitcnt(0);
 
-  // Pipeline: before computing block j, the last loads issued were [idx of j+2, rows of
-  // j+1] (kSlotsPerWave row loads last), so s_waitcnt vmcnt(kSlotsPerWave) guarantees
-  // that the rows of j and the idx of j+2 have landed while rows j+1 stay in flight.
+  // Pipeline: rows of block j+1 and the idx of block j+2 are in flight while block j is
+  // computed; every wave waits for all of its loads at the top of the block.
   if (blk_begin < blk_end) {
     issue_keys(blk_begin);
     if (blk_begin + 1 < blk_end) issue_keys(blk_begin + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     issue_rows(blk_begin, 0);
-    if (blk_begin + 2 < blk_end) issue_keys(blk_begin + 2);
-    if (blk_begin + 1 < blk_end) issue_rows(blk_begin + 1, 1);
   }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     const int j = blk - blk_begin;
     const int buf = j % kRowBufs;
-    if (blk + 2 < blk_end) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSlotsPerWave) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();                                     // landed for all; oldest buffers free
-    if (blk + 3 < blk_end) issue_keys(blk + 3);
-    if (blk + 2 < blk_end) issue_rows(blk + 2, (j + 2) % kRowBufs);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of blk, idx of blk+1
+    __syncthreads();                                     // landed for all; other buffer free
+    if (blk + 2 < blk_end) issue_keys(blk + 2);
+    if (blk + 1 < blk_end) issue_rows(blk + 1, (j + 1) % kRowBufs);
 
+    f32x4 sp = {0.f, 0.f, 0.f, 0.f};
     if (wave_active) {
       const uint8_t* kb = kvs[buf];
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
       // chunk 4ks+g of row r16 sits at 128*(ks/2) + 16*(((ks&1)*4 + g) ^ ((r16/2)&7)):
-      // two per-lane bases plus immediate offsets
+      // two per-lane bases (even/odd steps of this half) plus immediate offsets
       const uint8_t* kq0 = kb + k_off0;
       const uint8_t* kq1 = kb + k_off1;
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) {
+      for (int ks = 0; ks < kQSteps; ++ks) {
         const bf16x8 kop = *reinterpret_cast<const bf16x8*>((ks & 1 ? kq1 : kq0) + 128 * (ks >> 1));
-        s = mfma_bf16_16x16x32(kop, qop[ks], s);
+        sp = mfma_bf16_16x16x32(kop, qop[ks], sp);
       }
+      xch[j & 1][wv_id][lane] = sp;
+    }
+    __syncthreads();                                     // partial S^T tiles exchanged
+    if (wave_active) {
+      const uint8_t* kb = kvs[buf];
+      const f32x4 so = xch[j & 1][partner][lane];
+      const f32x4 s = ds == 0 ? sp_plus(sp, so) : sp_plus(so, sp);
       // lane holds head h, keys 4g+j of the block
       float sv[4];
       float bmax = -INFINITY;

@@ -134,21 +134,39 @@ __device__ __forceinline__ float tile_score(const Op<DT> (&a)[HB], const Op<DT> 
 // Materialised scores: one workgroup per (query row, chunk of keys); each wave scans
 // every fourth 64-key tile of the chunk, reading k^I straight from HBM (no reuse).
 // ---------------------------------------------------------------------------
-constexpr int kRowscanChunk = 4096;
+// Keys per workgroup: chosen so that rows x chunks fills the resident workgroup slots
+// (4 per CU) about once, without a partial last wave of workgroups.
+static int rowscan_chunk(int rows, int Lk) {
+  static int n_cu = 0;
+  if (n_cu == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n_cu = v;
+    else
+      n_cu = 256;
+  }
+  const long long target = 4LL * n_cu;
+  long long per_row = (target + rows - 1) / rows;
+  const long long max_chunks = (Lk + 255) / 256;
+  if (per_row > max_chunks) per_row = max_chunks;
+  if (per_row < 1) per_row = 1;
+  const long long chunk = ((Lk + per_row - 1) / per_row + 63) / 64 * 64;
+  return (int)chunk;
+}
 
 template <int DT, int HB>
 __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, float* __restrict__ scores,
-                                                              uint32_t* __restrict__ row_hist) {
+                                                              uint32_t* __restrict__ row_hist, int chunk_keys) {
   __shared__ uint32_t lhist[kRowHistBins];
   constexpr int RB = IdxTraits<DT>::kRowBytes;
-  const int n_chunks = (a.Lk + kRowscanChunk - 1) / kRowscanChunk;
+  const int n_chunks = (a.Lk + chunk_keys - 1) / chunk_keys;
   const int qrow = blockIdx.x / n_chunks;
   const int chunk = blockIdx.x - qrow * n_chunks;
   const int b = qrow / a.Lq, i = qrow - b * a.Lq;
   const int p = a.Lk - a.Lq + i;
   const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6, g = lane >> 4;
-  const int s_begin = chunk * kRowscanChunk;
-  const int s_end = min(a.Lk, s_begin + kRowscanChunk);
+  const int s_begin = chunk * chunk_keys;
+  const int s_end = min(a.Lk, s_begin + chunk_keys);
   float* out = scores + (size_t)qrow * a.Lk;
 
   const uint8_t* qptr = reinterpret_cast<const uint8_t*>(a.q) + (size_t)qrow * a.H_I * RB;
@@ -178,8 +196,10 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
   };
   const int s_first = s_begin + wv_id * kTileKeys;
   const int s_causal_end = min(s_end, p + 1);      // tiles starting here are all -inf
-  Op<DT> Bn[4];
+  // two tiles in flight per wave: Bn (next) and Bn2 (the one after)
+  Op<DT> Bn[4], Bn2[4];
   if (s_first < s_causal_end) load_tile(s_first, Bn);
+  if (s_first + 4 * kTileKeys < s_causal_end) load_tile(s_first + 4 * kTileKeys, Bn2);
   for (int s0 = s_first; s0 < s_end; s0 += 4 * kTileKeys) {
     const int s = s0 + lane;
     if (s0 >= s_causal_end) {  // whole tile is non-causal for this query
@@ -188,8 +208,11 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
     }
     Op<DT> Bk[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) Bk[kb] = Bn[kb];
-    if (s0 + 4 * kTileKeys < s_causal_end) load_tile(s0 + 4 * kTileKeys, Bn);
+    for (int kb = 0; kb < 4; ++kb) {
+      Bk[kb] = Bn[kb];
+      Bn[kb] = Bn2[kb];
+    }
+    if (s0 + 8 * kTileKeys < s_causal_end) load_tile(s0 + 8 * kTileKeys, Bn2);
     float val = tile_score<DT, HB>(A, Bk, W);
     if (DT == DSA_FP8_E4M3) val *= ksc[min(s, a.Lk - 1)];
     const bool causal = s <= p && s < s_end;
@@ -632,12 +655,13 @@ __global__ void zero_ints_kernel(int* p, int n) {
 // ---------------------------------------------------------------------------
 template <int DT>
 static hipError_t rowscan_dispatch(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s) {
-  dim3 grid((unsigned)((a.Lk + kRowscanChunk - 1) / kRowscanChunk) * (unsigned)(a.B * a.Lq));
+  const int chunk = rowscan_chunk(a.B * a.Lq, a.Lk);
+  dim3 grid((unsigned)((a.Lk + chunk - 1) / chunk) * (unsigned)(a.B * a.Lq));
   switch (a.H_I / 16) {
-    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
-    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
-    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
-    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores, row_hist); break;
+    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
+    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
+    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
+    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
   }
   return hipGetLastError();
 }

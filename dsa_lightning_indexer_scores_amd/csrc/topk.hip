@@ -86,6 +86,7 @@ __global__ __launch_bounds__(kTopBS) void topk_rows_kernel(const float* __restri
   __shared__ uint32_t lkeys[kListCap];
   __shared__ uint32_t lpos[kListCap];
   __shared__ uint32_t sh[kTopBS / 64 + 2];
+  __shared__ uint32_t wtot[16 * (kTopBS / 64)];
   const int row = blockIdx.x;
   const int tid = threadIdx.x;
   const float* x = scores + (size_t)row * row_stride;
@@ -120,30 +121,68 @@ __global__ __launch_bounds__(kTopBS) void topk_rows_kernel(const float* __restri
   uint32_t theta, need_eq;
   if (a1 + h1 <= (uint32_t)kListCap) {
     // ---- one streaming pass: candidates with digit >= d1 into the LDS list ----------
+    // A chunk is 16 sub-chunks of kTopBS consecutive entries (coalesced loads); entry
+    // (u, tid) goes to list slot base + prefix over (sub-chunk, wave) of the kept counts
+    // + its rank among the wave's kept entries, which keeps position order.  The next
+    // chunk's loads are issued before the current chunk is compacted.
+    constexpr int kSub = 16;
+    constexpr int kChunk = kTopBS * kSub;
+    constexpr int kNW = kTopBS / 64;
+    const int lane = tid & 63, w = tid >> 6;
     const uint32_t kmin = d1 << 21;
+    const float fmin = key_to_float(kmin);   // key >= kmin  <=>  score >= fmin
     uint32_t base = 0;
-    for (int c0 = 0; c0 < nv; c0 += kTopBS * 4) {
-      const int e0 = c0 + tid * 4;
-      uint32_t kk[4];
-      uint32_t cnt = 0;
+    float cur[kSub], nxt[kSub];
+    auto load_chunk = [&](int c0, float (&v)[kSub]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = e0 + u;
-        kk[u] = e < nv ? order_key(x[e]) : 0u;
-        cnt += kk[u] >= kmin ? 1u : 0u;
+      for (int u = 0; u < kSub; ++u) {
+        const int e = c0 + u * kTopBS + tid;
+        v[u] = e < nv ? x[e] : -INFINITY;
       }
-      uint32_t tot;
-      uint32_t o = base + block_excl_scan(cnt, sh, tot);
+    };
+    load_chunk(0, cur);
+    for (int c0 = 0; c0 < nv; c0 += kChunk) {
+      if (c0 + kChunk < nv) load_chunk(c0 + kChunk, nxt);
+      uint64_t m[kSub];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (kk[u] >= kmin) {
-          if (o < (uint32_t)kListCap) {   // holds by construction (o < a1 + h1)
-            lkeys[o] = kk[u];
-            lpos[o] = (uint32_t)(e0 + u);
-          }
-          ++o;
+      for (int u = 0; u < kSub; ++u) {
+        const int e = c0 + u * kTopBS + tid;
+        m[u] = ballot(e < nv && cur[u] >= fmin);
+        if (lane == 0) wtot[u * kNW + w] = (uint32_t)popc64(m[u]);
+      }
+      __syncthreads();
+      if (w == 0) {  // exclusive prefix of the kSub*kNW counts (4 per lane), in position order
+        uint32_t c[4], t = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { c[i] = wtot[4 * lane + i]; t += c[i]; }
+        uint32_t incl = t;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const uint32_t o = __shfl_up(incl, d);
+          if (lane >= d) incl += o;
         }
-      base += tot;
+        uint32_t run = incl - t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { wtot[4 * lane + i] = run; run += c[i]; }
+        if (lane == 63) sh[0] = incl;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        if (m[u] == 0) continue;   // wave-uniform: nothing kept in this sub-chunk
+        if ((m[u] >> lane) & 1ull) {
+          const uint32_t o = base + wtot[u * kNW + w] + rank_below(m[u]);
+          const int e = c0 + u * kTopBS + tid;
+          if (o < (uint32_t)kListCap) {   // holds by construction (o < a1 + h1)
+            lkeys[o] = order_key(cur[u]);
+            lpos[o] = (uint32_t)e;
+          }
+        }
+      }
+      base += sh[0];
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) cur[u] = nxt[u];
     }
     __syncthreads();
     const uint32_t nl = min(base, (uint32_t)kListCap);  // == a1 + h1
