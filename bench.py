@@ -14,6 +14,8 @@ bounded sample of query rows.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
 """
 import argparse
+import csv
+import hashlib
 import json
 import math
 import os
@@ -26,6 +28,95 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+
+# HBM traffic per launch comes from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
+# summarised under profiles/.  A summary is used only while the kernel's sources still
+# hash to the digest it records; otherwise the traffic is reported as null.
+PKG = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd")
+KERNEL_SOURCES = {"mla_attn_kernel": ["csrc/attn.hip"], "indexer_topk_kernel": ["csrc/indexer.hip"]}
+COMMON_SOURCES = ["csrc/dsa_common.hpp", "csrc/dsa_launch.hpp", "build_lib.py"]
+TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn_kernel", "profiles/mla_attn_kernel_prefill128k_hbm.txt"),
+                   "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
+PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
+               '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
+               '--copy-calibration')
+COPY_BYTES = 1 << 30
+
+
+def source_digest(kernel):
+    h = hashlib.sha256()
+    for rel in sorted(KERNEL_SOURCES[kernel] + COMMON_SOURCES):
+        with open(os.path.join(PKG, rel), "rb") as f:
+            h.update(rel.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch from the committed counter summary, or None when absent or stale."""
+    kernel, rel = TRAFFIC_SUMMARY[name]
+    path = os.path.join(ROOT, rel)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                fields[key.strip()] = val.strip()
+    if fields.get("source_digest") != source_digest(kernel):
+        return None
+    return int(fields["traffic_bytes_per_launch"])
+
+
+def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
+    """Summary text of the two counter runs for one kernel.  FETCH_SIZE and WRITE_SIZE are
+    KiB per dispatch; each is scaled by what it reads for the 1 GiB device copy that the
+    same run makes (the copy whose WRITE_SIZE is 1 GiB)."""
+    def load(path):
+        out = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                out[int(r["Dispatch_Id"])] = (r["Kernel_Name"], float(r["Counter_Value"]))
+        return out
+    fetch, write = load(fetch_csv), load(write_csv)
+    copies = [d for d, (n, v) in write.items()
+              if "copyBuffer" in n and abs(v * 1024 - COPY_BYTES) < 0.005 * COPY_BYTES]
+    if not copies:
+        raise SystemExit("no 1 GiB calibration copy in the WRITE_SIZE run")
+    cid = copies[-1]
+    if cid not in fetch or "copyBuffer" not in fetch[cid][0]:
+        raise SystemExit("the FETCH_SIZE run does not have the calibration copy at the same dispatch")
+    f_scale = COPY_BYTES / (fetch[cid][1] * 1024)
+    w_scale = COPY_BYTES / (write[cid][1] * 1024)
+    sel = [d for d, (n, v) in fetch.items() if kernel in n and template in n]
+    if not sel or any(d not in write for d in sel):
+        raise SystemExit(f"no dispatches of {kernel}{template} in both runs")
+    f_kib = sum(fetch[d][1] for d in sel) / len(sel)
+    w_kib = sum(write[d][1] for d in sel) / len(sel)
+    read_b = f_kib * 1024 * f_scale
+    write_b = w_kib * 1024 * w_scale
+    lines = [
+        f"# HBM traffic of dsa::{kernel}{template}, workload {workload}",
+        "# commands, from the repository root on one MI355X (cd /tmp && export TMPDIR=/tmp first):",
+        "#   " + PMC_COMMAND.format(counter="FETCH_SIZE", dir="<fetch_dir>"),
+        "#   " + PMC_COMMAND.format(counter="WRITE_SIZE", dir="<write_dir>"),
+        f"#   python3 bench.py --summarize-counters <fetch_dir>/run_counter_collection.csv "
+        f"<write_dir>/run_counter_collection.csv --kernel {kernel} --template '{template}' --workload {workload}",
+        f"calibration_copy_bytes: {COPY_BYTES}",
+        f"calibration_fetch_kib: {fetch[cid][1]:.2f}",
+        f"calibration_write_kib: {write[cid][1]:.2f}",
+        f"read_scale: {f_scale:.4f}",
+        f"write_scale: {w_scale:.4f}",
+        f"launches: {len(sel)}",
+        f"fetch_kib_per_launch: {f_kib:.1f}",
+        f"write_kib_per_launch: {w_kib:.1f}",
+        f"read_bytes_per_launch: {int(read_b)}",
+        f"write_bytes_per_launch: {int(write_b)}",
+        f"traffic_bytes_per_launch: {int(read_b + write_b)}",
+        f"source_digest: {source_digest(kernel)}",
+    ]
+    return "\n".join(lines)
 
 
 def log(*a):
@@ -43,11 +134,18 @@ def parse():
     ap.add_argument("--no-allfull", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 counter runs and exit")
+    ap.add_argument("--kernel", default="mla_attn_kernel")
+    ap.add_argument("--template", default="")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.kernel, args.template, args.workload))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
@@ -130,11 +228,13 @@ def main():
     if idx_ms >= attn_ms * cfg.n_layers:
         roof = {"kernel": "indexer_topk", "bound": "mfma", "achieved": round(idx_tfs, 2),
                 "peak": MFMA_PEAK_TFLOPS[cfg.idx_dtype], "unit": "TFLOP/s",
-                "frac": round(idx_tfs / MFMA_PEAK_TFLOPS[cfg.idx_dtype], 4), "traffic": None}
+                "frac": round(idx_tfs / MFMA_PEAK_TFLOPS[cfg.idx_dtype], 4)}
     else:
         roof = {"kernel": "sparse_attn", "bound": "mfma", "achieved": round(attn_tfs, 2),
                 "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(attn_tfs / MFMA_PEAK_TFLOPS["bf16"], 4), "traffic": None}
+                "frac": round(attn_tfs / MFMA_PEAK_TFLOPS["bf16"], 4)}
+    # measured HBM bytes per launch (counters), only for the workload they were taken on
+    roof["traffic"] = recorded_traffic(roof["kernel"]) if cfg.name == "prefill128k" else None
 
     result = {
         "metric": "indexed prefill tokens/s per 4-layer group @128K; decode us/token @200K; %roofline",

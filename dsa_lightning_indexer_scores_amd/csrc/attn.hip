@@ -66,8 +66,9 @@ struct MlaParams {
 // slices of a head tile also split the S^T reduction: each multiplies over 288 of the 576
 // latent dims, the partial tiles are exchanged through LDS, and both add them in the same
 // order (so both hold bitwise the same S^T).  WPE = minimum waves per SIMD the register
-// allocation must allow.
-template <int NW, int DVS, int WPE>
+// allocation must allow.  SPLIT: the keys are split over blockIdx.y and the kernel writes
+// unnormalised partials (o, m, l) for mla_combine_kernel instead of the output.
+template <int NW, int DVS, int WPE, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void mla_attn_kernel(MlaParams P) {
   constexpr int kDvPer = kMlaDv / DVS;          // value dims per wave
@@ -257,7 +258,7 @@ void mla_attn_kernel(MlaParams P) {
   const float l_run = wave_sum16x4(l_lane);
   const size_t qh = ((size_t)b * a.Lq + i) * a.H + h;   // (query, head) row
   const int d0 = kDvPer * ds;
-  if (P.n_split == 1) {
+  if constexpr (!SPLIT) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     if (a.out_dtype == DSA_F32) {
       float* orow = reinterpret_cast<float*>(a.out) + qh * kMlaDv + d0;
@@ -432,8 +433,14 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   P.part_o = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_o);
   P.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_ml);
   dim3 grid(pl.n_groups, pl.n_split);
-  if (pl.nw <= 4) mla_attn_kernel<4, 2, 2><<<grid, 256, 0, s>>>(P);
-  else mla_attn_kernel<8, 2, 2><<<grid, 512, 0, s>>>(P);
+  const bool split = pl.n_split > 1;
+  if (pl.nw <= 4) {
+    if (split) mla_attn_kernel<4, 2, 2, true><<<grid, 256, 0, s>>>(P);
+    else mla_attn_kernel<4, 2, 2, false><<<grid, 256, 0, s>>>(P);
+  } else {
+    if (split) mla_attn_kernel<8, 2, 2, true><<<grid, 512, 0, s>>>(P);
+    else mla_attn_kernel<8, 2, 2, false><<<grid, 512, 0, s>>>(P);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_split == 1) return e;
   mla_combine_kernel<<<a.B * a.Lq * a.H, 128, 0, s>>>(P.part_o, P.part_ml, pl.n_split, a.out, a.out_dtype, a.lse);
