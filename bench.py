@@ -43,6 +43,33 @@ PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuff
 COPY_BYTES = 1 << 30
 
 
+class Work:
+    """Algorithmic work of the path: causal (query, key) pairs the indexer scores and
+    selected pairs the sparse attention reads, and their flops."""
+
+    @staticmethod
+    def causal_pairs(L, Lq):
+        # queries at positions L-Lq .. L-1 see L-Lq+1 .. L keys
+        return (2 * L - Lq + 1) * Lq // 2
+
+    @staticmethod
+    def selected_pairs(L, k, Lq):
+        # a query at position p reads min(k, p + 1) keys
+        first = L - Lq + 1
+        if first > k:
+            return Lq * k
+        small = min(k, L)                      # counts first .. small are below or at k
+        return (first + small) * (small - first + 1) // 2 + (L - small) * k
+
+    @staticmethod
+    def indexer_flops(pairs, H_I, d_I):
+        return 2 * H_I * d_I * pairs
+
+    @staticmethod
+    def attention_flops(pairs, H, Dqk, Dv):
+        return 2 * H * (Dqk + Dv) * pairs
+
+
 def source_digest(kernel):
     h = hashlib.sha256()
     for rel in sorted(KERNEL_SOURCES[kernel] + COMMON_SOURCES):
@@ -132,6 +159,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-allfull", action="store_true")
+    ap.add_argument("--no-chunk1m", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -154,7 +182,7 @@ def main():
     import torch
     import synth
     import dsa_lightning_indexer_scores_amd as dsa
-    from oracle import accounting
+    accounting = Work
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -303,6 +331,9 @@ def main():
     if not args.no_decode:
         result["decode"] = bench_decode(args, dsa, synth, accounting, torch, np, dev, stream)
 
+    if not args.no_chunk1m:
+        result["chunk1m"] = bench_chunk1m(args, dsa, synth, accounting, torch, np, dev, stream)
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg)
 
@@ -358,6 +389,72 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out
+
+
+def bench_chunk1m(args, dsa, synth, accounting, torch, np, dev, stream):
+    """1,048,576-token prefill in 4096-query chunks, timed once over all 256 chunks: per
+    chunk the Full layer's fused indexer + top-k against the (c+1)*4096 keys so far, then
+    the sparse attention of the group's 4 layers.  The attention queries of one chunk are
+    drawn once per layer and reused by every chunk (the work per chunk is unchanged); the
+    indexer queries, keys and weights cover the whole sequence."""
+    cfg = synth.get_config("chunk1m")
+    L, C, k = cfg.L, cfg.chunk, cfg.topk
+    n_chunks = L // C
+    log(f"[bench] chunk1m: L={L} in {n_chunks} chunks of {C}, fp8 indexer, {cfg.n_layers} layers")
+    ind = synth.indexer_inputs(cfg, device=dev, Lq=L)
+    layers = [synth.attention_inputs(cfg, layer=l, device=dev, Lq=C) for l in range(cfg.n_layers)]
+    idx = torch.empty((1, C, k), dtype=torch.int32, device=dev)
+    out = torch.empty((1, C, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev)
+    ws = dsa.Workspace()
+    torch.cuda.synchronize()
+
+    def chunk(c, ev=None):
+        lo, hi = c * C, (c + 1) * C
+        if ev is not None:
+            ev[0].record(stream)
+        dsa.indexer_topk(ind["q"][:, lo:hi], ind["k"][:, :hi], ind["w"][:, lo:hi], k,
+                         q_scale=ind["q_scale"][:, lo:hi], k_scale=ind["k_scale"][:, :hi], ws=ws, out=idx)
+        if ev is not None:
+            ev[1].record(stream)
+        for lay in layers:
+            dsa.sparse_attn({**lay, "kv": lay["kv"][:, :hi]}, idx, ws=ws, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for c in (0, n_chunks - 1):                       # warm-up: smallest and largest chunk
+        chunk(c)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_chunks)]
+    t0 = time.time()
+    for c in range(n_chunks):
+        chunk(c, evs[c])
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    idx_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    attn_ms = [e[1].elapsed_time(e[2]) / cfg.n_layers for e in evs]
+    t_idx = sum(idx_ms) / 1e3                      # one Full layer's indexer over the sequence
+    t_attn = sum(attn_ms) / 1e3                    # one layer's attention over the sequence
+    group = t_idx + cfg.n_layers * t_attn
+    last_pairs = accounting.causal_pairs(L, C)
+    last_tfs = accounting.indexer_flops(last_pairs, cfg.H_I, cfg.d_I) / (idx_ms[-1] * 1e-3) / 1e12
+    all_pairs = accounting.causal_pairs(L, L)
+    idx_tfs = accounting.indexer_flops(all_pairs, cfg.H_I, cfg.d_I) / t_idx / 1e12
+    log(f"[bench] chunk1m: indexer+topk {t_idx:.2f} s/layer, attention {t_attn * 1e3:.1f} ms/layer, "
+        f"group {group:.2f} s (wall {wall:.1f} s)")
+    out_d = {"workload": cfg.name, "L": L, "chunk": C, "chunks": n_chunks,
+             "indexer_topk_s_per_full_layer": round(t_idx, 4),
+             "indexer_tflops": round(idx_tfs, 1), "indexer_frac": round(idx_tfs / MFMA_PEAK_TFLOPS["fp8"], 4),
+             "last_chunk_indexer_ms": round(idx_ms[-1], 3),
+             "last_chunk_indexer_tflops": round(last_tfs, 1),
+             "attn_s_per_layer": round(t_attn, 4),
+             "group_s": round(group, 3), "tokens_per_s": round(L / group, 1),
+             "all_full_group_s_derived": round(cfg.n_layers * (t_idx + t_attn), 3),
+             "stack80": {"indexshare_20_full_s": round(20 * group, 1),
+                         "all_80_full_s": round(80 * (t_idx + t_attn), 1),
+                         "note": "derived from the measured per-layer indexer and attention times"}}
+    del ind, layers, idx, out
+    torch.cuda.empty_cache()
+    return out_d
 
 
 def cpu_baseline(cfg, target_s=15.0):

@@ -1,0 +1,42 @@
+"""Host-side checks of bench.py's bookkeeping (no GPU): its work accounting against the
+oracle's pair counts, and the counter summary it derives HBM traffic from."""
+import random
+
+import bench
+from oracle import accounting
+
+
+def test_bench_work_accounting_matches_oracle_counts():
+    rng = random.Random(0)
+    cases = [(131072, 2048, 131072), (200001, 2048, 1), (1048576, 2048, 4096), (1024, 64, 1024),
+             (10, 2048, 10), (3000, 2048, 5)]
+    cases += [(L, rng.randint(1, 3000), rng.randint(1, L)) for L in (rng.randint(1, 9000) for _ in range(500))]
+    for L, k, Lq in cases:
+        assert bench.Work.causal_pairs(L, Lq) == accounting.causal_pairs(L, Lq)
+        assert bench.Work.selected_pairs(L, k, Lq) == accounting.selected_pairs(L, k, Lq)
+    assert bench.Work.indexer_flops(10, 64, 128) == accounting.indexer_flops(10, 64, 128)
+    assert bench.Work.attention_flops(10, 32, 576, 512) == accounting.attention_flops(10, 32, 576, 512)
+
+
+def _csv(path, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for d, name, cn, v in rows:
+            f.write(f'{d},"{name}",{cn},{v}\n')
+
+
+def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    k = "void dsa::mla_attn_kernel<4, 2, 2, false>(dsa::MlaParams)"
+    _csv(fetch, [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 99.0),
+                 (5, k, "FETCH_SIZE", 1000.0), (6, k, "FETCH_SIZE", 3000.0),
+                 (9, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
+    _csv(write, [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 50.0),
+                 (5, k, "WRITE_SIZE", 10.0), (6, k, "WRITE_SIZE", 30.0),
+                 (9, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
+    text = bench.summarize_counters(str(fetch), str(write), "mla_attn_kernel", "<4, 2, 2, false>", "w")
+    fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
+    assert float(fields["read_scale"]) == 2.0 and float(fields["write_scale"]) == 1.0
+    assert int(fields["launches"]) == 2
+    # mean fetch 2000 KiB read twice over, mean write 20 KiB
+    assert int(fields["traffic_bytes_per_launch"]) == 2000 * 1024 * 2 + 20 * 1024

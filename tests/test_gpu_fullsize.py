@@ -1,0 +1,195 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times,
+checked against the fp64 oracle on sampled query rows (the oracle computes each sampled row
+over all of its causal keys).
+
+* prefill 131072 tokens, FP8 indexer, k = 2048, MLA attention of a Full and a Shared layer;
+* decode: 64 sequences x 200001 keys (1 query each) and the 4-query MTP variant sharing the
+  first query's index row;
+* the last 4096-query chunk of a 1,048,576-token prefill;
+* chunked prefill (4096-query chunks) equals the unchunked call bit for bit.
+
+Bars as in test_gpu_parity: index sets equal except inside the tau band around the row's
+k-th oracle score (tau 2e-2 for FP8); attention max|err| <= 1e-2 * RMS(oracle output) on the
+kernel's fp32 result, and the bf16 output equal to the round-to-nearest-even of that result.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import dsa_lightning_indexer_scores_amd as dsa
+from tests._helpers import to_f64, index_sets_agree
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+TAU_FP8 = 2e-2
+
+
+def _say(*a):
+    print("[fullsize]", *a, file=sys.stderr, flush=True)
+
+
+def _free():
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _oracle_score_row(ind, b, r, Lq, Lk, kI=None, ks=None):
+    """fp64 scores of query row r of sequence b (position Lk - Lq + r) over all keys."""
+    p = Lk - Lq + r
+    kI = to_f64(ind["k"][b]) if kI is None else kI
+    ks = to_f64(ind["k_scale"][b]) if ks is None else ks
+    q = to_f64(ind["q"][b, r:r + 1])
+    w = to_f64(ind["w"][b, r:r + 1])
+    qs = to_f64(ind["q_scale"][b, r:r + 1])
+    # the single query passed as the last of (Lk - p) queries sits at position p
+    return oracle.indexer_scores_rows(q, kI, w, [0], Lk, qs, ks, Lk - p)[0], p
+
+
+def _check_sets(idx_rows, score_rows, positions, k):
+    sc = np.stack(score_rows)
+    nv = [p + 1 for p in positions]
+    ref = oracle.topk_rows(sc, nv, k)
+    ok, nbad, msg = index_sets_agree(idx_rows, ref, sc, nv, k, TAU_FP8)
+    assert ok, msg
+    return nbad
+
+
+def _check_attention(q_rows, kv_rows, idx_rows, sm_scale, got32):
+    """Oracle attention of the sampled rows.  kv_rows(j) gives (K, idx) for row j: the
+    sequence's float64 latent rows [n, 576] and the row's index list into them (either the
+    whole cache with the selected positions, or only the selected rows, which is the same
+    definition restricted to the listed keys)."""
+    refs = []
+    for j in range(q_rows.shape[0]):
+        kv, ir = kv_rows(j)
+        ref, _ = oracle.sparse_attention_rows(q_rows[j:j + 1], kv[:, None, :], kv[:, None, :512],
+                                              ir[None], sm_scale, 1)
+        refs.append(ref[0])
+    ref = np.stack(refs)
+    rms = math.sqrt(float(np.mean(ref ** 2)))
+    err = float(np.abs(got32 - ref).max())
+    assert err <= 1e-2 * rms, (err, rms)
+    return err / rms
+
+
+def test_prefill128k_full_size_sampled_rows():
+    cfg = synth.get_config("prefill128k")
+    L, k = cfg.L, cfg.topk
+    _say("prefill128k: generating indexer inputs")
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    ws = dsa.Workspace()
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"],
+                           k_scale=ind["k_scale"], ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = sorted(set([0, 1, k - 2, k - 1, k, L // 2, L - 2, L - 1] + rng.integers(0, L, 4).tolist()))
+    _say("prefill128k: oracle scores of rows", rows)
+    kI, ks = to_f64(ind["k"][0]), to_f64(ind["k_scale"][0])
+    scs, pos = zip(*[_oracle_score_row(ind, 0, r, L, L, kI, ks) for r in rows])
+    idx_np = idx[0, rows].cpu().numpy()
+    nbad = _check_sets(idx_np, scs, pos, k)
+    _say(f"prefill128k: index sets agree ({nbad} rows differ inside the band)")
+    del ind, kI
+    _free()
+    for layer in (0, 3):                         # the Full layer and a Shared layer
+        lay = synth.attention_inputs(cfg, layer=layer, device=DEV)
+        out32 = dsa.sparse_attn(lay, idx, ws=ws, out_dtype=torch.float32)
+        outbf = dsa.sparse_attn(lay, idx, ws=ws)
+        assert torch.equal(outbf[0, rows], out32[0, rows].to(torch.bfloat16))
+        kv = to_f64(lay["kv"][0])
+        rel = _check_attention(to_f64(lay["q"][0, rows]), lambda j: (kv, idx_np[j]), idx_np,
+                               lay["sm_scale"], out32[0, rows].cpu().numpy().astype(np.float64))
+        _say(f"prefill128k: layer {layer} attention max|err|/RMS = {rel:.2e}")
+        del lay, out32, outbf, kv
+        _free()
+
+
+def test_decode200k_full_size_and_mtp():
+    cfg = synth.get_config("decode200k")
+    B, Lk, k = cfg.B, cfg.L, cfg.topk
+    _say("decode200k: generating indexer inputs")
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    ws = dsa.Workspace()
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"],
+                           k_scale=ind["k_scale"], ws=ws)             # [B, 1, k]
+    torch.cuda.synchronize()
+    seqs = [0, 17, B - 1]
+    scs, pos = zip(*[_oracle_score_row(ind, b, 0, 1, Lk) for b in seqs])
+    idx_np = idx[seqs, 0].cpu().numpy()
+    nbad = _check_sets(idx_np, scs, pos, k)
+    _say(f"decode200k: index sets of sequences {seqs} agree ({nbad} differ inside the band)")
+    del ind
+    _free()
+    lay = synth.attention_inputs(cfg, layer=0, device=DEV)
+    out32 = dsa.sparse_attn(lay, idx, ws=ws, out_dtype=torch.float32)
+    outbf = dsa.sparse_attn(lay, idx, ws=ws)
+    assert torch.equal(outbf, out32.to(torch.bfloat16))
+    for j, b in enumerate(seqs):
+        kv = to_f64(lay["kv"][b])
+        rel = _check_attention(to_f64(lay["q"][b, 0:1]), lambda _, j=j: (kv, idx_np[j]), idx_np[j:j + 1],
+                               lay["sm_scale"], out32[b, 0:1].cpu().numpy().astype(np.float64))
+        _say(f"decode200k: sequence {b} attention max|err|/RMS = {rel:.2e}")
+    del lay, out32, outbf
+    _free()
+    # MTP draft: 4 queries per sequence share the first step's index row
+    lay4 = synth.attention_inputs(cfg, layer=1, device=DEV, Lq=cfg.mtp)
+    out4 = dsa.sparse_attn(lay4, idx, idx_q_stride=0, ws=ws, out_dtype=torch.float32)
+    for j, b in enumerate(seqs[:2]):
+        kv = to_f64(lay4["kv"][b])
+        rel = _check_attention(to_f64(lay4["q"][b]), lambda _, j=j: (kv, idx_np[j]),
+                               np.repeat(idx_np[j:j + 1], cfg.mtp, axis=0),
+                               lay4["sm_scale"], out4[b].cpu().numpy().astype(np.float64))
+        _say(f"decode200k MTP: sequence {b} attention max|err|/RMS = {rel:.2e}")
+    del lay4, out4
+    _free()
+
+
+def test_chunk1m_last_chunk_sampled_rows():
+    cfg = synth.get_config("chunk1m")
+    Lk, C, k = cfg.L, cfg.chunk, cfg.topk
+    _say("chunk1m: generating the last chunk's indexer inputs")
+    ind = synth.indexer_inputs(cfg, device=DEV, Lq=C)                 # queries Lk-C .. Lk-1
+    ws = dsa.Workspace()
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"],
+                           k_scale=ind["k_scale"], ws=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    rows = sorted(set([0, 1, C // 2, C - 1] + rng.integers(0, C, 2).tolist()))
+    kI, ks = to_f64(ind["k"][0]), to_f64(ind["k_scale"][0])
+    scs, pos = zip(*[_oracle_score_row(ind, 0, r, C, Lk, kI, ks) for r in rows])
+    idx_np = idx[0, rows].cpu().numpy()
+    nbad = _check_sets(idx_np, scs, pos, k)
+    _say(f"chunk1m: index sets of rows {rows} agree ({nbad} differ inside the band)")
+    del ind, kI
+    _free()
+    lay = synth.attention_inputs(cfg, layer=0, device=DEV, Lq=C)
+    out32 = dsa.sparse_attn(lay, idx, ws=ws, out_dtype=torch.float32)
+
+    def selected_rows(j):                        # only the listed rows of the 1M-row cache
+        sel = idx_np[j][idx_np[j] >= 0]
+        kv = to_f64(lay["kv"][0, torch.from_numpy(sel.astype(np.int64)).to(DEV)])
+        return kv, np.arange(len(sel))
+
+    rel = _check_attention(to_f64(lay["q"][0, rows]), selected_rows, idx_np, lay["sm_scale"],
+                           out32[0, rows].cpu().numpy().astype(np.float64))
+    _say(f"chunk1m: attention max|err|/RMS = {rel:.2e}")
+    del lay, out32
+    _free()
+
+
+def test_chunked_prefill_equals_unchunked():
+    L, C, k = 16384, 4096, 2048
+    cfg = synth.get_config("chunk1m", L=L)
+    ind = synth.indexer_inputs(cfg, device=DEV, Lq=L)
+    full = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"], k_scale=ind["k_scale"])
+    for c in range(L // C):
+        lo, hi = c * C, (c + 1) * C
+        part = dsa.indexer_topk(ind["q"][:, lo:hi], ind["k"][:, :hi], ind["w"][:, lo:hi], k,
+                                q_scale=ind["q_scale"][:, lo:hi], k_scale=ind["k_scale"][:, :hi])
+        assert torch.equal(part, full[:, lo:hi]), f"chunk {c}"
