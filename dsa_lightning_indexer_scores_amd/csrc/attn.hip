@@ -37,8 +37,8 @@ constexpr int kBlkBytes = kBlk * kRowBytes;     // 18432
 constexpr int kDmaPerBlk = kBlkBytes / 1024;    // 18 wave-wide 1 KB direct-to-LDS loads
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
-constexpr int kRowBufs = 2;                     // row blocks: computing, in flight
-constexpr int kKeyBufs = 3;                     // idx blocks held: j .. j+2
+constexpr float kMaxStart = 1e30f;              // initial running maximum is -kMaxStart
+constexpr int kKeyBufs = 4;                     // idx ring slots (j .. j+2 in use)
 constexpr int kQSteps = 18 / 2;                 // 32-dim MFMA steps per wave (half of 576)
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
@@ -67,15 +67,17 @@ struct MlaParams {
 // latent dims, the partial tiles are exchanged through LDS, and both add them in the same
 // order (so both hold bitwise the same S^T).  WPE = minimum waves per SIMD the register
 // allocation must allow.  SPLIT: the keys are split over blockIdx.y and the kernel writes
-// unnormalised partials (o, m, l) for mla_combine_kernel instead of the output.
-template <int NW, int DVS, int WPE, bool SPLIT>
+// unnormalised partials (o, m, l) for mla_combine_kernel instead of the output.  NB = row
+// buffers: 2 keeps one block of rows in flight (more workgroups fit a CU), 3 keeps up to
+// two in flight (for the few, long-latency workgroups of decode).
+template <int NW, int DVS, int WPE, bool SPLIT, int NB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void mla_attn_kernel(MlaParams P) {
   constexpr int kDvPer = kMlaDv / DVS;          // value dims per wave
   constexpr int kDt = kDvPer / 16;              // 16-dim output tiles per wave
   constexpr int kSlotsPerWave = (kDmaPerBlk + NW - 1) / NW;
   constexpr int kDummy = kSlotsPerWave * NW - kDmaPerBlk;   // padding slots (fixed counts)
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[kRowBufs][kBlkBytes + kDummy * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NB][kBlkBytes + kDummy * 1024];
   __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs][64];   // idx entries of blocks
   __shared__ __attribute__((aligned(16))) f32x4 xch[2][NW][64];         // partial S^T tiles
   const AttnArgs& a = P.a;
@@ -110,32 +112,41 @@ void mla_attn_kernel(MlaParams P) {
   const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride * 2;
   const size_t row_bytes = (size_t)a.k_row_stride * 2;
 
-  // key of entry r of a block (from the LDS ring); -1 if padding / out of range
-  auto block_key = [&](int blk, int r) -> int {
-    const int pos = blk * kBlk + r;
-    const int key = keyring[(blk - blk_begin) % kKeyBufs][r];
-    return (pos < a.topk && key >= 0 && key < a.Lk) ? key : -1;
-  };
-  // idx entries of a block into its ring slot.  Every wave issues the same load (same
-  // bytes to the same place) so that all waves count the same number of loads; lanes past
-  // the block read clamped in-range positions that are never used.
+  // idx entries of a block into its ring slot (lanes 0..15).  Every wave issues the same
+  // load (same bytes to the same place) so that all waves count the same number of loads.
+  // Positions past topk (a last partial block) are stored as -1.
   auto issue_keys = [&](int blk) {
-    const int pos = min(blk * kBlk + lane, a.topk - 1);
-    dma_4(idx_row + pos, lds_offset(&keyring[(blk - blk_begin) % kKeyBufs][0]));
+    int* slot = &keyring[(blk - blk_begin) & (kKeyBufs - 1)][0];
+    const int pos = blk * kBlk + lane;
+    if (lane < kBlk) {
+      if (pos < a.topk) dma_4(idx_row + pos, lds_offset(slot));
+      else slot[lane] = -1;
+    }
   };
-  // the block's 16 latent rows into kvs[buf] (invalid rows read row 0 and are masked).
-  // Every wave issues the same number of loads; padding slots fill a dummy area.
+  // the block's 16 latent rows into kvs[buf] (rows of invalid entries read row 0 and are
+  // masked later).  Every wave issues the same number of loads; padding slots fill a dummy
+  // area.  The ring entries are read first: the loads below are ordered after them.
+  int dma_row[kSlotsPerWave];
+  const uint8_t* dma_src[kSlotsPerWave];
+#pragma unroll
+  for (int u = 0; u < kSlotsPerWave; ++u) {
+    const int j = wv_id + u * NW;
+    const int piece = j * 64 + lane;
+    const int r = min(piece / kChunks, kBlk - 1);
+    const int cs = piece - (piece / kChunks) * kChunks;
+    dma_row[u] = r;
+    dma_src[u] = kvbase + (j < kDmaPerBlk ? 16 * swz(r, cs) : 0);
+  }
+  const uint32_t row_bytes32 = (uint32_t)row_bytes;
   auto issue_rows = [&](int blk, int buf) {
+    const int* slot = &keyring[(blk - blk_begin) & (kKeyBufs - 1)][0];
+    int key[kSlotsPerWave];
+#pragma unroll
+    for (int u = 0; u < kSlotsPerWave; ++u) key[u] = slot[dma_row[u]];
 #pragma unroll
     for (int u = 0; u < kSlotsPerWave; ++u) {
-      const int j = wv_id + u * NW;
-      const int piece = j * 64 + lane;
-      const int r = min(piece / kChunks, kBlk - 1);
-      const int cs = piece - (piece / kChunks) * kChunks;
-      int key = block_key(blk, r);
-      key = key < 0 ? 0 : key;
-      const uint8_t* src = kvbase + (size_t)key * row_bytes + (j < kDmaPerBlk ? 16 * swz(r, cs) : 0);
-      dma_16(src, lds_offset(&kvs[buf][j * 1024]));
+      const uint32_t kk = (uint32_t)key[u] < (uint32_t)a.Lk ? (uint32_t)key[u] : 0u;
+      dma_16(dma_src[u] + (uint64_t)kk * row_bytes32, lds_offset(&kvs[buf][(wv_id + u * NW) * 1024]));
     }
   };
 
@@ -153,7 +164,9 @@ void mla_attn_kernel(MlaParams P) {
   f32x4 o[kDt];
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_use = -INFINITY, l_lane = 0.f;
+  // running maximum in log2 units of the scaled logits; finite so that exp2 of an invalid
+  // (-inf) logit minus it is 0 and the first raise multiplies the empty state by 0
+  float m_use = -kMaxStart, l_lane = 0.f;
   const float sl2 = a.sm_scale * kLog2e;
   // loop-invariant LDS offsets (bytes within a row buffer)
   // this wave's half starts at 32-dim step kQSteps*ds (chunk 4*kQSteps*ds; kQSteps is odd,
@@ -173,22 +186,34 @@ void mla_attn_kernel(MlaParams P) {
   __builtin_amdgcn_s_waitcnt(0);
 
   // Pipeline: rows of block j+1 and the idx of block j+2 are in flight while block j is
-  // computed; every wave waits for all of its loads at the top of the block.
+  // computed (requested during block j, after its QK); every wave waits for all of its
+  // loads at the top of the block.
+  // With NB = 3 the rows of blk+2 are also requested during block blk.  Loads complete
+  // in issue order, and each block issues the idx of a later block before its rows, so at
+  // the top of a block only the rows requested by the previous block may still be in
+  // flight.
+  constexpr int D = NB - 1;                     // blocks of rows requested ahead
   if (blk_begin < blk_end) {
     issue_keys(blk_begin);
     if (blk_begin + 1 < blk_end) issue_keys(blk_begin + 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     issue_rows(blk_begin, 0);
+    if constexpr (D == 2) {
+      if (blk_begin + 2 < blk_end) issue_keys(blk_begin + 2);
+      if (blk_begin + 1 < blk_end) issue_rows(blk_begin + 1, 1);
+    }
   }
 
   for (int blk = blk_begin; blk < blk_end; ++blk) {
     const int j = blk - blk_begin;
-    const int buf = j % kRowBufs;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of blk, idx of blk+1
-    __syncthreads();                                     // landed for all; other buffer free
-    if (blk + 2 < blk_end) issue_keys(blk + 2);
-    if (blk + 1 < blk_end) issue_rows(blk + 1, (j + 1) % kRowBufs);
+    const int buf = j % NB;
+    if (D == 2 && blk + 1 < blk_end)                     // rows of blk and idx of blk+2 landed
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kSlotsPerWave) : "memory");
+    else                                                 // rows of blk and idx of blk+1 landed
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();                                     // landed for all; oldest buffer free
+    if (blk + D + 1 < blk_end) issue_keys(blk + D + 1);
 
     f32x4 sp = {0.f, 0.f, 0.f, 0.f};
     if (wave_active) {
@@ -197,34 +222,48 @@ void mla_attn_kernel(MlaParams P) {
       // two per-lane bases (even/odd steps of this half) plus immediate offsets
       const uint8_t* kq0 = kb + k_off0;
       const uint8_t* kq1 = kb + k_off1;
+      // operand reads run kKAhead steps ahead of the MFMAs that consume them
+      constexpr int kKAhead = 3;
+      bf16x8 kop[kQSteps];
 #pragma unroll
-      for (int ks = 0; ks < kQSteps; ++ks) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>((ks & 1 ? kq1 : kq0) + 128 * (ks >> 1));
-        sp = mfma_bf16_16x16x32(kop, qop[ks], sp);
+      for (int ks = 0; ks < kQSteps; ++ks)
+        kop[ks] = *reinterpret_cast<const bf16x8*>((ks & 1 ? kq1 : kq0) + 128 * (ks >> 1));
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ++ks) sp = mfma_bf16_16x16x32(kop[ks], qop[ks], sp);
+      __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+#pragma unroll
+      for (int ks = 0; ks < kQSteps - kKAhead; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
       xch[j & 1][wv_id][lane] = sp;
     }
+    // the next block's rows are requested after this block's QK, which thereby starts
+    // right after the barrier
+    if (blk + D < blk_end) issue_rows(blk + D, (j + D) % NB);
     __syncthreads();                                     // partial S^T tiles exchanged
     if (wave_active) {
       const uint8_t* kb = kvs[buf];
-      const f32x4 so = xch[j & 1][partner][lane];
-      const f32x4 s = ds == 0 ? sp_plus(sp, so) : sp_plus(so, sp);
-      // lane holds head h, keys 4g+j of the block
-      float sv[4];
-      float bmax = -INFINITY;
-      const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j % kKeyBufs][4 * g]);
-      const int kkv[4] = {kk4.x, kk4.y, kk4.z, kk4.w};
-      const int pos0 = blk * kBlk + 4 * g;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bool valid = (pos0 + jj < a.topk) & ((unsigned)kkv[jj] < (unsigned)a.Lk);
-        sv[jj] = valid ? s[jj] * sl2 : -INFINITY;
-        bmax = fmaxf(bmax, sv[jj]);
+      // both halves add the two partial tiles (fp32 addition commutes exactly), so both
+      // hold the same S^T; lane holds head h, keys 4g+jj of the block
+      const f32x4 s = sp + xch[j & 1][partner][lane];
+      const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j & (kKeyBufs - 1)][4 * g]);
+      const bool v0 = (uint32_t)kk4.x < (uint32_t)a.Lk, v1 = (uint32_t)kk4.y < (uint32_t)a.Lk;
+      const bool v2 = (uint32_t)kk4.z < (uint32_t)a.Lk, v3 = (uint32_t)kk4.w < (uint32_t)a.Lk;
+      // scaled logits in log2 units (the block maximum is then one of them exactly, so a
+      // lone dominant key gets p = 1 exactly)
+      float sv[4] = {s[0] * sl2, s[1] * sl2, s[2] * sl2, s[3] * sl2};
+      if (ballot(!(v0 & v1 & v2 & v3))) {        // some entry of the block invalid (rare)
+        sv[0] = v0 ? sv[0] : -INFINITY;
+        sv[1] = v1 ? sv[1] : -INFINITY;
+        sv[2] = v2 ? sv[2] : -INFINITY;
+        sv[3] = v3 ? sv[3] : -INFINITY;
       }
-      bmax = wave_max16x4(bmax);
+      const float bmax = wave_max16x4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
       const bool need = bmax > m_use + kRescaleGap;
       if (ballot(need)) {
-        const float alpha = need ? (m_use == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_use - bmax)) : 1.f;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - bmax) : 1.f;
         if (need) m_use = bmax;
         l_lane *= alpha;
 #pragma unroll
@@ -232,25 +271,34 @@ void mla_attn_kernel(MlaParams P) {
       }
       bf16x8 pb;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float pj = (sv[j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sv[j] - m_use);
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pj = __builtin_amdgcn_exp2f(sv[jj] - m_use);
         l_lane += pj;
         const __bf16 hi = (__bf16)pj;
-        pb[j] = hi;
-        pb[j + 4] = (__bf16)(pj - (float)hi);
+        pb[jj] = hi;
+        pb[jj + 4] = (__bf16)(pj - (float)hi);
       }
       // O^T += V^T . P^T over the block's 16 keys (each key twice: hi and lo part of p)
       // V^T rows for dims 16dt..16dt+15: chunk c0 + 2dt of row vrow, at
       // v_off[dt % 4] + 128 * (dt / 4).  Each key enters twice (hi and lo part of p), so
       // the same transposed read fills both halves of the operand.
+      // transposed reads run kVAhead tiles ahead of the MFMAs that consume them
+      constexpr int kVAhead = 4;
+      bf16x4 vt[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) vt[dt] = lds_read_tr16(kb + v_off[dt & 3] + 128 * (dt >> 2));
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        const uint8_t* vp = kb + v_off[dt & 3] + 128 * (dt >> 2);
-        const bf16x4 v0 = lds_read_tr16(vp);
-        const bf16x4 v1 = lds_read_tr16(vp);
-        const bf16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = __builtin_shufflevector(vt[dt], vt[dt], 0, 1, 2, 3, 0, 1, 2, 3);
         o[dt] = mfma_bf16_16x16x32(va, pb, o[dt]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, kVAhead, 0);
+#pragma unroll
+      for (int dt = 0; dt < kDt - kVAhead; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kVAhead, 0);
     }
   }
 
@@ -435,11 +483,11 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
   if (pl.nw <= 4) {
-    if (split) mla_attn_kernel<4, 2, 2, true><<<grid, 256, 0, s>>>(P);
-    else mla_attn_kernel<4, 2, 2, false><<<grid, 256, 0, s>>>(P);
+    if (split) mla_attn_kernel<4, 2, 2, true, 3><<<grid, 256, 0, s>>>(P);
+    else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);
   } else {
-    if (split) mla_attn_kernel<8, 2, 2, true><<<grid, 512, 0, s>>>(P);
-    else mla_attn_kernel<8, 2, 2, false><<<grid, 512, 0, s>>>(P);
+    if (split) mla_attn_kernel<8, 2, 2, true, 3><<<grid, 512, 0, s>>>(P);
+    else mla_attn_kernel<8, 2, 2, false, 2><<<grid, 512, 0, s>>>(P);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.n_split == 1) return e;

@@ -60,15 +60,20 @@ __device__ __forceinline__ int popc64(uint64_t m) { return __popcll(m); }
 template <typename T>
 __device__ __forceinline__ T uniform(T v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ float wave_max16x4(float v) {  // max over lanes {l, l^16, l^32, l^48}
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+// max / sum over the lanes {l, l^16, l^32, l^48}, with the gfx950 lane swaps (no LDS):
+// permlane32_swap(v, v) yields the two 32-lane halves of v side by side, permlane16_swap
+// the two 16-lane rows of each half.
+__device__ __forceinline__ float wave_max16x4(float v) {
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+  auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(y[0]), __uint_as_float(y[1]));
 }
 __device__ __forceinline__ float wave_sum16x4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+  auto y = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(y[0]) + __uint_as_float(y[1]);
 }
 
 // Reduce-scatter of four per-lane partial sums p[0..3] over the four 16-lane groups:
