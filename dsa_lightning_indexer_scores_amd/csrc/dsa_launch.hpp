@@ -18,7 +18,7 @@ struct IndexerArgs {
 
 // Capacity (entries) of the per-row streaming candidate buffer of the fused kernel.
 inline int topk_buffer_capacity(int k) {
-  int cap = 2 * k;
+  int cap = 4 * k;
   if (cap < k + 512) cap = k + 512;
   return (cap + 63) / 64 * 64;
 }

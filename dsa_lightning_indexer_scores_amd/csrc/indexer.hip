@@ -106,28 +106,58 @@ __device__ __forceinline__ f32x4 dot16<DSA_BF16>(const Op<DSA_BF16>& a, const Op
   return c;
 }
 
-// Scores of one token against a 64-key tile.  a[hb]: the token's heads 16hb..16hb+15;
-// b[kb]: keys 16kb..16kb+15 of the tile; wv[hb][i] = w'[16hb + 4g + i].
-// Returns, in lane l, sum_j w'_j ReLU(q_j . k_{s0+l}) (before the fp8 key scale).
-// Shared by the materialising and the fused kernels so both produce identical bits.
+// Scores of TW tokens against a 64-key tile.  a[tt][hb]: token tt's heads
+// 16hb..16hb+15; b[kb]: keys 16kb..16kb+15 of the tile; wv[tt][hb][i] = w'[16hb + 4g + i].
+// Returns, in lane l of out[tt], sum_j w'_j ReLU(q_j . k_{s0+l}) (before the fp8 key
+// scale).  Shared by the materialising and the fused kernels so both produce identical
+// bits (each token's arithmetic does not depend on TW).  The (key block, token) groups of
+// MFMAs are issued one group ahead of their epilogues, so the matrix core and the VALU
+// work on different groups at the same time.
+template <int DT, int HB, int TW>
+__device__ __forceinline__ void tile_scores(const Op<DT> (&a)[TW][HB], const Op<DT> (&b)[4],
+                                            const f32x4 (&wv)[TW][HB], float (&out)[TW]) {
+  constexpr int kMfmaPerDot = (DT == DSA_FP8_E4M3) ? 1 : 4;
+  f32x4 d[4][TW][HB];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) d[kb][tt][hb] = dot16<DT>(a[tt][hb], b[kb]);
+  float p[TW][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      float acc = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        acc = fmaf(wv[tt][hb][0], fmaxf(d[kb][tt][hb][0], 0.f), acc);
+        acc = fmaf(wv[tt][hb][1], fmaxf(d[kb][tt][hb][1], 0.f), acc);
+        acc = fmaf(wv[tt][hb][2], fmaxf(d[kb][tt][hb][2], 0.f), acc);
+        acc = fmaf(wv[tt][hb][3], fmaxf(d[kb][tt][hb][3], 0.f), acc);
+      }
+      p[tt][kb] = acc;
+    }
+  __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDot * HB, 0);
+#pragma unroll
+  for (int grp = 1; grp < 4 * TW; ++grp) {
+    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDot * HB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8 * HB, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x002, 8 * HB, 0);
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) out[tt] = reduce_scatter4(p[tt][0], p[tt][1], p[tt][2], p[tt][3]);
+}
+
 template <int DT, int HB>
 __device__ __forceinline__ float tile_score(const Op<DT> (&a)[HB], const Op<DT> (&b)[4],
                                             const f32x4 (&wv)[HB]) {
-  float p[4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    float acc = 0.f;
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      const f32x4 d = dot16<DT>(a[hb], b[kb]);
-      acc = fmaf(wv[hb][0], fmaxf(d[0], 0.f), acc);
-      acc = fmaf(wv[hb][1], fmaxf(d[1], 0.f), acc);
-      acc = fmaf(wv[hb][2], fmaxf(d[2], 0.f), acc);
-      acc = fmaf(wv[hb][3], fmaxf(d[3], 0.f), acc);
-    }
-    p[kb] = acc;
-  }
-  return reduce_scatter4(p[0], p[1], p[2], p[3]);
+  const Op<DT>(&a1)[1][HB] = *reinterpret_cast<const Op<DT>(*)[1][HB]>(&a);
+  const f32x4(&w1)[1][HB] = *reinterpret_cast<const f32x4(*)[1][HB]>(&wv);
+  float out[1];
+  tile_scores<DT, HB, 1>(a1, b, w1, out);
+  return out[0];
 }
 
 // ---------------------------------------------------------------------------
@@ -538,12 +568,23 @@ void indexer_topk_kernel(FusedParams P) {
     // covers the in-flight tile loads
     __builtin_amdgcn_s_waitcnt(0);
 
+    // the head weights of this wave's tokens stay in registers for the whole item
+    __syncthreads();  // wsh filled by the whole workgroup
+    f32x4 W[TW][HB];
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        W[tt][hb] = *reinterpret_cast<const f32x4*>(&wsh[(wv_id * TW + tt) * H_I + hb * 16 + 4 * g]);
+
     uint32_t theta[TW], cnt[TW];
+    float theta_f[TW];  // the float whose order key is theta (-inf: admit every key)
     uint32_t* rk[TW];
     uint32_t* rp[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
       theta[tt] = 0u;
+      theta_f[tt] = -INFINITY;
       cnt[tt] = 0u;
       rk[tt] = P.row_keys + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
       rp[tt] = P.row_pos + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
@@ -563,26 +604,33 @@ void indexer_topk_kernel(FusedParams P) {
       const float ks = fp8 ? kscl[cur][lane] : 1.f;
       const int s = s0 + lane;
 
+      int p_last = p_t[0];
+#pragma unroll
+      for (int tt = 1; tt < TW; ++tt) p_last = max(p_last, p_t[tt]);
+      if (p_last < s0) continue;  // wave-uniform: every token past its causal range / absent
+      float sc[TW];
+      tile_scores<DT, HB, TW>(A, Bk, W, sc);
 #pragma unroll
       for (int tt = 0; tt < TW; ++tt) {
         if (p_t[tt] < s0) continue;  // wave-uniform: token past its causal range / absent
-        f32x4 W[HB];
-        const float* wrow = &wsh[(wv_id * TW + tt) * H_I];
-#pragma unroll
-        for (int hb = 0; hb < HB; ++hb) W[hb] = *reinterpret_cast<const f32x4*>(wrow + hb * 16 + 4 * g);
-        const float val = tile_score<DT, HB>(A[tt], Bk, W) * ks;
-        const uint32_t key = order_key(val);
-        const bool pred = (s <= p_t[tt]) && (s < s_hi) && (key > theta[tt]);
+        const float val = sc[tt] * ks;
+        // val > theta_f is key > theta (the order-key map is strictly increasing on
+        // floats with -0 = +0); positions are checked only in a tile that crosses the
+        // causal edge or the segment end
+        bool pred = val > theta_f[tt];
+        if (s0 + kTileKeys - 1 > p_t[tt] || s0 + kTileKeys > s_hi) pred = pred && (s <= p_t[tt]) && (s < s_hi);
         const uint64_t m = ballot(pred);
         if (m) {
           if (pred) {
-            rk[tt][cnt[tt] + rank_below(m)] = key;
+            rk[tt][cnt[tt] + rank_below(m)] = order_key(val);
             rp[tt][cnt[tt] + rank_below(m)] = (uint32_t)s;
           }
           cnt[tt] += popc64(m);
-          if (cnt[tt] > (uint32_t)(P.cap - kTileKeys))
+          if (cnt[tt] > (uint32_t)(P.cap - kTileKeys)) {
             cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
                                   hist[wv_id], theta[tt]);
+            theta_f[tt] = key_to_float(theta[tt]);
+          }
         }
       }
     }
