@@ -292,32 +292,50 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* 
 
 // ---------------------------------------------------------------------------
 // Wave-level selection on a candidate list held as two arrays in global memory:
-// keys[0..n) (uint32 order keys) and pos[0..n) (positions, ascending).  Loads are
-// issued 8 per lane at a time so that one wave keeps 512 entries in flight.
+// keys[0..n) (uint32 order keys) and pos[0..n) (positions, ascending).  One pass reads
+// the list in batches of 1024 entries: lane l holds entries base + 256 j + 4 l + i
+// (j, i = 0..3), loaded as 16-byte vectors, and the next batch is requested before the
+// current one is processed, so each pass costs about one memory latency per batch.
 // ---------------------------------------------------------------------------
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;          // 2048 LDS bins per wave
 constexpr int kBinsPerLane = kBins / 64;
+constexpr uint32_t kBatch = 1024;
+
+__device__ __forceinline__ void load_batch(const uint32_t* v, uint32_t base, uint32_t n, uint32_t (&x)[16]) {
+  const uint32_t l4 = 4u * lane_id();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t e = base + 256u * j + l4;
+    if (e + 3 < n) {
+      const uint4 t = *reinterpret_cast<const uint4*>(v + e);
+      x[4 * j] = t.x; x[4 * j + 1] = t.y; x[4 * j + 2] = t.z; x[4 * j + 3] = t.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] = (e + i < n) ? v[e + i] : 0u;
+    }
+  }
+}
 
 // Histogram of bits [shift, shift + nbits) of the keys whose higher bits equal prefix.
+// keys must be 16-byte aligned.
 __device__ void hist_pass(const uint32_t* keys, uint32_t n, uint32_t prefix, uint32_t pmask, int shift,
                           int nbits, uint32_t* hist) {
   const int lane = lane_id();
   const uint32_t dmask = (1u << nbits) - 1u;
   for (int b = lane; b < kBins; b += 64) hist[b] = 0;
   wave_lds_fence();
-  for (uint32_t base = 0; base < n; base += 512) {
-    uint32_t kk[8];
+  uint32_t cur[16], nxt[16];
+  if (n > 0) load_batch(keys, 0, n, cur);
+  for (uint32_t base = 0; base < n; base += kBatch) {
+    if (base + kBatch < n) load_batch(keys, base + kBatch, n, nxt);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      kk[j] = e < n ? keys[e] : 0u;
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t e = base + 256u * (q >> 2) + 4u * lane + (q & 3);
+      if (e < n && (cur[q] & pmask) == prefix) atomicAdd(&hist[(cur[q] >> shift) & dmask], 1u);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      if (e < n && (kk[j] & pmask) == prefix) atomicAdd(&hist[(kk[j] >> shift) & dmask], 1u);
-    }
+    for (int q = 0; q < 16; ++q) cur[q] = nxt[q];
   }
   wave_lds_fence();
 }
@@ -351,6 +369,60 @@ __device__ void find_digit(const uint32_t* hist, uint32_t krem, uint32_t& d, uin
   wave_lds_fence();
 }
 
+// Exclusive prefix over lanes of a per-lane count c in 0..7, and the wave total.
+__device__ __forceinline__ uint32_t lane_prefix(uint32_t c, uint32_t& total) {
+  const uint64_t b0 = ballot(c & 1u), b1 = ballot(c & 2u), b2 = ballot(c & 4u);
+  total = popc64(b0) + 2u * popc64(b1) + 4u * popc64(b2);
+  return rank_below(b0) + 2u * rank_below(b1) + 4u * rank_below(b2);
+}
+
+// In-place stable compaction keeping the entries with take(key, eq_rank) true, where
+// eq_rank is the number of keys == theta that precede the entry.  Destinations never
+// pass the entries still to be read (out <= index), so the list can be compacted in place.
+template <typename Take>
+__device__ uint32_t compact_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, Take take) {
+  const int lane = lane_id();
+  uint32_t out = 0, eq_seen = 0;
+  uint32_t ck[16], cp[16], nk[16], np[16];
+  if (n > 0) { load_batch(keys, 0, n, ck); load_batch(pos, 0, n, cp); }
+  for (uint32_t base = 0; base < n; base += kBatch) {
+    if (base + kBatch < n) { load_batch(keys, base + kBatch, n, nk); load_batch(pos, base + kBatch, n, np); }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t e0 = base + 256u * j + 4u * lane;
+      uint32_t eqc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eqc += (e0 + i < n && ck[4 * j + i] == theta) ? 1u : 0u;
+      uint32_t eq_tot;
+      uint32_t eq_r = eq_seen + lane_prefix(eqc, eq_tot);
+      bool tk[4];
+      uint32_t tc = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v = e0 + i < n;
+        const bool eq = v && ck[4 * j + i] == theta;
+        tk[i] = v && take(ck[4 * j + i], eq, eq_r);
+        eq_r += eq ? 1u : 0u;
+        tc += tk[i] ? 1u : 0u;
+      }
+      uint32_t t_tot;
+      uint32_t dst = out + lane_prefix(tc, t_tot);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tk[i]) {
+          keys[dst] = ck[4 * j + i];
+          pos[dst] = cp[4 * j + i];
+          ++dst;
+        }
+      out += t_tot;
+      eq_seen += eq_tot;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) { ck[q] = nk[q]; cp[q] = np[q]; }
+  }
+  return out;
+}
+
 // Exact k-th largest key theta among keys[0..n) (n > k) and need_eq, the number of
 // entries equal to theta in the top k (the first need_eq of them in array order).
 __device__ void select_exact(const uint32_t* keys, uint32_t n, uint32_t k, uint32_t* hist, uint32_t& theta,
@@ -370,61 +442,14 @@ __device__ void select_exact(const uint32_t* keys, uint32_t n, uint32_t k, uint3
 
 // In-place stable compaction keeping keys > theta and the first need_eq keys == theta.
 __device__ uint32_t compact_exact(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, uint32_t need_eq) {
-  const int lane = lane_id();
-  uint32_t out = 0, eq_seen = 0;
-  for (uint32_t base = 0; base < n; base += 512) {
-    uint32_t kk[8], pp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      kk[j] = e < n ? keys[e] : 0u;
-      pp[j] = e < n ? pos[e] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      const bool v = e < n;
-      const bool gt = v && kk[j] > theta;
-      const bool eq = v && kk[j] == theta;
-      const uint64_t meq = ballot(eq);
-      const bool take = gt || (eq && eq_seen + rank_below(meq) < need_eq);
-      const uint64_t mt = ballot(take);
-      if (take) {  // destination <= e: never ahead of the entries still to be read
-        keys[out + rank_below(mt)] = kk[j];
-        pos[out + rank_below(mt)] = pp[j];
-      }
-      out += popc64(mt);
-      eq_seen += popc64(meq);
-    }
-  }
-  return out;
+  return compact_list(keys, pos, n, theta, [=](uint32_t key, bool eq, uint32_t eq_rank) {
+    return key > theta || (eq && eq_rank < need_eq);
+  });
 }
 
 // In-place stable compaction keeping every key >= th.
 __device__ uint32_t compact_ge(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t th) {
-  const int lane = lane_id();
-  uint32_t out = 0;
-  for (uint32_t base = 0; base < n; base += 512) {
-    uint32_t kk[8], pp[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      kk[j] = e < n ? keys[e] : 0u;
-      pp[j] = e < n ? pos[e] : 0u;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 64 + lane;
-      const bool take = e < n && kk[j] >= th;
-      const uint64_t mt = ballot(take);
-      if (take) {
-        keys[out + rank_below(mt)] = kk[j];
-        pos[out + rank_below(mt)] = pp[j];
-      }
-      out += popc64(mt);
-    }
-  }
-  return out;
+  return compact_list(keys, pos, n, th, [=](uint32_t key, bool, uint32_t) { return key >= th; });
 }
 
 // Exact top-k of a candidate list: afterwards keys/pos[0..min(n,k)) hold the k largest
@@ -475,13 +500,30 @@ __device__ uint32_t shrink_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint3
 // most causal keys are dispatched first.  With one segment the kernel writes idx
 // directly; with several it writes each segment's top-k list for a merge kernel.
 // ---------------------------------------------------------------------------
+constexpr int kStage = 256;   // staged candidates per token before a bulk append
+
+// Appends the n staged candidates (LDS, in position order) to the global list after its
+// cnt entries; returns the new count.
+__device__ uint32_t flush_stage(const uint32_t* sk, const uint32_t* sp, uint32_t n, uint32_t* keys,
+                                uint32_t* pos, uint32_t cnt) {
+  const int lane = lane_id();
+  wave_lds_fence();
+  for (uint32_t j = lane; j < n; j += 64) {
+    keys[cnt + j] = sk[j];
+    pos[cnt + j] = sp[j];
+  }
+  wave_lds_fence();  // the stage is refilled only after these reads
+  return cnt + n;
+}
+
 struct FusedParams {
   IndexerArgs a;
   int k, cap, S, seg_len, nqb, n_items;
   int32_t* idx;
   uint32_t* row_keys;   // [grid * TQ * cap]
   uint32_t* row_pos;
-  uint32_t* seg_keys;   // [B * Lq * S * k]   (S > 1)
+  int seg_stride;       // entries per row of the segment lists (S * k rounded up to 4)
+  uint32_t* seg_keys;   // [B * Lq * seg_stride]   (S > 1)
   uint32_t* seg_pos;
   int32_t* seg_cnt;     // [B * Lq * S]
   int* counter;
@@ -501,6 +543,10 @@ void indexer_topk_kernel(FusedParams P) {
   __shared__ __attribute__((aligned(16))) float kscl[2][kTileKeys];
   __shared__ __attribute__((aligned(16))) float wsh[TQ * H_I];
   __shared__ uint32_t hist[4][kBins];
+  // per-token staging of admitted candidates: appends are LDS writes, and the global
+  // list receives them in bulk (tile loads then never wait for candidate stores)
+  __shared__ uint32_t stg_key[TQ][kStage];
+  __shared__ uint32_t stg_pos[TQ][kStage];
   __shared__ int item_sh;
 
   const IndexerArgs& a = P.a;
@@ -577,7 +623,7 @@ void indexer_topk_kernel(FusedParams P) {
       for (int hb = 0; hb < HB; ++hb)
         W[tt][hb] = *reinterpret_cast<const f32x4*>(&wsh[(wv_id * TW + tt) * H_I + hb * 16 + 4 * g]);
 
-    uint32_t theta[TW], cnt[TW];
+    uint32_t theta[TW], cnt[TW], scnt[TW];
     float theta_f[TW];  // the float whose order key is theta (-inf: admit every key)
     uint32_t* rk[TW];
     uint32_t* rp[TW];
@@ -585,6 +631,7 @@ void indexer_topk_kernel(FusedParams P) {
     for (int tt = 0; tt < TW; ++tt) {
       theta[tt] = 0u;
       theta_f[tt] = -INFINITY;
+      scnt[tt] = 0u;
       cnt[tt] = 0u;
       rk[tt] = P.row_keys + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
       rp[tt] = P.row_pos + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
@@ -621,21 +668,30 @@ void indexer_topk_kernel(FusedParams P) {
         if (s0 + kTileKeys - 1 > p_t[tt] || s0 + kTileKeys > s_hi) pred = pred && (s <= p_t[tt]) && (s < s_hi);
         const uint64_t m = ballot(pred);
         if (m) {
+          uint32_t* sk = stg_key[wv_id * TW + tt];
+          uint32_t* sp = stg_pos[wv_id * TW + tt];
           if (pred) {
-            rk[tt][cnt[tt] + rank_below(m)] = order_key(val);
-            rp[tt][cnt[tt] + rank_below(m)] = (uint32_t)s;
+            sk[scnt[tt] + rank_below(m)] = order_key(val);
+            sp[scnt[tt] + rank_below(m)] = (uint32_t)s;
           }
-          cnt[tt] += popc64(m);
-          if (cnt[tt] > (uint32_t)(P.cap - kTileKeys)) {
-            cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
-                                  hist[wv_id], theta[tt]);
-            theta_f[tt] = key_to_float(theta[tt]);
+          scnt[tt] += popc64(m);
+          if (scnt[tt] > (uint32_t)(kStage - kTileKeys)) {
+            cnt[tt] = flush_stage(sk, sp, scnt[tt], rk[tt], rp[tt], cnt[tt]);
+            scnt[tt] = 0;
+            if (cnt[tt] > (uint32_t)(P.cap - kStage)) {
+              cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
+                                    hist[wv_id], theta[tt]);
+              theta_f[tt] = key_to_float(theta[tt]);
+            }
           }
         }
       }
     }
 
     // finalize this wave's rows
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt)
+      cnt[tt] = flush_stage(stg_key[wv_id * TW + tt], stg_pos[wv_id * TW + tt], scnt[tt], rk[tt], rp[tt], cnt[tt]);
     __threadfence_block();
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
@@ -647,8 +703,8 @@ void indexer_topk_kernel(FusedParams P) {
         int32_t* out = P.idx + row * P.k;
         for (int j = lane; j < P.k; j += 64) out[j] = j < (int)cnt[tt] ? (int32_t)rp[tt][j] : -1;
       } else {
-        uint32_t* ok = P.seg_keys + (row * P.S + seg) * P.k;
-        uint32_t* op = P.seg_pos + (row * P.S + seg) * P.k;
+        uint32_t* ok = P.seg_keys + row * P.seg_stride + (size_t)seg * P.k;
+        uint32_t* op = P.seg_pos + row * P.seg_stride + (size_t)seg * P.k;
         for (int j = lane; j < (int)cnt[tt]; j += 64) {
           ok[j] = rk[tt][j];
           op[j] = rp[tt][j];
@@ -662,14 +718,14 @@ void indexer_topk_kernel(FusedParams P) {
 // Merge of per-segment top-k lists (segments are in position order, so their
 // concatenation is in ascending position order).  One wave per query row.
 __global__ __launch_bounds__(256) void merge_segments_kernel(uint32_t* seg_keys, uint32_t* seg_pos,
-                                                             const int32_t* seg_cnt, int rows, int S, int k,
+                                                             const int32_t* seg_cnt, int rows, int S, int k, int stride,
                                                              int32_t* idx) {
   __shared__ uint32_t hist[4][kBins];
   const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wv_id;
   if (row >= rows) return;
-  uint32_t* bk = seg_keys + (size_t)row * S * k;
-  uint32_t* bp = seg_pos + (size_t)row * S * k;
+  uint32_t* bk = seg_keys + (size_t)row * stride;
+  uint32_t* bp = seg_pos + (size_t)row * stride;
   // pack the lists contiguously at the start of the row's region (moves only downwards)
   uint32_t n = 0;
   for (int sg = 0; sg < S; ++sg) {
@@ -738,7 +794,7 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, uint32_t* 
 }
 
 struct FusedPlan {
-  int TQ, nqb, S, seg_len, n_items, grid, cap;
+  int TQ, nqb, S, seg_len, n_items, grid, cap, seg_stride;
   size_t off_rowbuf, off_seg, off_cnt, total;
 };
 
@@ -767,7 +823,8 @@ static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
   off += (size_t)p.grid * p.TQ * p.cap * sizeof(uint32_t) * 2;
   off = (off + 255) / 256 * 256;
   p.off_seg = off;
-  if (S > 1) off += (size_t)B * Lq * S * k * sizeof(uint32_t) * 2;
+  p.seg_stride = (S * k + 3) / 4 * 4;  // 16-byte aligned rows
+  if (S > 1) off += (size_t)B * Lq * p.seg_stride * sizeof(uint32_t) * 2;
   off = (off + 255) / 256 * 256;
   p.off_cnt = off;
   if (S > 1) off += (size_t)B * Lq * S * sizeof(int32_t);
@@ -806,7 +863,8 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.row_keys = reinterpret_cast<uint32_t*>(w8 + pl.off_rowbuf);
   P.row_pos = P.row_keys + (size_t)pl.grid * pl.TQ * pl.cap;
   P.seg_keys = reinterpret_cast<uint32_t*>(w8 + pl.off_seg);
-  P.seg_pos = P.seg_keys + (size_t)a.B * a.Lq * pl.S * k;
+  P.seg_stride = pl.seg_stride;
+  P.seg_pos = P.seg_keys + (size_t)a.B * a.Lq * pl.seg_stride;
   P.seg_cnt = reinterpret_cast<int32_t*>(w8 + pl.off_cnt);
   P.counter = reinterpret_cast<int*>(w8);
   zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 1);
@@ -816,7 +874,7 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   if (e != hipSuccess) return e;
   if (pl.S > 1) {
     const int rows = a.B * a.Lq;
-    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k, idx);
+    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k, pl.seg_stride, idx);
     e = hipGetLastError();
   }
   return e;
