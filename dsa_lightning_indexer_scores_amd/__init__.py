@@ -153,15 +153,19 @@ def indexer_scores(q, k, w, q_scale=None, k_scale=None, out=None, stream=None):
     return out
 
 
-def topk(scores, k, n_valid=None, return_vals=False, stream=None):
-    """Deterministic top-k over the rows of a 2-D (or batched) fp32 score tensor."""
+def topk(scores, k, n_valid=None, return_vals=False, ws=None, stream=None):
+    """Deterministic top-k over the rows of a 2-D (or batched) fp32 score tensor.  With a
+    Workspace, few long rows are split over several workgroups."""
     _require_cuda(scores, n_valid)
     n = scores.shape[-1]
     rows = scores.numel() // n
     idx = torch.empty(scores.shape[:-1] + (k,), dtype=torch.int32, device=scores.device)
     vals = torch.empty(idx.shape, dtype=torch.float32, device=scores.device) if return_vals else None
+    buf, nbytes = None, 0
+    if ws is not None:
+        buf, nbytes = ws.get(workspace_size(DSA_OP_TOPK, 0, 1, rows, n, k), scores.device)
     _check("dsa_topk", load_library().dsa_topk(
-        _ptr(scores), n, rows, n, _ptr(n_valid), k, _ptr(idx), _ptr(vals), None, 0, _stream(stream)))
+        _ptr(scores), n, rows, n, _ptr(n_valid), k, _ptr(idx), _ptr(vals), _ptr(buf), nbytes, _stream(stream)))
     return (idx, vals) if return_vals else idx
 
 

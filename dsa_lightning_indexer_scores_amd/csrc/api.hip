@@ -110,7 +110,9 @@ size_t materialised_scores_bytes(int B, int Lq, int Lk) { return round_up((size_
 size_t materialised_hist_bytes(int B, int Lq) { return round_up((size_t)B * Lq * dsa::kRowHistBins * sizeof(uint32_t)); }
 
 size_t indexer_topk_ws(int dtype, int B, int Lq, int Lk, int k) {
-  if (use_materialised(dtype, Lq)) return materialised_scores_bytes(B, Lq, Lk) + materialised_hist_bytes(B, Lq);
+  if (use_materialised(dtype, Lq))
+    return materialised_scores_bytes(B, Lq, Lk) + materialised_hist_bytes(B, Lq) +
+           round_up(dsa::topk_split_ws(B * Lq, Lk, false));
   return dsa::indexer_topk_fused_ws(B, Lq, Lk, k, dtype);
 }
 
@@ -125,12 +127,16 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
   const dsa::IndexerArgs a = make_indexer_args(in, B, Lq, Lk);
   hipError_t e;
   if (use_materialised(in->dtype, Lq)) {
-    float* scores = static_cast<float*>(ws);
-    uint32_t* hist = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + materialised_scores_bytes(B, Lq, Lk));
+    uint8_t* w8 = static_cast<uint8_t*>(ws);
+    float* scores = reinterpret_cast<float*>(w8);
+    const size_t off_hist = materialised_scores_bytes(B, Lq, Lk);
+    const size_t off_split = off_hist + materialised_hist_bytes(B, Lq);
+    uint32_t* hist = reinterpret_cast<uint32_t*>(w8 + off_hist);
     e = dsa::launch_zero(hist, materialised_hist_bytes(B, Lq), s);
     if (e == hipSuccess) e = dsa::launch_indexer_scores(a, scores, hist, s);
     if (e == hipSuccess)
-      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, hist, k, idx, nullptr, s);
+      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, hist, k, idx, nullptr, w8 + off_split,
+                                ws_bytes - off_split, s);
   } else {
     e = dsa::launch_indexer_topk_fused(a, k, idx, ws, ws_bytes, s);
   }
@@ -144,8 +150,9 @@ extern "C" {
 size_t dsa_workspace_size(int op, int dtype, int B, int Lq, int Lk, int k, int heads) {
   if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0) return 0;
   switch (op) {
-    case DSA_OP_TOPK:
-      return 0;
+    case DSA_OP_TOPK:  // optional: B * Lq rows of Lk scores
+      if (k > kMaxTopkK) return 0;
+      return dsa::topk_split_ws(B * Lq, Lk, true);
     case DSA_OP_INDEXER_TOPK:
       if (dtype < DSA_F32 || dtype > DSA_FP8_E4M3 || k > kMaxFusedK || Lq > Lk) return 0;
       return indexer_topk_ws(dtype, B, Lq, Lk, k);
@@ -176,14 +183,13 @@ int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* s
 
 int dsa_topk(const float* scores, int64_t row_stride, int rows, int n, const int32_t* n_valid, int k,
              int32_t* idx, float* vals, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!scores || !idx) return DSA_ERR_ARG;
   if (rows <= 0 || n <= 0 || k <= 0 || k > kMaxTopkK || row_stride < n) return DSA_ERR_ARG;
   if (!aligned(scores, 4) || !aligned(idx, 4) || (vals && !aligned(vals, 4)) || (n_valid && !aligned(n_valid, 4)))
     return DSA_ERR_ALIGN;
+  if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
   const hipError_t e = dsa::launch_topk_rows(scores, row_stride, rows, n, n_valid, 0, 0, nullptr, k, idx, vals,
-                                             static_cast<hipStream_t>(stream));
+                                             ws, ws ? ws_bytes : 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

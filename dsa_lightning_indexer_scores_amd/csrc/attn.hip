@@ -39,7 +39,6 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
 constexpr float kMaxStart = 1e30f;              // initial running maximum is -kMaxStart
 constexpr int kKeyBufs = 4;                     // idx ring slots (j .. j+2 in use)
-constexpr int kQSteps = 18 / 2;                 // 32-dim MFMA steps per wave (half of 576)
 
 __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -75,11 +74,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void mla_attn_kernel(MlaParams P) {
   constexpr int kDvPer = kMlaDv / DVS;          // value dims per wave
   constexpr int kDt = kDvPer / 16;              // 16-dim output tiles per wave
+  constexpr int kQSteps = 18 / DVS;             // 32-dim QK MFMA steps per wave
   constexpr int kSlotsPerWave = (kDmaPerBlk + NW - 1) / NW;
   constexpr int kDummy = kSlotsPerWave * NW - kDmaPerBlk;   // padding slots (fixed counts)
   __shared__ __attribute__((aligned(16))) uint8_t kvs[NB][kBlkBytes + kDummy * 1024];
   __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs][64];   // idx entries of blocks
-  __shared__ __attribute__((aligned(16))) f32x4 xch[2][NW][64];         // partial S^T tiles
+  __shared__ __attribute__((aligned(16))) f32x4 xch[DVS == 2 ? 2 : 1][DVS == 2 ? NW : 1][64];  // partial S^T
   const AttnArgs& a = P.a;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wv_id = uniform(tid >> 6);      // wave index, kept in a scalar register
@@ -160,7 +160,7 @@ void mla_attn_kernel(MlaParams P) {
 #pragma unroll
     for (int ks = 0; ks < kQSteps; ++ks) qop[ks] = qrow[4 * (ks + kQSteps * ds) + g];
   }
-  const int partner = wv_id + (ds == 0 ? hpq : -hpq);   // same head tile, other half
+  const int partner = wv_id + (ds == 0 ? hpq : -hpq);   // same head tile, other half (DVS = 2)
   f32x4 o[kDt];
 #pragma unroll
   for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -237,17 +237,18 @@ void mla_attn_kernel(MlaParams P) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
-      xch[j & 1][wv_id][lane] = sp;
+      if constexpr (DVS == 2) xch[j & 1][wv_id][lane] = sp;
     }
     // the next block's rows are requested after this block's QK, which thereby starts
     // right after the barrier
     if (blk + D < blk_end) issue_rows(blk + D, (j + D) % NB);
-    __syncthreads();                                     // partial S^T tiles exchanged
+    if constexpr (DVS == 2) __syncthreads();             // partial S^T tiles exchanged
     if (wave_active) {
       const uint8_t* kb = kvs[buf];
-      // both halves add the two partial tiles (fp32 addition commutes exactly), so both
-      // hold the same S^T; lane holds head h, keys 4g+jj of the block
-      const f32x4 s = sp + xch[j & 1][partner][lane];
+      // with DVS = 2 both halves add the two partial tiles (fp32 addition commutes
+      // exactly), so both hold the same S^T; lane holds head h, keys 4g+jj of the block
+      f32x4 s = sp;
+      if constexpr (DVS == 2) s = sp + xch[j & 1][partner][lane];
       const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j & (kKeyBufs - 1)][4 * g]);
       const bool v0 = (uint32_t)kk4.x < (uint32_t)a.Lk, v1 = (uint32_t)kk4.y < (uint32_t)a.Lk;
       const bool v2 = (uint32_t)kk4.z < (uint32_t)a.Lk, v3 = (uint32_t)kk4.w < (uint32_t)a.Lk;

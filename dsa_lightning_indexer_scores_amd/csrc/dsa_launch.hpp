@@ -35,9 +35,12 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
                                      size_t ws_bytes, hipStream_t s);
 
 // --- top-k over materialised rows -------------------------------------------
+// With scratch of at least topk_split_ws(rows, n, row_hist == nullptr) bytes, few long
+// rows are split over several workgroups; otherwise one workgroup handles a row.
+size_t topk_split_ws(int rows, int n, bool with_hist);
 hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, int n,
                             const int32_t* n_valid, int causal_Lq, int causal_Lk, const uint32_t* row_hist,
-                            int k, int32_t* idx, float* vals, hipStream_t s);
+                            int k, int32_t* idx, float* vals, void* scratch, size_t scratch_bytes, hipStream_t s);
 
 // --- sparse attention --------------------------------------------------------
 struct AttnArgs {

@@ -130,7 +130,8 @@ typedef struct {
  * Bytes of device workspace needed by `op` (a dsa_op) for these sizes; 0 if none.
  * dtype is the indexer dtype for DSA_OP_INDEXER_TOPK / DSA_OP_LAYER_GROUP and the
  * attention dtype for DSA_OP_SPARSE_ATTN; `heads` is the attention head count H for
- * DSA_OP_SPARSE_ATTN and DSA_OP_LAYER_GROUP (0 elsewhere).  The value covers both
+ * DSA_OP_SPARSE_ATTN and DSA_OP_LAYER_GROUP (0 elsewhere).  For DSA_OP_TOPK the rows
+ * are B * Lq rows of Lk scores (the optional workspace of dsa_topk).  The value covers both
  * idx_q_stride conventions of dsa_sparse_attn.  Pure host arithmetic, no device call;
  * returns 0 for invalid arguments (the entry point then reports them).
  */
@@ -154,7 +155,10 @@ int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* s
  * entries are candidates (n_valid == NULL means n for every row).  Writes idx[r, 0..k)
  * (ascending positions, -1 padding, ties to the lower position) and, if vals != NULL,
  * vals[r, j] = score of idx[r, j] (-inf for padding).  Requires 1 <= k <= 65536,
- * n >= 1, row_stride >= n.  Needs no workspace: ws may be NULL (ws_bytes ignored).
+ * n >= 1, row_stride >= n.  The workspace is optional: with ws == NULL one workgroup
+ * handles each row; with ws of at least dsa_workspace_size(DSA_OP_TOPK, 0, 1, rows, n,
+ * k, 0) bytes (256-byte aligned), few long rows are split over several workgroups.
+ * Both give the same result.
  */
 int dsa_topk(const float* scores, int64_t row_stride, int rows, int n,
              const int32_t* n_valid, int k, int32_t* idx, float* vals, void* ws,

@@ -91,15 +91,17 @@ def test_topk_bitexact_edge_cases(case):
         x = (rng.standard_normal((rows, n)) * 3).astype(np.float32)
         nv = np.array([n, 150000], dtype=np.int32)
     ref = oracle.topk_rows(x.astype(np.float64), nv, k)
-    got_idx, got_val = dsa.topk(torch.from_numpy(x).to(DEV), k, n_valid=torch.from_numpy(nv).to(DEV),
-                                return_vals=True)
-    got_idx = got_idx.cpu().numpy()
-    assert np.array_equal(got_idx, ref)
-    gv = got_val.cpu().numpy()
-    for r in range(rows):
-        sel = ref[r] >= 0
-        assert np.array_equal(gv[r][sel], x[r][ref[r][sel]])
-        assert np.all(np.isneginf(gv[r][~sel]))
+    # one workgroup per row, then (with a workspace) rows split over several workgroups
+    for ws in (None, dsa.Workspace()):
+        got_idx, got_val = dsa.topk(torch.from_numpy(x).to(DEV), k, n_valid=torch.from_numpy(nv).to(DEV),
+                                    return_vals=True, ws=ws)
+        got_idx = got_idx.cpu().numpy()
+        assert np.array_equal(got_idx, ref)
+        gv = got_val.cpu().numpy()
+        for r in range(rows):
+            sel = ref[r] >= 0
+            assert np.array_equal(gv[r][sel], x[r][ref[r][sel]])
+            assert np.all(np.isneginf(gv[r][~sel]))
 
 
 # ---------------------------------------------------------------------------
