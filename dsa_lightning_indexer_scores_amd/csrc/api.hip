@@ -106,7 +106,9 @@ dsa::AttnArgs make_attn_args(const dsa_attn_in* in, int B, int Lq, int Lk, const
   return a;
 }
 
-size_t materialised_scores_bytes(int B, int Lq, int Lk) { return round_up((size_t)B * Lq * Lk * sizeof(float)); }
+// materialised score rows start on 256-byte boundaries (whole-line stores)
+int64_t score_stride(int Lk) { return ((int64_t)Lk + 63) / 64 * 64; }
+size_t materialised_scores_bytes(int B, int Lq, int Lk) { return round_up((size_t)B * Lq * score_stride(Lk) * sizeof(float)); }
 size_t materialised_hist_bytes(int B, int Lq) { return round_up((size_t)B * Lq * dsa::kRowHistBins * sizeof(uint32_t)); }
 
 size_t indexer_topk_ws(int dtype, int B, int Lq, int Lk, int k) {
@@ -133,9 +135,9 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
     const size_t off_split = off_hist + materialised_hist_bytes(B, Lq);
     uint32_t* hist = reinterpret_cast<uint32_t*>(w8 + off_hist);
     e = dsa::launch_zero(hist, materialised_hist_bytes(B, Lq), s);
-    if (e == hipSuccess) e = dsa::launch_indexer_scores(a, scores, hist, s);
+    if (e == hipSuccess) e = dsa::launch_indexer_scores(a, scores, score_stride(Lk), hist, s);
     if (e == hipSuccess)
-      e = dsa::launch_topk_rows(scores, Lk, B * Lq, Lk, nullptr, Lq, Lk, hist, k, idx, nullptr, w8 + off_split,
+      e = dsa::launch_topk_rows(scores, score_stride(Lk), B * Lq, Lk, nullptr, Lq, Lk, hist, k, idx, nullptr, w8 + off_split,
                                 ws_bytes - off_split, s);
   } else {
     e = dsa::launch_indexer_topk_fused(a, k, idx, ws, ws_bytes, s);
@@ -176,7 +178,7 @@ int dsa_indexer_scores(const dsa_indexer_in* in, int B, int Lq, int Lk, float* s
   if (st != DSA_OK) return st;
   if (!scores) return DSA_ERR_ARG;
   if (!aligned(scores, 4)) return DSA_ERR_ALIGN;
-  const hipError_t e = dsa::launch_indexer_scores(make_indexer_args(in, B, Lq, Lk), scores, nullptr,
+  const hipError_t e = dsa::launch_indexer_scores(make_indexer_args(in, B, Lq, Lk), scores, Lk, nullptr,
                                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

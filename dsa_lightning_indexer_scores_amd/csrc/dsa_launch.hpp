@@ -24,9 +24,11 @@ inline int topk_buffer_capacity(int k) {
 }
 
 // --- indexer ---------------------------------------------------------------
+// scores: row r = (b, i) at scores + r * stride (stride >= Lk).
 // row_hist (optional, [B*Lq][2048] uint32, zeroed by the caller): per-row histogram of
 // the top 11 bits of the order keys of the causal scores.
-hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s);
+hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, int64_t stride, uint32_t* row_hist,
+                                 hipStream_t s);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 constexpr int kRowHistBins = 2048;
 // Fused streaming indexer + top-k for query counts large enough to fill the GPU.

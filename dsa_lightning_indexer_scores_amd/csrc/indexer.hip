@@ -186,7 +186,8 @@ static int rowscan_chunk(int rows, int Lk) {
 
 template <int DT, int HB>
 __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, float* __restrict__ scores,
-                                                              uint32_t* __restrict__ row_hist, int chunk_keys) {
+                                                              int64_t stride, uint32_t* __restrict__ row_hist,
+                                                              int chunk_keys) {
   __shared__ uint32_t lhist[kRowHistBins];
   constexpr int RB = IdxTraits<DT>::kRowBytes;
   const int n_chunks = (a.Lk + chunk_keys - 1) / chunk_keys;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
   const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6, g = lane >> 4;
   const int s_begin = chunk * chunk_keys;
   const int s_end = min(a.Lk, s_begin + chunk_keys);
-  float* out = scores + (size_t)qrow * a.Lk;
+  float* out = scores + (size_t)qrow * stride;
 
   const uint8_t* qptr = reinterpret_cast<const uint8_t*>(a.q) + (size_t)qrow * a.H_I * RB;
   Op<DT> A[HB];
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
 }
 
 // Reference-size fp32 path: one thread per (query, key); q row and weights in LDS.
-__global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* __restrict__ scores,
+__global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* __restrict__ scores, int64_t stride,
                                                           uint32_t* __restrict__ row_hist) {
   extern __shared__ float smem[];
   const int n_chunks = (a.Lk + 255) / 256;
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a, float* 
     val = acc;
     if (row_hist) atomicAdd(&row_hist[(size_t)qrow * kRowHistBins + (order_key(val) >> 21)], 1u);
   }
-  scores[(size_t)qrow * a.Lk + s] = val;
+  scores[(size_t)qrow * stride + s] = val;
 }
 
 // ---------------------------------------------------------------------------
@@ -758,14 +759,15 @@ __global__ void zero_ints_kernel(int* p, int n) {
 // Host launchers.
 // ---------------------------------------------------------------------------
 template <int DT>
-static hipError_t rowscan_dispatch(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s) {
+static hipError_t rowscan_dispatch(const IndexerArgs& a, float* scores, int64_t stride, uint32_t* row_hist,
+                                   hipStream_t s) {
   const int chunk = rowscan_chunk(a.B * a.Lq, a.Lk);
   dim3 grid((unsigned)((a.Lk + chunk - 1) / chunk) * (unsigned)(a.B * a.Lq));
   switch (a.H_I / 16) {
-    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
-    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
-    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
-    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores, row_hist, chunk); break;
+    case 1: indexer_rowscan_kernel<DT, 1><<<grid, 256, 0, s>>>(a, scores, stride, row_hist, chunk); break;
+    case 2: indexer_rowscan_kernel<DT, 2><<<grid, 256, 0, s>>>(a, scores, stride, row_hist, chunk); break;
+    case 3: indexer_rowscan_kernel<DT, 3><<<grid, 256, 0, s>>>(a, scores, stride, row_hist, chunk); break;
+    default: indexer_rowscan_kernel<DT, 4><<<grid, 256, 0, s>>>(a, scores, stride, row_hist, chunk); break;
   }
   return hipGetLastError();
 }
@@ -782,15 +784,16 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, uint32_t* row_hist, hipStream_t s) {
+hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, int64_t stride, uint32_t* row_hist,
+                                 hipStream_t s) {
   if (a.dtype == DSA_F32) {
     dim3 grid((unsigned)((a.Lk + 255) / 256) * (unsigned)(a.B * a.Lq));
     const size_t smem = (size_t)(a.H_I * a.d_I + a.H_I) * sizeof(float);
-    indexer_f32_kernel<<<grid, 256, smem, s>>>(a, scores, row_hist);
+    indexer_f32_kernel<<<grid, 256, smem, s>>>(a, scores, stride, row_hist);
     return hipGetLastError();
   }
-  if (a.dtype == DSA_BF16) return rowscan_dispatch<DSA_BF16>(a, scores, row_hist, s);
-  return rowscan_dispatch<DSA_FP8_E4M3>(a, scores, row_hist, s);
+  if (a.dtype == DSA_BF16) return rowscan_dispatch<DSA_BF16>(a, scores, stride, row_hist, s);
+  return rowscan_dispatch<DSA_FP8_E4M3>(a, scores, stride, row_hist, s);
 }
 
 struct FusedPlan {
