@@ -39,7 +39,7 @@ TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn_kernel", "profiles/mla_attn_kernel_
                    "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
 PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
                '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
-               '--copy-calibration')
+               '--no-chunk1m --copy-calibration')
 COPY_BYTES = 1 << 30
 
 
@@ -94,6 +94,25 @@ def recorded_traffic(name):
     if fields.get("source_digest") != source_digest(kernel):
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+def summarize_trace(trace_csv):
+    """Per (kernel, grid size) launch statistics of a rocprofv3 kernel trace: the same
+    kernel is launched with different grids by the workloads of one benchmark run."""
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Kernel_Name"]
+            if "dsa::" not in name:
+                continue
+            grid = (r.get("Grid_Size_X") or r.get("Grid_Size") or "?", r.get("Grid_Size_Y", "1"))
+            dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            groups.setdefault((name, grid), []).append(dur)
+    lines = ["kernel,grid_x,grid_y,calls,avg_us,min_us,max_us"]
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f'"{name}",{grid[0]},{grid[1]},{len(d)},{sum(d) / len(d) / 1e3:.2f},'
+                     f'{min(d) / 1e3:.2f},{max(d) / 1e3:.2f}')
+    return "\n".join(lines)
 
 
 def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
@@ -164,6 +183,8 @@ def parse():
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the HBM traffic summary of two rocprofv3 counter runs and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="print per (kernel, grid) launch statistics of a rocprofv3 kernel trace and exit")
     ap.add_argument("--kernel", default="mla_attn_kernel")
     ap.add_argument("--template", default="")
     return ap.parse_args()
@@ -171,6 +192,9 @@ def parse():
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.kernel, args.template, args.workload))
         return
