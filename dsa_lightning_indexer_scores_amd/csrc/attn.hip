@@ -335,22 +335,34 @@ void mla_attn_kernel(MlaParams P) {
   }
 }
 
-// Combine split partials: one workgroup (128 threads x 4 dims) per (query, head).
+// Combine split partials: one workgroup (128 threads x 4 dims) per (query, head).  All
+// partials (at most kMaxSplit) are requested before any is used.
+constexpr int kMaxSplit = 8;
 __global__ __launch_bounds__(128) void mla_combine_kernel(const float* __restrict__ part_o,
                                                           const float* __restrict__ part_ml, int n_split,
                                                           void* out, int out_dtype, float* lse) {
   const size_t qh = blockIdx.x;
   const float* ml = part_ml + qh * n_split * 2;
+  // slots past n_split re-read the last partial and get weight 0
+  float m[kMaxSplit], l[kMaxSplit];
+  f32x4 v[kMaxSplit];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    const int spc = min(sp, n_split - 1);
+    m[sp] = ml[2 * spc];
+    l[sp] = ml[2 * spc + 1];
+    v[sp] = *reinterpret_cast<const f32x4*>(part_o + (qh * n_split + spc) * kMlaDv + 4 * threadIdx.x);
+  }
   float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, ml[2 * sp]);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) M = fmaxf(M, m[sp]);
   float L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < n_split; ++sp) {
-    const float m = ml[2 * sp], l = ml[2 * sp + 1];
-    const float sc = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    L += sc * l;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (qh * n_split + sp) * kMlaDv + 4 * threadIdx.x);
-    acc += sc * v;
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplit; ++sp) {
+    const float sc = (sp >= n_split || m[sp] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m[sp] - M);
+    L += sc * l[sp];
+    acc += sc * v[sp];
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (out_dtype == DSA_F32) {
@@ -443,7 +455,7 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   int split = 1;
   if (p.n_groups < 1024) {       // split the keys to fill the GPU (decode)
     split = (1024 + p.n_groups - 1) / p.n_groups;
-    if (split > 8) split = 8;
+    if (split > kMaxSplit) split = kMaxSplit;
     if (split > n_blk) split = n_blk;
   }
   p.bps = (n_blk + split - 1) / split;
@@ -484,7 +496,7 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
   if (pl.nw <= 4) {
-    if (split) mla_attn_kernel<4, 2, 2, true, 3><<<grid, 256, 0, s>>>(P);
+    if (split) mla_attn_kernel<4, 2, 3, true, 2><<<grid, 256, 0, s>>>(P);
     else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);
   } else {
     if (split) mla_attn_kernel<8, 2, 2, true, 3><<<grid, 512, 0, s>>>(P);
