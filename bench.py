@@ -8,10 +8,11 @@ Inputs are resident in HBM before the timed region starts.
 
 Also reported (same JSON line): decode at 64 x 200K (1 new token per sequence) step and
 per-token latency, the all-layers-Full comparator (every layer runs its own indexer),
-per-kernel HIP-event timings with their roofline fractions, and the CPU oracle timed on a
-bounded sample of query rows.
+per-kernel HIP-event timings with their roofline fractions, an 80-layer stack run one call
+per layer under the FSSS, released (freq 4, offset 3) and all-Full schedules, and the CPU
+oracle timed on a bounded sample of query rows.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-stack]
 """
 import argparse
 import csv
@@ -178,6 +179,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-allfull", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 80-layer stack at the prefill workload")
     ap.add_argument("--no-chunk1m", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
@@ -338,6 +340,8 @@ def main():
                                 "pages_context": "1.82x prefill / 1.48x decode end-to-end at 200K (30B model); "
                                                  ">=1.3x for 744B above 100K; hardware not stated"}
         log(f"[bench] all-Full group {ms_af:.2f} ms vs IndexShare {ms_step:.2f} ms")
+        if not args.no_stack:
+            result["stack80"] = bench_stack(dsa, torch, inds, layers, outs, ws, k, stream)
         del others, inds, idxs
 
     if args.copy_calibration:
@@ -362,6 +366,32 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_stack(dsa, torch, inds, layers, outs, ws, k, stream, n=80):
+    """An n-layer stack run one call per layer (dsa.LayerStack), under three schedules:
+    20 x FSSS (freq 4, offset 0), the released configuration (freq 4, offset 3) and
+    all-Full (every layer runs its own indexer).  Layer l uses the operands of group
+    position l % 4 (the workload's four layers), so the stack needs no more memory."""
+    res = {"layers": n, "workload_layers_reused": len(layers)}
+    sched = {"fsss": dsa.layer_schedule(n, freq=4, offset=0),
+             "released_freq4_offset3": dsa.layer_schedule(n, freq=4, offset=3),
+             "all_full": dsa.layer_schedule(n, freq=1, offset=0)}
+    for name, anchors in sched.items():
+        st = dsa.LayerStack(anchors, k, ws=ws)
+        m = len(layers)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for l in range(n):
+            st.layer(l, layers[l % m], indexer=inds[l % m] if st.is_full(l) else None, out=outs[l % m])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = {"full_layers": st.n_full, "s": round(e0.elapsed_time(e1) / 1e3, 3)}
+        log(f"[bench] {n}-layer stack, {name}: {st.n_full} Full layers, {res[name]['s']:.3f} s")
+        del st
+    res["all_full_over_fsss"] = round(res["all_full"]["s"] / res["fsss"]["s"], 3)
+    return res
 
 
 def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):

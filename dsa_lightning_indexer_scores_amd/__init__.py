@@ -17,7 +17,7 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
     "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
-    "sparse_attn", "layer_group", "Workspace",
+    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "Workspace",
 ]
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
@@ -73,9 +73,11 @@ def load_library():
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
+    lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
-    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_layer_group"):
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_layer_group",
+               "dsa_layer_schedule"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -261,3 +263,58 @@ def layer_group(full, layers, topk_k, ws=None, return_lse=False, outs=None, idx_
     if return_lse:
         return idx_out, outs, lses
     return idx_out, outs
+
+
+def layer_schedule(n_layers, freq=4, offset=0, pattern=None):
+    """Anchor of every layer of an IndexShare stack (dsa_layer_schedule): the Full layer
+    whose index set the layer attends with; a layer is Full when it is its own anchor.
+    pattern: optional string of 'F' / 'S', one per layer (then freq and offset are unused)."""
+    out = (ctypes.c_int32 * max(int(n_layers), 1))()
+    st = load_library().dsa_layer_schedule(int(n_layers), int(freq), int(offset),
+                                           None if pattern is None else pattern.encode(), out)
+    if st < 0:
+        raise DsaError("dsa_layer_schedule", st)
+    return [int(a) for a in out[:n_layers]]
+
+
+class LayerStack:
+    """The layers of an IndexShare stack, run one call per layer in layer order (the way a
+    model's forward pass reaches them).  A Full layer runs the indexer + top-k on its own
+    operands into the stack's index buffer and then its sparse attention; a Shared layer
+    runs only its sparse attention, with the set its anchor left in the buffer.
+
+    anchors: as returned by layer_schedule.  topk_k: k of the top-k.
+    """
+
+    def __init__(self, anchors, topk_k, ws=None):
+        self.anchors = list(anchors)
+        self.k = int(topk_k)
+        self.ws = ws or Workspace()
+        self.idx = None
+        self.held = None          # the Full layer whose set is in self.idx
+
+    def is_full(self, layer):
+        return self.anchors[layer] == layer
+
+    @property
+    def n_full(self):
+        return sum(1 for l in range(len(self.anchors)) if self.is_full(l))
+
+    def layer(self, l, attn, indexer=None, out=None, out_dtype=None, stream=None):
+        """Run layer l.  attn: the layer's attention operands (as for sparse_attn);
+        indexer: its indexer operands (dict q, k, w, q_scale, k_scale), required for a Full
+        layer and ignored for a Shared one.  Returns the attention output."""
+        if self.is_full(l):
+            if indexer is None:
+                raise ValueError(f"layer {l} is a Full layer: its indexer operands are required")
+            q = indexer["q"]
+            shape = (q.shape[0], q.shape[1], self.k)
+            if self.idx is None or tuple(self.idx.shape) != shape or self.idx.device != q.device:
+                self.idx = torch.empty(shape, dtype=torch.int32, device=q.device)
+            indexer_topk(q, indexer["k"], indexer["w"], self.k, q_scale=indexer.get("q_scale"),
+                         k_scale=indexer.get("k_scale"), ws=self.ws, out=self.idx, stream=stream)
+            self.held = l
+        elif self.held != self.anchors[l]:
+            raise RuntimeError(f"layer {l} attends with the set of layer {self.anchors[l]}, "
+                               f"but the stack holds the set of layer {self.held}")
+        return sparse_attn(attn, self.idx, ws=self.ws, out=out, out_dtype=out_dtype, stream=stream)

@@ -250,6 +250,31 @@ int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n
   return DSA_OK;
 }
 
+int dsa_layer_schedule(int n_layers, int freq, int offset, const char* pattern, int32_t* anchor_out) {
+  if (n_layers < 0 || !anchor_out) return DSA_ERR_ARG;
+  int n_full = 0, last_full = -1;
+  for (int l = 0; l < n_layers; ++l) {
+    bool full;
+    if (pattern) {
+      if (pattern[l] == 'F') full = true;
+      else if (pattern[l] == 'S') full = false;
+      else return DSA_ERR_ARG;              // also a pattern shorter than n_layers
+    } else {
+      if (freq < 1 || offset < 0) return DSA_ERR_ARG;
+      full = l < offset || (l - offset) % freq == 0;
+    }
+    if (full) {
+      last_full = l;
+      ++n_full;
+    } else if (last_full < 0) {
+      return DSA_ERR_ARG;                   // a Shared layer needs a Full layer before it
+    }
+    anchor_out[l] = last_full;
+  }
+  if (pattern && n_layers >= 0 && pattern[n_layers] != '\0') return DSA_ERR_ARG;
+  return n_full;
+}
+
 const char* dsa_status_string(int status) {
   switch (status) {
     case DSA_OK: return "DSA_OK";

@@ -211,6 +211,26 @@ int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n
                     int B, int Lq, int Lk, int k, int32_t* idx_out, void* ws,
                     size_t ws_bytes, void* stream);
 
+/*
+ * Layer schedule of an IndexShare stack ([B] section 5.2: the released configuration
+ * sets index_topk_freq = 4, index_skip_topk_offset = 3 and no explicit pattern, and
+ * after the offset the indexer types repeat full, shared, shared, shared; [A] section
+ * "IndexShare": a Shared layer uses the index set of the nearest Full layer before it).
+ * Host only: no device memory, no stream, nothing enqueued.
+ *   pattern == NULL: layer l is Full when l < offset or (l - offset) % freq == 0
+ *     (freq >= 1, offset >= 0; the pages leave the meaning of the offset open, this reads
+ *     it as that many leading Full layers before the periodic part);
+ *   pattern != NULL: a string of exactly n_layers characters 'F' / 'S' (the explicit
+ *     per-layer pattern); freq and offset are ignored.
+ * anchor_out [n_layers] (host memory, caller-owned) receives, for every layer, the index
+ * of the Full layer whose idx it attends with (its own index for a Full layer).
+ * Returns the number of Full layers (>= 0), or DSA_ERR_ARG for n_layers < 0, a null
+ * anchor_out, freq < 1 or offset < 0 without a pattern, a pattern of another length or
+ * with other characters, or a Shared layer with no Full layer before it (anchor_out is
+ * then partly written).
+ */
+int dsa_layer_schedule(int n_layers, int freq, int offset, const char* pattern, int32_t* anchor_out);
+
 /* Static string naming a status code. */
 const char* dsa_status_string(int status);
 

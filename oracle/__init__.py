@@ -35,6 +35,7 @@ from .dsa import (
     sparse_attention_rows,
     layer_group,
 )
+from .schedule import indexer_types, anchors
 from .accounting import (
     causal_pairs,
     selected_pairs,

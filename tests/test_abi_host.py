@@ -127,3 +127,27 @@ def test_layer_group_argument_errors():
     assert st == -3                                             # layers disagree on H
     st = lib.dsa_layer_group(ctypes.byref(full), None, 1, 1, 64, 64, 16, 0x4000, 0x100000, 1 << 40, None)
     assert st == -1
+
+
+def test_layer_schedule_matches_the_oracle():
+    # host-only entry point: no device memory, callable without a GPU
+    import oracle
+    for n in (0, 1, 4, 7, 80):
+        for freq in (1, 2, 4, 5):
+            for off in (0, 1, 3):
+                ref = oracle.anchors(oracle.indexer_types(n, freq=freq, offset=off))
+                assert dsa.layer_schedule(n, freq=freq, offset=off) == ref, (n, freq, off)
+    for pat in ("F", "FSSS", "FFFSSSFS", "FSFSSSSF"):
+        assert dsa.layer_schedule(len(pat), pattern=pat) == oracle.anchors(oracle.indexer_types(len(pat), pattern=pat))
+    # the released configuration (freq 4, offset 3) over 80 layers: 3 + 20 Full layers
+    a = dsa.layer_schedule(80, freq=4, offset=3)
+    assert sum(1 for l, x in enumerate(a) if x == l) == 23
+
+
+@pytest.mark.parametrize("args", [(3, 4, 0, b"SFF"), (3, 4, 0, b"FS"), (3, 4, 0, b"FSSS"), (3, 4, 0, b"FSX"),
+                                  (3, 0, 0, None), (3, 4, -1, None), (-1, 4, 0, None)])
+def test_layer_schedule_errors(args):
+    lib = dsa.load_library()
+    out = (ctypes.c_int32 * 8)()
+    assert lib.dsa_layer_schedule(*args, out) == -1
+    assert lib.dsa_layer_schedule(3, 4, 0, None, None) == -1

@@ -287,3 +287,41 @@ def test_layer_group_shares_full_index_set(name, L, k):
     assert ok, msg
     for l in (0, 3):
         _attn_check(layers[l], idx.cpu().numpy(), outs[l], None, rows)
+
+
+# ---------------------------------------------------------------------------
+# IndexShare stack: the released schedule (freq 4, offset 3) over 8 layers
+# ---------------------------------------------------------------------------
+
+def test_layer_stack_follows_the_schedule():
+    L, k, n = 900, 128, 8
+    cfg = synth.get_config("prefill16k", L=L, Lq=L, topk=k)
+    anchors = dsa.layer_schedule(n, freq=4, offset=3)               # F F F F S S S F
+    assert anchors == oracle.anchors(oracle.indexer_types(n, freq=4, offset=3))
+    inds = {l: synth.indexer_inputs(cfg, device=DEV, layer=l) for l in range(n) if anchors[l] == l}
+    layers = [synth.attention_inputs(cfg, layer=l % 4, device=DEV) for l in range(n)]
+    stack = dsa.LayerStack(anchors, k)
+    assert stack.n_full == 5
+    for l in range(n):
+        out = stack.layer(l, layers[l], indexer=inds.get(l), out_dtype=torch.float32)
+        a = anchors[l]
+        ind = inds[a]
+        idx_a = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+        assert stack.held == a and torch.equal(stack.idx, idx_a)       # the anchor's set, bitwise
+        assert torch.equal(out, dsa.sparse_attn(layers[l], idx_a, out_dtype=torch.float32))
+    # a Shared layer whose anchor's set is not held is refused
+    fresh = dsa.LayerStack(anchors, k)
+    with pytest.raises(RuntimeError):
+        fresh.layer(4, layers[4])
+    with pytest.raises(ValueError):
+        fresh.layer(0, layers[0])
+    # oracle on sampled rows of the last Shared layer (anchor 3)
+    rows = [0, k - 1, L // 2, L - 1]
+    ora = indexer_to_oracle(inds[3])
+    sc = _oracle_rows(ora, 0, rows, L, L)
+    ref = oracle.topk_rows(sc, [r + 1 for r in rows], k)
+    idx3 = dsa.indexer_topk(inds[3]["q"], inds[3]["k"], inds[3]["w"], k, **_ind_args(inds[3]))
+    ok, _, msg = index_sets_agree(idx3.cpu().numpy()[0][rows], ref, sc, [r + 1 for r in rows], k, TAU["bf16"])
+    assert ok, msg
+    out6 = dsa.sparse_attn(layers[6], idx3, out_dtype=torch.float32)
+    _attn_check(layers[6], idx3.cpu().numpy(), out6, None, rows)
