@@ -45,6 +45,11 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
 
+template <int N>
+struct Phase {
+  static constexpr int value = N;
+};
+
 __device__ __forceinline__ f32x4 sp_plus(f32x4 lo_half, f32x4 hi_half) { return lo_half + hi_half; }
 
 // LDS chunk slot of global 16-byte chunk c of block row r (an involution).
@@ -335,6 +340,273 @@ void mla_attn_kernel(MlaParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 32-key blocks (two 16-key sub-blocks) for workgroups of four waves, i.e. one query of
+// 32 heads: the waves form two pairs (one per head tile); wave ds of a pair scores
+// sub-block ds over all 576 latent dims, the pair exchanges the block maximum and then
+// the two-part (hi, lo) bf16 probabilities through LDS, and each wave accumulates its
+// 256 value dims over all 32 keys.  Compared with 16-key blocks split by latent dims, a
+// V^T operand now carries 8 distinct keys (two transposed reads, no duplication), the
+// hi and lo parts of p are two MFMAs on the same operand, and each 32 keys take three
+// barriers and one max reduction instead of four and two.
+// ---------------------------------------------------------------------------
+constexpr int kBlk2 = 32;                        // keys per block
+constexpr int kBlk2Bytes = 2 * kBlkBytes;        // 36864
+constexpr int kDmaPerBlk2 = kBlk2Bytes / 1024;   // 36 wave-wide 1 KB direct-to-LDS loads
+constexpr int kKeyBufs2 = 4;                     // idx ring slots (j .. j+2 in use)
+
+template <bool SPLIT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void mla_attn32_kernel(MlaParams P) {
+  constexpr int NW = 4;
+  constexpr int kDt = 16;                        // 16-dim output tiles per wave (256 dims)
+  constexpr int kQSteps = 18;                    // 32-dim QK steps over the 576 latent dims
+  constexpr int kSlots = kDmaPerBlk2 / NW;       // 9 loads per wave per block
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kBlk2Bytes];
+  __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs2][kBlk2];
+  __shared__ __attribute__((aligned(16))) float xm[NW][64];     // block maxima, then l
+  __shared__ __attribute__((aligned(16))) i32x4 xp[NW][64];     // packed (hi, lo) p
+  const AttnArgs& a = P.a;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv_id = uniform(tid >> 6);
+  const int hpq = a.H / 16;                      // head tiles per query (1 or 2)
+  const int ng = P.n_groups;
+  int grp;
+  {
+    const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
+    const int per = ng >> 3, rem = ng & 7;
+    grp = (xcd < rem) ? xcd * (per + 1) + jj : rem * (per + 1) + (xcd - rem) * per + jj;
+  }
+  const int split = blockIdx.y;
+  const int b = grp / a.Lq;
+  const int i = grp - b * a.Lq;                  // one query per workgroup
+  const int ht = wv_id % hpq;                    // head tile
+  const int ds = wv_id / hpq;                    // sub-block scored, value half accumulated
+  const bool wave_active = wv_id < 2 * hpq;
+  const int partner = ds == 0 ? wv_id + hpq : wv_id - hpq;
+  const int32_t* idx_row = a.idx_q_stride ? a.idx + (size_t)b * a.Lq * a.idx_q_stride + (size_t)i * a.idx_q_stride
+                                          : a.idx + (size_t)b * a.topk;
+  const int n_blk_total = (a.topk + kBlk2 - 1) / kBlk2;
+  const int blk_begin = split * P.blocks_per_split;
+  const int blk_end = min(n_blk_total, blk_begin + P.blocks_per_split);
+  const int nb = blk_end - blk_begin;
+  const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride * 2;
+  const uint32_t row_bytes32 = (uint32_t)(a.k_row_stride * 2);
+
+  // idx entries of the t-th block of this range into ring slot t % 4 (lanes 0..31; every
+  // wave issues the same load); positions past topk are -1
+  auto issue_keys = [&](int t) {
+    int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
+    const int pos = (blk_begin + t) * kBlk2 + lane;
+    if (lane < kBlk2) {
+      if (pos < a.topk) dma_4(idx_row + pos, lds_offset(slot));
+      else slot[lane] = -1;
+    }
+  };
+  // the block's 32 latent rows (row r at r * 1152, 16-byte chunks swizzled as swz(r, c))
+  int dma_row[kSlots];
+  uint32_t dma_off[kSlots];
+#pragma unroll
+  for (int u = 0; u < kSlots; ++u) {
+    const int piece = (wv_id + u * NW) * 64 + lane;
+    const int r = piece / kChunks;
+    dma_row[u] = r;
+    dma_off[u] = 16 * swz(r, piece - r * kChunks);
+  }
+  // loads u0 .. u1-1 of this wave for the t-th block
+  auto issue_rows = [&](int t, int buf, auto u0c, auto u1c) {
+    constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
+    const int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
+    int key[u1 - u0];
+#pragma unroll
+    for (int u = u0; u < u1; ++u) key[u - u0] = slot[dma_row[u]];
+#pragma unroll
+    for (int u = u0; u < u1; ++u) {
+      const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
+      dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(&kvs[buf][(wv_id + u * NW) * 1024]));
+    }
+  };
+  using C0 = Phase<0>;
+  using C3 = Phase<3>;
+  using C6 = Phase<6>;
+  using C9 = Phase<kSlots>;
+
+  if (nb > 0) issue_keys(0);
+  if (nb > 1) issue_keys(1);
+  // Q^T operand over all 576 dims: head h, dims [32 ks + 8 g, +8)
+  const int h = ht * 16 + r16;
+  bf16x8 qop[kQSteps];
+  {
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+        reinterpret_cast<const uint16_t*>(a.q) + (((size_t)b * a.Lq + i) * a.H + (wave_active ? h : 0)) * kMlaD);
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) qop[ks] = qrow[4 * ks + g];
+  }
+  f32x4 o[kDt];
+#pragma unroll
+  for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_use = -kMaxStart, l_lane = 0.f;
+  const float sl2 = a.sm_scale * kLog2e;
+  // K operand of row r16 of sub-block ds: chunk 4ks+g sits at 128*(ks/2) + 16*swz
+  const int kbase_off = ds * kBlkBytes + r16 * kRowBytes;
+  const int k_off0 = kbase_off + 16 * swz(r16, g);
+  const int k_off1 = kbase_off + 16 * swz(r16, 4 + g);
+  // V^T operand of value dims 256 ds + 16 dt.. (sub-block 0; sub-block 1 is kBlkBytes on)
+  int v_off[4];
+  {
+    const int vrow = 4 * g + (r16 >> 2);
+    const int c0 = 2 * kDt * ds + ((r16 & 3) >> 1);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v_off[u] = vrow * kRowBytes + 16 * swz(vrow, c0 + 2 * u) + 8 * (r16 & 1);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                 // operands and the first idx entries
+  if (nb > 0) {
+    __syncthreads();
+    issue_rows(0, 0, C0{}, C9{});
+  }
+
+  for (int j = 0; j < nb; ++j) {
+    const int buf = j & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of j, idx of j+1
+    __syncthreads();                                     // B1: landed for all; other buffer free
+    // the next block's rows go out in three parts spread over the block (every wave of
+    // the CU would otherwise queue all of its loads at the same moment)
+    if (j + 2 < nb) issue_keys(j + 2);
+    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C0{}, C3{});
+    const uint8_t* kb = kvs[buf];
+    float sv[4];
+    float own_max = -INFINITY;
+    if (wave_active) {
+      // S^T of sub-block ds: two independent chains (even and odd steps)
+      constexpr int kKAhead = 4;
+      bf16x8 kop[kQSteps];
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ++ks)
+        kop[ks] = *reinterpret_cast<const bf16x8*>(kb + (ks & 1 ? k_off1 : k_off0) + 128 * (ks >> 1));
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ks += 2) {
+        s0 = mfma_bf16_16x16x32(kop[ks], qop[ks], s0);
+        s1 = mfma_bf16_16x16x32(kop[ks + 1], qop[ks + 1], s1);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+#pragma unroll
+      for (int ks = 0; ks < kQSteps - kKAhead; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+      const f32x4 s = s0 + s1;
+      // lane holds head h, keys 16 ds + 4 g + jj of the block
+      const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j & (kKeyBufs2 - 1)][16 * ds + 4 * g]);
+      sv[0] = s[0] * sl2;
+      sv[1] = s[1] * sl2;
+      sv[2] = s[2] * sl2;
+      sv[3] = s[3] * sl2;
+      const uint32_t kmax = max(max((uint32_t)kk4.x, (uint32_t)kk4.y), max((uint32_t)kk4.z, (uint32_t)kk4.w));
+      if (ballot(kmax >= (uint32_t)a.Lk)) {      // some entry invalid (rare)
+        sv[0] = (uint32_t)kk4.x < (uint32_t)a.Lk ? sv[0] : -INFINITY;
+        sv[1] = (uint32_t)kk4.y < (uint32_t)a.Lk ? sv[1] : -INFINITY;
+        sv[2] = (uint32_t)kk4.z < (uint32_t)a.Lk ? sv[2] : -INFINITY;
+        sv[3] = (uint32_t)kk4.w < (uint32_t)a.Lk ? sv[3] : -INFINITY;
+      }
+      own_max = wave_max16x4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      xm[wv_id][lane] = own_max;
+    }
+    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C3{}, C6{});
+    __syncthreads();                                     // B2: block maxima exchanged
+    if (wave_active) {
+      // both waves of the pair see the same two maxima, so they raise m_use identically
+      const float bmax = fmaxf(own_max, xm[partner][lane]);
+      const bool need = bmax > m_use + kRescaleGap;
+      if (ballot(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_use - bmax) : 1.f;
+        if (need) m_use = bmax;
+        l_lane *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) o[dt] *= alpha;
+      }
+      float pj[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        pj[jj] = __builtin_amdgcn_exp2f(sv[jj] - m_use);
+        l_lane += pj[jj];
+      }
+      // p = hi + lo, hi = RNE_bf16(p), lo = RNE_bf16(p - hi)
+      const uint32_t h01 = pack_bf16x2(pj[0], pj[1]), h23 = pack_bf16x2(pj[2], pj[3]);
+      const uint32_t l01 = pack_bf16x2(pj[0] - __uint_as_float(h01 << 16), pj[1] - __uint_as_float(h01 & 0xffff0000u));
+      const uint32_t l23 = pack_bf16x2(pj[2] - __uint_as_float(h23 << 16), pj[3] - __uint_as_float(h23 & 0xffff0000u));
+      xp[wv_id][lane] = i32x4{(int)h01, (int)h23, (int)l01, (int)l23};
+    }
+    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C6{}, C9{});
+    __syncthreads();                                     // B3: probabilities exchanged
+    if (wave_active) {
+      const i32x4 mine = xp[wv_id][lane], other = xp[partner][lane];
+      const i32x4 p0 = ds == 0 ? mine : other, p1 = ds == 0 ? other : mine;   // sub-blocks 0, 1
+      const bf16x8 pb_hi = __builtin_bit_cast(bf16x8, i32x4{p0[0], p0[1], p1[0], p1[1]});
+      const bf16x8 pb_lo = __builtin_bit_cast(bf16x8, i32x4{p0[2], p0[3], p1[2], p1[3]});
+      // O^T += V^T . P^T: K slots 8g..8g+3 are keys 4g.. of sub-block 0, 8g+4.. those of 1
+      constexpr int kVAhead = 4;
+      bf16x4 vt0[kDt], vt1[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        vt0[dt] = lds_read_tr16(kb + v_off[dt & 3] + 128 * (dt >> 2));
+        vt1[dt] = lds_read_tr16(kb + kBlkBytes + v_off[dt & 3] + 128 * (dt >> 2));
+      }
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        const bf16x8 va = __builtin_shufflevector(vt0[dt], vt1[dt], 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = mfma_bf16_16x16x32(va, pb_hi, o[dt]);
+        o[dt] = mfma_bf16_16x16x32(va, pb_lo, o[dt]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVAhead, 0);
+#pragma unroll
+      for (int dt = 0; dt < kDt - kVAhead; ++dt) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kVAhead, 0);
+    }
+  }
+
+  // l over the whole block range: each wave summed its own sub-block; add in sub-block order
+  const float l_own = wave_sum16x4(l_lane);
+  __syncthreads();                                       // xm free
+  if (wave_active) xm[wv_id][lane] = l_own;
+  __syncthreads();
+  if (!wave_active) return;
+  const float l_other = xm[partner][lane];
+  const float l_run = ds == 0 ? l_own + l_other : l_other + l_own;
+  const size_t qh = ((size_t)b * a.Lq + i) * a.H + h;
+  const int d0 = 256 * ds;
+  if constexpr (!SPLIT) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (a.out_dtype == DSA_F32) {
+      float* orow = reinterpret_cast<float*>(a.out) + qh * kMlaDv + d0;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(orow + 16 * dt + 4 * g) = o[dt] * inv;
+    } else {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + qh * kMlaDv + d0;
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (__bf16)(o[dt][e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 16 * dt + 4 * g) = v;
+      }
+    }
+    if (a.lse && g == 0 && ds == 0) a.lse[qh] = l_run > 0.f ? (m_use + log2f(l_run)) / kLog2e : -INFINITY;
+  } else {
+    float* po = P.part_o + (qh * P.n_split + split) * kMlaDv + d0;
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * g) = o[dt];
+    if (g == 0 && ds == 0) {
+      P.part_ml[(qh * P.n_split + split) * 2 + 0] = m_use;
+      P.part_ml[(qh * P.n_split + split) * 2 + 1] = l_run;
+    }
+  }
+}
+
 // Combine split partials: one workgroup (128 threads x 4 dims) per (query, head).  All
 // partials (at most kMaxSplit) are requested before any is used.
 constexpr int kMaxSplit = 8;
@@ -437,13 +709,15 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 struct MlaPlan {
   int nq, dvs, nw, n_groups, n_split, bps;
+  bool k32;           // mla_attn32_kernel (32-key blocks, one query per workgroup)
   size_t off_o, off_ml, total;
 };
 
 static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   MlaPlan p;
   p.nq = 1;
-  if (idx_q_stride == 0) {  // queries of a sequence share one row: batch them per workgroup
+  p.k32 = H <= 32;          // one query's heads fit two wave pairs
+  if (idx_q_stride == 0 && !p.k32) {  // queries of a sequence share one row: batch them per workgroup
     p.nq = Lq;
     while (p.nq > 1 && (p.nq * (H / 16) * 2 > 8 || Lq % p.nq)) --p.nq;
   }
@@ -451,7 +725,7 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   p.dvs = 2;
   p.nw = p.nq * (H / 16) * p.dvs;
   p.n_groups = B * (Lq / p.nq);
-  const int n_blk = (k + kBlk - 1) / kBlk;
+  const int n_blk = (k + (p.k32 ? kBlk2 : kBlk) - 1) / (p.k32 ? kBlk2 : kBlk);
   int split = 1;
   if (p.n_groups < 1024) {       // split the keys to fill the GPU (decode)
     split = (1024 + p.n_groups - 1) / p.n_groups;
@@ -495,7 +769,10 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   P.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_ml);
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
-  if (pl.nw <= 4) {
+  if (pl.k32) {
+    if (split) mla_attn32_kernel<true><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false><<<grid, 256, 0, s>>>(P);
+  } else if (pl.nw <= 4) {
     if (split) mla_attn_kernel<4, 2, 3, true, 2><<<grid, 256, 0, s>>>(P);
     else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);
   } else {

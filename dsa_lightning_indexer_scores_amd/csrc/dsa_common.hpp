@@ -31,6 +31,13 @@ __device__ __forceinline__ f32x4 mfma_fp8_16x16x128(i32x8 a, i32x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
+// two floats to a bf16 pair (round to nearest even), the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float x, float y) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x, y}, bf16x2));
+}
+
 // ---------------------------------------------------------------------------
 // Order-preserving map float -> uint32 (larger float -> larger key); -0 maps to +0 so
 // that signed zeros tie.  Key 0 is never produced by a finite or infinite float, so
