@@ -34,9 +34,9 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 # summarised under profiles/.  A summary is used only while the kernel's sources still
 # hash to the digest it records; otherwise the traffic is reported as null.
 PKG = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd")
-KERNEL_SOURCES = {"mla_attn_kernel": ["csrc/attn.hip"], "indexer_topk_kernel": ["csrc/indexer.hip"]}
+KERNEL_SOURCES = {"mla_attn32_kernel": ["csrc/attn.hip"], "indexer_topk_kernel": ["csrc/indexer.hip"]}
 COMMON_SOURCES = ["csrc/dsa_common.hpp", "csrc/dsa_launch.hpp", "build_lib.py"]
-TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn_kernel", "profiles/mla_attn_kernel_prefill128k_hbm.txt"),
+TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_kernel_prefill128k_hbm.txt"),
                    "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
 PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
                '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
@@ -187,7 +187,7 @@ def parse():
                     help="print the HBM traffic summary of two rocprofv3 counter runs and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="print per (kernel, grid) launch statistics of a rocprofv3 kernel trace and exit")
-    ap.add_argument("--kernel", default="mla_attn_kernel")
+    ap.add_argument("--kernel", default="mla_attn32_kernel")
     ap.add_argument("--template", default="")
     return ap.parse_args()
 

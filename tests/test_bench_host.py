@@ -27,14 +27,14 @@ def _csv(path, rows):
 
 def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
     fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
-    k = "void dsa::mla_attn_kernel<4, 2, 2, false>(dsa::MlaParams)"
+    k = "void dsa::mla_attn32_kernel<false>(dsa::MlaParams)"
     _csv(fetch, [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 99.0),
                  (5, k, "FETCH_SIZE", 1000.0), (6, k, "FETCH_SIZE", 3000.0),
                  (9, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
     _csv(write, [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 50.0),
                  (5, k, "WRITE_SIZE", 10.0), (6, k, "WRITE_SIZE", 30.0),
                  (9, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
-    text = bench.summarize_counters(str(fetch), str(write), "mla_attn_kernel", "<4, 2, 2, false>", "w")
+    text = bench.summarize_counters(str(fetch), str(write), "mla_attn32_kernel", "<false>", "w")
     fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
     assert float(fields["read_scale"]) == 2.0 and float(fields["write_scale"]) == 1.0
     assert int(fields["launches"]) == 2
