@@ -17,7 +17,7 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
     "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
-    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "Workspace",
+    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "Workspace",
 ]
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
@@ -74,10 +74,11 @@ def load_library():
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
     lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
+    lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_layer_group",
-               "dsa_layer_schedule"):
+               "dsa_layer_schedule", "dsa_quantize_e4m3"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -318,3 +319,31 @@ class LayerStack:
             raise RuntimeError(f"layer {l} attends with the set of layer {self.anchors[l]}, "
                                f"but the stack holds the set of layer {self.held}")
         return sparse_attn(attn, self.idx, ws=self.ws, out=out, out_dtype=out_dtype, stream=stream)
+
+
+def quantize_e4m3(x, codes=None, scales=None, stream=None):
+    """Per-token E4M3 quantization (dsa_quantize_e4m3): x [T, ...] float32 or bfloat16,
+    one token per leading index.  Returns (codes uint8 [T, ...], scales float32 [T]).
+    codes / scales may be given as 2-D [T, n] / 1-D [T] views with a row stride (e.g. the
+    slot of a decode step in a k^I cache: cache[:, p] and scale_cache[:, p])."""
+    _require_cuda(x)
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    T = x.shape[0]
+    n = x[0].numel() if T > 0 else 0
+    x2 = x.reshape(T, n)
+    if x2.stride(1) != 1:
+        raise ValueError("each token's values must be contiguous")
+    if codes is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    c2 = codes.view(T, n) if codes.dim() != 2 else codes     # view: never a silent copy
+    if c2.dtype != torch.uint8 or tuple(c2.shape) != (T, n) or c2.stride(1) != 1:
+        raise ValueError("codes must be uint8 [T, n] with contiguous rows")
+    if scales is None:
+        scales = torch.empty(T, dtype=torch.float32, device=x.device)
+    if scales.dtype != torch.float32 or tuple(scales.shape) != (T,):
+        raise ValueError("scales must be float32 [T]")
+    _check("dsa_quantize_e4m3", load_library().dsa_quantize_e4m3(
+        _ptr(x2), DSA_BF16 if x.dtype == torch.bfloat16 else DSA_F32, T, n, x2.stride(0), _ptr(c2), c2.stride(0),
+        _ptr(scales), scales.stride(0), _stream(stream)))
+    return codes, scales

@@ -250,6 +250,20 @@ int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n
   return DSA_OK;
 }
 
+int dsa_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64_t x_row_stride, uint8_t* codes,
+                      int64_t code_row_stride, float* scales, int64_t scale_stride, void* stream) {
+  if (!x || !codes || !scales) return DSA_ERR_ARG;
+  if (x_dtype != DSA_F32 && x_dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (rows <= 0 || row_elems <= 0 || row_elems > (1 << 20) || (row_elems % 4) != 0) return DSA_ERR_SHAPE;
+  if (x_row_stride < row_elems || code_row_stride < row_elems || scale_stride < 1) return DSA_ERR_SHAPE;
+  const size_t esize = x_dtype == DSA_F32 ? 4 : 2;
+  if (!aligned(x, 4 * esize) || (x_row_stride % 4) != 0) return DSA_ERR_ALIGN;
+  if (!aligned(codes, 4) || (code_row_stride % 4) != 0 || !aligned(scales, 4)) return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_quantize_e4m3(x, x_dtype, rows, row_elems, x_row_stride, codes, code_row_stride,
+                                                 scales, scale_stride, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
 int dsa_layer_schedule(int n_layers, int freq, int offset, const char* pattern, int32_t* anchor_out) {
   if (n_layers < 0 || !anchor_out) return DSA_ERR_ARG;
   int n_full = 0, last_full = -1;

@@ -44,6 +44,12 @@ hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, i
                             const int32_t* n_valid, int causal_Lq, int causal_Lk, const uint32_t* row_hist,
                             int k, int32_t* idx, float* vals, void* scratch, size_t scratch_bytes, hipStream_t s);
 
+// --- per-token E4M3 quantization ---------------------------------------------
+// rows of row_elems values (fp32 or bf16, row r at x + r * x_stride elements) -> codes at
+// codes + r * c_stride bytes and scales[r * s_stride].
+hipError_t launch_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64_t x_stride,
+                                uint8_t* codes, int64_t c_stride, float* scales, int64_t s_stride, hipStream_t s);
+
 // --- sparse attention --------------------------------------------------------
 struct AttnArgs {
   const void* q;

@@ -212,6 +212,28 @@ int dsa_layer_group(const dsa_indexer_in* full, const dsa_attn_in* layers, int n
                     size_t ws_bytes, void* stream);
 
 /*
+ * Per-token E4M3 quantization of indexer operands, the step before the path ([A]
+ * "IndexShare": the indexer is kept FP8-friendly; [B] section 5.2: its own light
+ * projections and a per-layer index-key cache).  Row r holds row_elems values (one
+ * token: H_I * d_I for q^I, d_I for k^I) at x + r * x_row_stride elements, fp32 or bf16
+ * (x_dtype).  It writes
+ *   scales[r * scale_stride] = amax_r / 448 (1 for an all-zero row), single precision;
+ *   codes[r * code_row_stride + e] = OCP E4M3 code of x[r][e] / scale, round to nearest
+ *   even, sign kept.
+ * These are exactly the codes and scales the indexer entry points consume.  Strided
+ * destinations let a decode step append each sequence's new k^I row to its cache slot:
+ * codes = k_cache + p * d_I, code_row_stride = Lk_max * d_I, scales = k_scale_cache + p,
+ * scale_stride = Lk_max.
+ * All pointers are caller-owned device memory.  row_elems must be a multiple of 4 (at most
+ * 2^20), x 16-byte (fp32) or 8-byte (bf16) aligned with x_row_stride a multiple of 4,
+ * codes and scales 4-byte aligned with code_row_stride a multiple of 4.  NaN or infinite
+ * inputs are a precondition violation.  Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE,
+ * DSA_ERR_SHAPE, DSA_ERR_ALIGN or DSA_ERR_HIP.
+ */
+int dsa_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64_t x_row_stride, uint8_t* codes,
+                      int64_t code_row_stride, float* scales, int64_t scale_stride, void* stream);
+
+/*
  * Layer schedule of an IndexShare stack ([B] section 5.2: the released configuration
  * sets index_topk_freq = 4, index_skip_topk_offset = 3 and no explicit pattern, and
  * after the offset the indexer types repeat full, shared, shared, shared; [A] section

@@ -25,7 +25,7 @@ hand-worked examples, closed forms, invariants and library routines (see
 ``tests/test_oracle_*.py``).  No function in this package is "parity unpinned".
 """
 
-from .formats import decode_bf16, decode_e4m3, E4M3_MAX
+from .formats import decode_bf16, decode_e4m3, encode_e4m3, quantize_e4m3_per_token, E4M3_MAX
 from .dsa import (
     causal_position,
     indexer_scores,

@@ -47,3 +47,43 @@ _E4M3 = _e4m3_table()
 def decode_e4m3(codes):
     """uint8 OCP E4M3 codes (any shape) -> float64 values, exactly (NaN for 0x7F/0xFF)."""
     return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+# ---------------------------------------------------------------------------
+# Encoder (the step before the path: per-token quantization of the indexer's q^I and
+# k^I).  The reading is the one the pages leave open, as above: one fp32 scale per token,
+# scale = amax / 448 (1 for an all-zero token), codes = round-to-nearest-even of
+# x / scale in E4M3.  Both divisions are single-precision (IEEE round to nearest), so a
+# device encoder can match the codes bit for bit.
+# ---------------------------------------------------------------------------
+
+_POS_CODES = np.arange(0x7F, dtype=np.uint8)           # 0x00 .. 0x7E: the non-negative finite values
+_POS_VALUES = _E4M3[_POS_CODES]                         # increasing
+
+
+def encode_e4m3(y):
+    """float values with |y| <= 448 (any shape) -> nearest E4M3 codes, ties to the even
+    code (mantissa bit 0 clear), sign kept (including -0)."""
+    y = np.asarray(y, dtype=np.float64)
+    a = np.abs(y)
+    if np.any(a > E4M3_MAX) or np.any(np.isnan(a)):
+        raise ValueError("values must be finite with |y| <= 448")
+    hi = np.searchsorted(_POS_VALUES, a, side="left")   # first value >= a
+    hi = np.minimum(hi, len(_POS_VALUES) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALUES[lo]
+    d_hi = _POS_VALUES[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((_POS_CODES[hi] & 1) == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    return code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+
+
+def quantize_e4m3_per_token(x):
+    """x: [T, ...] float32 -> (codes uint8 [T, ...], scale float32 [T])."""
+    x = np.asarray(x, dtype=np.float32)
+    T = x.shape[0]
+    amax = np.abs(x.reshape(T, -1)).max(axis=1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    y = x / scale.reshape((T,) + (1,) * (x.ndim - 1))            # float32 division
+    y = np.clip(y, -E4M3_MAX, E4M3_MAX)
+    return encode_e4m3(y), scale

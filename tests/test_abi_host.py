@@ -151,3 +151,17 @@ def test_layer_schedule_errors(args):
     out = (ctypes.c_int32 * 8)()
     assert lib.dsa_layer_schedule(*args, out) == -1
     assert lib.dsa_layer_schedule(3, 4, 0, None, None) == -1
+
+
+@host_only
+@pytest.mark.parametrize("args,st", [
+    ((0x1000, 5, 4, 128, 128, 0x2000, 128, 0x3000, 1), -2),     # dtype
+    ((0x1000, 0, 4, 126, 128, 0x2000, 128, 0x3000, 1), -3),     # row_elems not a multiple of 4
+    ((0x1000, 0, 4, 128, 64, 0x2000, 128, 0x3000, 1), -3),      # row stride < row_elems
+    ((0x1004, 0, 4, 128, 128, 0x2000, 128, 0x3000, 1), -4),     # fp32 x not 16-byte aligned
+    ((0x1000, 0, 4, 128, 128, 0x2001, 128, 0x3000, 1), -4),     # codes not 4-byte aligned
+    ((None, 0, 4, 128, 128, 0x2000, 128, 0x3000, 1), -1),
+])
+def test_quantize_argument_errors(args, st):
+    lib = dsa.load_library()
+    assert lib.dsa_quantize_e4m3(*args, None) == st

@@ -325,3 +325,72 @@ def test_layer_stack_follows_the_schedule():
     assert ok, msg
     out6 = dsa.sparse_attn(layers[6], idx3, out_dtype=torch.float32)
     _attn_check(layers[6], idx3.cpu().numpy(), out6, None, rows)
+
+
+# ---------------------------------------------------------------------------
+# per-token E4M3 quantization (the step before the path): bit-exact
+# ---------------------------------------------------------------------------
+
+def _quant_inputs(dtype, T=37, H=64, D=128, seed=8):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(T, H, D, generator=g)
+    x[3] = 0.0                                    # all-zero token: scale 1, codes 0
+    x[5] *= 1e-6                                  # subnormal codes
+    x[7] *= 3e4
+    x[9, 0, :5] = torch.tensor([-0.0, 1.0, -1.0, 0.0, 2.0])
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_e4m3_bit_exact(dtype):
+    x = _quant_inputs(dtype)
+    codes, scales = dsa.quantize_e4m3(x.to(DEV))
+    ref_c, ref_s = oracle.quantize_e4m3_per_token(x.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    # the input generator's route (torch's cast) gives the same bytes
+    syn_c, syn_s = synth.encode_e4m3_per_token(x.float())
+    assert torch.equal(codes.cpu(), syn_c) and torch.equal(scales.cpu(), syn_s)
+
+
+def test_quantize_appends_to_cache_slot():
+    B, Lmax, D, p = 5, 96, 128, 41
+    cache = torch.full((B, Lmax, D), 0x5A, dtype=torch.uint8, device=DEV)
+    sc_cache = torch.full((B, Lmax), -1.0, dtype=torch.float32, device=DEV)
+    new = torch.randn(B, D, device=DEV, dtype=torch.float32)
+    dsa.quantize_e4m3(new, codes=cache[:, p], scales=sc_cache[:, p])
+    ref_c, ref_s = oracle.quantize_e4m3_per_token(new.cpu().numpy())
+    assert np.array_equal(cache[:, p].cpu().numpy(), ref_c)
+    assert np.array_equal(sc_cache[:, p].cpu().numpy(), ref_s)
+    others = torch.ones(Lmax, dtype=torch.bool)
+    others[p] = False
+    assert torch.all(cache[:, others] == 0x5A) and torch.all(sc_cache[:, others] == -1.0)
+
+
+def test_cache_filled_by_quantize_gives_the_indexer_its_operands():
+    # prefill writes 700 k^I rows into a 1024-slot cache, three decode steps append one
+    # row each; the indexer then reads the cache prefix.  The bytes must equal the input
+    # generator's encoding of the same floats, so the selected idx match too.
+    cfg = _cfg("fp8", 703, 64)
+    Lmax, L0, Lk = 1024, 700, 703
+    g = torch.Generator().manual_seed(9)
+    kf = torch.randn(Lk, cfg.d_I, generator=g)
+    qf = torch.randn(1, cfg.H_I, cfg.d_I, generator=g)
+    w = (torch.rand(1, 1, cfg.H_I, generator=g) / cfg.H_I).to(DEV)
+    cache = torch.zeros((1, Lmax, cfg.d_I), dtype=torch.uint8, device=DEV)
+    sc_cache = torch.zeros((1, Lmax), dtype=torch.float32, device=DEV)
+    dsa.quantize_e4m3(kf[:L0].to(DEV), codes=cache[0, :L0], scales=sc_cache[0, :L0])
+    for p in range(L0, Lk):
+        dsa.quantize_e4m3(kf[p:p + 1].to(DEV), codes=cache[:, p], scales=sc_cache[:, p])
+    qc, qs = dsa.quantize_e4m3(qf.to(DEV))
+    kc_ref, ks_ref = synth.encode_e4m3_per_token(kf)
+    qc_ref, qs_ref = synth.encode_e4m3_per_token(qf)
+    assert torch.equal(cache[0, :Lk].cpu(), kc_ref) and torch.equal(sc_cache[0, :Lk].cpu(), ks_ref)
+    assert torch.equal(qc.cpu(), qc_ref) and torch.equal(qs.cpu(), qs_ref)
+    idx = dsa.indexer_topk(qc.reshape(1, 1, cfg.H_I, cfg.d_I), cache[:, :Lk], w, 64,
+                           q_scale=qs.reshape(1, 1), k_scale=sc_cache[:, :Lk])
+    idx_ref = dsa.indexer_topk(qc_ref.to(DEV).reshape(1, 1, cfg.H_I, cfg.d_I),
+                               kc_ref.to(DEV).reshape(1, Lk, cfg.d_I), w, 64,
+                               q_scale=qs_ref.to(DEV).reshape(1, 1),
+                               k_scale=ks_ref.to(DEV).reshape(1, Lk))
+    assert torch.equal(idx, idx_ref)

@@ -51,3 +51,55 @@ def test_bf16_hand_values_and_library():
     bits = bits[(bits & 0x7F80) != 0x7F80]          # finite patterns only
     lib = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(lib, decode_bf16(bits))
+
+
+# ---------------------------------------------------------------------------
+# encoder pins
+# ---------------------------------------------------------------------------
+
+def test_e4m3_encode_matches_library_cast():
+    # torch's float32 -> float8_e4m3fn cast rounds to nearest even: an independent encoder
+    from oracle import encode_e4m3
+    rng = np.random.default_rng(5)
+    y = np.concatenate([rng.uniform(-448, 448, 200000), rng.uniform(-0.02, 0.02, 100000),
+                        rng.normal(0, 3, 100000)]).astype(np.float32)
+    y = np.clip(y, -448, 448)
+    lib = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(encode_e4m3(y), lib)
+
+
+def test_e4m3_encode_ties_and_round_trip():
+    from oracle import encode_e4m3
+    # every representable value encodes to its own code
+    codes = np.arange(0x7F, dtype=np.uint8)
+    assert np.array_equal(encode_e4m3(decode_e4m3(codes)), codes)
+    # midpoints go to the even code: 1.0625 lies between 1.0 (0x38) and 1.125 (0x39)
+    assert encode_e4m3(np.float64(1.0625)) == 0x38
+    assert encode_e4m3(np.float64(1.1875)) == 0x3A          # between 1.125 (0x39) and 1.25 (0x3A)
+    assert encode_e4m3(np.float64(2.0 ** -10)) == 0x00      # half the smallest subnormal: to 0
+    assert encode_e4m3(np.float64(3 * 2.0 ** -10)) == 0x02  # 1.5 steps: to 2 (even)
+    assert encode_e4m3(np.float64(-0.0)) == 0x80
+    with pytest.raises(ValueError):
+        encode_e4m3(np.float64(449.0))
+
+
+def test_per_token_quantization_definition():
+    from oracle import quantize_e4m3_per_token
+    rng = np.random.default_rng(6)
+    x = rng.normal(0, 1, (6, 3, 16)).astype(np.float32)
+    x[2] = 0.0                                               # an all-zero token
+    x[4] *= 2.0 ** 40                                        # scaling by 2^j is exact
+    codes, scale = quantize_e4m3_per_token(x)
+    assert scale[2] == 1.0 and np.all(codes[2] == 0)
+    for t in (0, 1, 3, 4, 5):
+        amax = np.abs(x[t]).max()
+        assert scale[t] == np.float32(amax) / np.float32(448.0)
+        # the largest element maps to +-448 exactly
+        i = np.unravel_index(np.abs(x[t]).argmax(), x[t].shape)
+        assert abs(decode_e4m3(codes[t][i])) == 448.0
+    c4, s4 = quantize_e4m3_per_token(x[4:5] / np.float32(2.0 ** 40))
+    assert np.array_equal(c4[0], codes[4]) and s4[0] * np.float32(2.0 ** 40) == scale[4]
+    # dequantized values are within half an E4M3 step of x
+    deq = decode_e4m3(codes) * scale[:, None, None]
+    step = np.maximum(np.abs(deq), 2.0 ** -6 * scale[:, None, None]) * 2.0 ** -3
+    assert np.all(np.abs(deq - x) <= 0.5 * step * (1 + 1e-6))
