@@ -353,16 +353,35 @@ void mla_attn_kernel(MlaParams P) {
 constexpr int kBlk2 = 32;                        // keys per block
 constexpr int kBlk2Bytes = 2 * kBlkBytes;        // 36864
 constexpr int kDmaPerBlk2 = kBlk2Bytes / 1024;   // 36 wave-wide 1 KB direct-to-LDS loads
-constexpr int kKeyBufs2 = 4;                     // idx ring slots (j .. j+2 in use)
 
-template <bool SPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+// s_waitcnt vmcnt(m) for the largest m <= n in [0, C] (n is wave-uniform); waiting for
+// fewer outstanding loads than n is always safe.
+template <int C>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if constexpr (C == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= C) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C) : "memory");
+    else wait_vm_at_most<C - 1>(n);
+  }
+}
+
+// NB = latent row buffers: block j is computed from buffer j % NB while the rows of
+// blocks j+1 .. j+NB-1 are in flight.  NB = 2 leaves room for two workgroups per CU (the
+// prefill grids); NB = 4 takes most of the LDS for one workgroup per CU with three blocks
+// (108 KB) in flight, for the few long-latency workgroups of decode.  The idx ring runs
+// 2 NB - 2 blocks ahead, so a block's entries have landed before its rows are requested.
+template <bool SPLIT, int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 2 : 1)))
 void mla_attn32_kernel(MlaParams P) {
   constexpr int NW = 4;
   constexpr int kDt = 16;                        // 16-dim output tiles per wave (256 dims)
   constexpr int kQSteps = 18;                    // 32-dim QK steps over the 576 latent dims
   constexpr int kSlots = kDmaPerBlk2 / NW;       // 9 loads per wave per block
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[2][kBlk2Bytes];
+  constexpr int kKeyAhead = 2 * NB - 2;          // idx blocks requested ahead of compute
+  constexpr int kKeyBufs2 = NB == 2 ? 4 : 8;     // ring slots (j .. j + kKeyAhead in use)
+  static_assert((NB & (NB - 1)) == 0 && kKeyBufs2 > kKeyAhead, "ring sizes");
+  __shared__ __attribute__((aligned(16))) uint8_t kvs[NB][kBlk2Bytes];
   __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs2][kBlk2];
   __shared__ __attribute__((aligned(16))) float xm[NW][64];     // block maxima, then l
   __shared__ __attribute__((aligned(16))) i32x4 xp[NW][64];     // packed (hi, lo) p
@@ -431,8 +450,7 @@ void mla_attn32_kernel(MlaParams P) {
   using C6 = Phase<6>;
   using C9 = Phase<kSlots>;
 
-  if (nb > 0) issue_keys(0);
-  if (nb > 1) issue_keys(1);
+  for (int t = 0; t < kKeyAhead && t < nb; ++t) issue_keys(t);
   // Q^T operand over all 576 dims: head h, dims [32 ks + 8 g, +8)
   const int h = ht * 16 + r16;
   bf16x8 qop[kQSteps];
@@ -462,17 +480,34 @@ void mla_attn32_kernel(MlaParams P) {
   __builtin_amdgcn_s_waitcnt(0);                 // operands and the first idx entries
   if (nb > 0) {
     __syncthreads();
-    issue_rows(0, 0, C0{}, C9{});
+#pragma unroll
+    for (int t = 0; t < NB - 1; ++t)
+      if (t < nb) issue_rows(t, t, C0{}, C9{});
   }
 
   for (int j = 0; j < nb; ++j) {
-    const int buf = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of j, idx of j+1
-    __syncthreads();                                     // B1: landed for all; other buffer free
+    const int buf = j & (NB - 1);
+    const int nbuf = (j + NB - 1) & (NB - 1);
+    if constexpr (NB == 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of j, idx of j+2 and before
+    } else {
+      // loads this wave issued after the rows of block j: those of the iterations
+      // t = j-NB+2 .. j-1 (idx of block t + kKeyAhead, rows of block t + NB - 1; the
+      // prologue issued rows only)
+      int after = 0;
+#pragma unroll
+      for (int d = NB - 2; d >= 1; --d) {
+        const int t = j - d;
+        after += (t + NB - 1 < nb) ? kSlots : 0;
+        after += (t >= 0 && t + kKeyAhead < nb) ? 1 : 0;
+      }
+      wait_vm_at_most<(NB - 2) * (kSlots + 1)>(uniform(after));
+    }
+    __syncthreads();                                     // B1: landed for all; buffer of j-1 free
     // the next block's rows go out in three parts spread over the block (every wave of
     // the CU would otherwise queue all of its loads at the same moment)
-    if (j + 2 < nb) issue_keys(j + 2);
-    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C0{}, C3{});
+    if (j + kKeyAhead < nb) issue_keys(j + kKeyAhead);
+    if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C0{}, C3{});
     const uint8_t* kb = kvs[buf];
     float sv[4];
     float own_max = -INFINITY;
@@ -513,7 +548,7 @@ void mla_attn32_kernel(MlaParams P) {
       own_max = wave_max16x4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
       xm[wv_id][lane] = own_max;
     }
-    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C3{}, C6{});
+    if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C3{}, C6{});
     __syncthreads();                                     // B2: block maxima exchanged
     if (wave_active) {
       // both waves of the pair see the same two maxima, so they raise m_use identically
@@ -538,7 +573,7 @@ void mla_attn32_kernel(MlaParams P) {
       const uint32_t l23 = pack_bf16x2(pj[2] - __uint_as_float(h23 << 16), pj[3] - __uint_as_float(h23 & 0xffff0000u));
       xp[wv_id][lane] = i32x4{(int)h01, (int)h23, (int)l01, (int)l23};
     }
-    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1, C6{}, C9{});
+    if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C6{}, C9{});
     __syncthreads();                                     // B3: probabilities exchanged
     if (wave_active) {
       const i32x4 mine = xp[wv_id][lane], other = xp[partner][lane];
@@ -710,6 +745,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 struct MlaPlan {
   int nq, dvs, nw, n_groups, n_split, bps;
   bool k32;           // mla_attn32_kernel (32-key blocks, one query per workgroup)
+  bool deep;          // its four-buffer form: one workgroup per CU, three blocks in flight
   size_t off_o, off_ml, total;
 };
 
@@ -727,8 +763,12 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   p.n_groups = B * (Lq / p.nq);
   const int n_blk = (k + (p.k32 ? kBlk2 : kBlk) - 1) / (p.k32 ? kBlk2 : kBlk);
   int split = 1;
-  if (p.n_groups < 1024) {       // split the keys to fill the GPU (decode)
-    split = (1024 + p.n_groups - 1) / p.n_groups;
+  // few query rows (decode): one deep workgroup per CU, the keys split to reach ~256 of
+  // them; otherwise split to reach ~1024 two-buffer workgroups
+  p.deep = p.k32 && p.n_groups <= 256;
+  const int target = p.deep ? 256 : 1024;
+  if (p.n_groups < target) {
+    split = (target + p.n_groups - 1) / p.n_groups;
     if (split > kMaxSplit) split = kMaxSplit;
     if (split > n_blk) split = n_blk;
   }
@@ -769,9 +809,12 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   P.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_ml);
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
-  if (pl.k32) {
-    if (split) mla_attn32_kernel<true><<<grid, 256, 0, s>>>(P);
-    else mla_attn32_kernel<false><<<grid, 256, 0, s>>>(P);
+  if (pl.k32 && pl.deep) {
+    if (split) mla_attn32_kernel<true, 4><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 4><<<grid, 256, 0, s>>>(P);
+  } else if (pl.k32) {
+    if (split) mla_attn32_kernel<true, 2><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 2><<<grid, 256, 0, s>>>(P);
   } else if (pl.nw <= 4) {
     if (split) mla_attn_kernel<4, 2, 3, true, 2><<<grid, 256, 0, s>>>(P);
     else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);

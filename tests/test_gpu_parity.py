@@ -254,6 +254,37 @@ def test_mla_decode_split_and_mtp_shared_rows():
                     idx_rows_override=np.repeat(shared[b][None], 4, axis=0))
 
 
+# Few query rows take the four-buffer attention (one workgroup per CU, three blocks of 32
+# keys in flight, keys split to reach ~256 workgroups).  Cases: splits of one and two
+# blocks (fewer than the ring holds), a ragged last block, an unsplit 256-row grid, and
+# -1 / out-of-range entries.
+@pytest.mark.parametrize("B,Lq,Lk,k,seed", [
+    (1, 1, 3000, 2048, 0),      # 8 splits of 8 blocks
+    (2, 1, 500, 100, 1),        # 4 blocks, ragged: one block per split
+    (2, 1, 900, 520, 2),        # 17 blocks: splits of 3, the last of 2
+    (5, 2, 2000, 1000, 3),      # 10 rows, 32 blocks (last ragged), splits of 4
+    (4, 1, 2100, 2047, 4),      # ragged 2047
+    (1, 256, 400, 300, 5),      # 256 rows: no split, 10 blocks per workgroup
+])
+def test_mla_deep_ring_edge_cases(B, Lq, Lk, k, seed):
+    cfg = synth.get_config("decode200k", L=Lk, B=B)
+    lay = synth.attention_inputs(cfg, layer=1, device=DEV, Lq=Lq)
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.sort(rng.permutation(Lk)[:k]) for _ in range(B * Lq)]).reshape(B, Lq, k).astype(np.int32)
+    idx[0, 0, ::7] = -1                      # holes
+    idx[-1, -1, 3::5] = Lk + 11              # out of range: skipped
+    if k > 64:
+        idx[0, -1, k - 40:] = -1             # padded tail
+    out, lse = dsa.sparse_attn(lay, torch.from_numpy(idx).to(DEV), return_lse=True, out_dtype=torch.float32)
+    ol_idx = idx.copy()
+    ol_idx[ol_idx >= Lk] = -1
+    for b in range(B):
+        rows = sorted({0, Lq - 1, Lq // 2})
+        _attn_check(lay, ol_idx, out, lse, rows, b=b)
+    out_bf = dsa.sparse_attn(lay, torch.from_numpy(idx).to(DEV))
+    assert torch.equal(out_bf, out.to(torch.bfloat16))
+
+
 def test_tiny_mha_fp32_attention_parity():
     cfg = synth.get_config("tiny")
     ind = synth.indexer_inputs(cfg, device=DEV)
