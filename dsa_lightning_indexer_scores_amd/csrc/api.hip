@@ -112,9 +112,10 @@ size_t materialised_scores_bytes(int B, int Lq, int Lk) { return round_up((size_
 size_t materialised_hist_bytes(int B, int Lq) { return round_up((size_t)B * Lq * dsa::kRowHistBins * sizeof(uint32_t)); }
 
 size_t indexer_topk_ws(int dtype, int B, int Lq, int Lk, int k) {
-  if (use_materialised(dtype, Lq))
+  if (dtype == DSA_F32)
     return materialised_scores_bytes(B, Lq, Lk) + materialised_hist_bytes(B, Lq) +
            round_up(dsa::topk_split_ws(B * Lq, Lk, false));
+  if (use_materialised(dtype, Lq)) return round_up(dsa::chunk_lists_ws(B * Lq, Lk));
   return dsa::indexer_topk_fused_ws(B, Lq, Lk, k, dtype);
 }
 
@@ -128,7 +129,10 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
                      size_t ws_bytes, hipStream_t s) {
   const dsa::IndexerArgs a = make_indexer_args(in, B, Lq, Lk);
   hipError_t e;
-  if (use_materialised(in->dtype, Lq)) {
+  if (in->dtype != DSA_F32 && use_materialised(in->dtype, Lq)) {
+    // few queries (decode): chunk candidate lists, no score rows
+    e = dsa::launch_indexer_topk_lists(a, k, idx, ws, ws_bytes, s);
+  } else if (use_materialised(in->dtype, Lq)) {
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     float* scores = reinterpret_cast<float*>(w8);
     const size_t off_hist = materialised_scores_bytes(B, Lq, Lk);

@@ -36,6 +36,26 @@ size_t indexer_topk_fused_ws(int B, int Lq, int Lk, int k, int dtype);
 hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, void* ws,
                                      size_t ws_bytes, hipStream_t s);
 
+// --- few query rows (decode): chunk candidate lists, then the row top-k -------
+// Every (row, chunk) workgroup keeps its chunk's scores in LDS and writes, in position
+// order, the entries whose top-11-bit digit is at least the chunk's own k-th digit.  The
+// row's k-th key is never below any chunk's, so the lists hold every entry of the row's
+// top-k; the finishing kernel filters them by the row's digit and selects exactly.
+struct ChunkLists {
+  int chunk;            // keys per chunk (multiple of 64)
+  int n_chunks;         // chunks per row
+  int64_t row_stride;   // list slots per row (>= n_chunks * chunk); chunk c at c * chunk
+  uint32_t* keys;       // [rows][row_stride] order keys
+  uint32_t* pos;        // [rows][row_stride] positions
+  uint32_t* cnt;        // [rows][n_chunks] entries per list
+  uint32_t* row_hist;   // [rows][2048] top-11-bit histogram of the causal scores
+};
+size_t chunk_lists_ws(int rows, int Lk);
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                                     hipStream_t s);
+hipError_t launch_topk_lists_finish(const ChunkLists& L, int rows, int causal_Lq, int causal_Lk, int k,
+                                    int32_t* idx, hipStream_t s);
+
 // --- top-k over materialised rows -------------------------------------------
 // With scratch of at least topk_split_ws(rows, n, row_hist == nullptr) bytes, few long
 // rows are split over several workgroups; otherwise one workgroup handles a row.

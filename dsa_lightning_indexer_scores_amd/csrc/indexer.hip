@@ -217,45 +217,288 @@ __global__ __launch_bounds__(256) void indexer_rowscan_kernel(IndexerArgs a, flo
     for (int j = threadIdx.x; j < kRowHistBins; j += 256) lhist[j] = 0;
     __syncthreads();
   }
-  // software pipeline: the next tile's key operands are loaded before this tile is scored
-  auto load_tile = [&](int s0, Op<DT> (&Bk)[4]) {
+  const int s_first = s_begin + wv_id * kTileKeys;
+  const int s_causal_end = min(s_end, p + 1);      // keys past this are -inf for this query
+  constexpr int kStride = 4 * kTileKeys;           // the four waves interleave tiles
+  // Key rows are clamped into [s_begin, last]: loads of tiles past the causal end or the
+  // chunk re-read the last row (an L2 hit) instead of being skipped, so every step issues
+  // the same loads and the wait counts stay exact.
+  const int last = max(s_begin, s_causal_end - 1);
+  const int n_tiles = s_first < s_end ? (s_end - s_first + kStride - 1) / kStride : 0;
+  auto load_tile = [&](int t, Op<DT> (&Bk)[4], float& kscale) {
+    const int s0 = s_first + t * kStride;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int key = min(s0 + kb * 16 + (lane & 15), a.Lk - 1);
+      const int key = min(s0 + kb * 16 + (lane & 15), last);
       Bk[kb] = load_op<DT>(kbase + (size_t)key * RB, g);
     }
+    if (DT == DSA_FP8_E4M3) kscale = ksc[min(s0 + lane, last)];
   };
-  const int s_first = s_begin + wv_id * kTileKeys;
-  const int s_causal_end = min(s_end, p + 1);      // tiles starting here are all -inf
-  // two tiles in flight per wave: Bn (next) and Bn2 (the one after)
-  Op<DT> Bn[4], Bn2[4];
-  if (s_first < s_causal_end) load_tile(s_first, Bn);
-  if (s_first + 4 * kTileKeys < s_causal_end) load_tile(s_first + 4 * kTileKeys, Bn2);
-  for (int s0 = s_first; s0 < s_end; s0 += 4 * kTileKeys) {
-    const int s = s0 + lane;
-    if (s0 >= s_causal_end) {  // whole tile is non-causal for this query
-      if (s < s_end) out[s] = -INFINITY;
-      continue;
-    }
-    Op<DT> Bk[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      Bk[kb] = Bn[kb];
-      Bn[kb] = Bn2[kb];
-    }
-    if (s0 + 8 * kTileKeys < s_causal_end) load_tile(s0 + 8 * kTileKeys, Bn2);
+  // Two tiles in flight per wave, in three buffers that rotate by name (the loop is
+  // unrolled three ways): tile t is scored from buffer t % 3 while the loads of tiles t+1
+  // and t+2 are outstanding.  A rotation by register copies would make every iteration
+  // wait for the loads it had just issued.
+  Op<DT> B0[4], B1[4], B2[4];
+  float k0 = 1.f, k1 = 1.f, k2 = 1.f;
+  if (n_tiles > 0) {
+    load_tile(0, B0, k0);
+    load_tile(1, B1, k1);
+  }
+  // request tile t + 2 into Bl (whose previous tile is done), then score tile t from Bk
+  auto step = [&](int t, const Op<DT> (&Bk)[4], float kk, Op<DT> (&Bl)[4], float& kl) {
+    load_tile(t + 2, Bl, kl);
+    if (t >= n_tiles) return;                      // wave-uniform
+    const int s = s_first + t * kStride + lane;
     float val = tile_score<DT, HB>(A, Bk, W);
-    if (DT == DSA_FP8_E4M3) val *= ksc[min(s, a.Lk - 1)];
-    const bool causal = s <= p && s < s_end;
+    if (DT == DSA_FP8_E4M3) val *= kk;
+    const bool causal = s < s_causal_end;
     if (s < s_end) out[s] = causal ? val : -INFINITY;
     if (row_hist && causal) atomicAdd(&lhist[order_key(val) >> 21], 1u);
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, B0, k0, B2, k2);
+    step(t + 1, B1, k1, B0, k0);
+    step(t + 2, B2, k2, B1, k1);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last prefetches (unused)
   if (row_hist) {
     __syncthreads();
     uint32_t* rh = row_hist + (size_t)qrow * kRowHistBins;
     for (int j = threadIdx.x; j < kRowHistBins; j += 256)
       if (lhist[j]) atomicAdd(&rh[j], lhist[j]);
   }
+}
+
+// ---------------------------------------------------------------------------
+// Few query rows (decode): one workgroup per (query row, chunk of keys) scores the chunk
+// exactly as indexer_rowscan_kernel (same tile_score, so the same bits), but keeps the
+// scores in LDS.  At the end it adds its top-11-bit histogram to the row's, finds the
+// digit dc of its own k-th largest key (count(digit > dc) < k <= count(digit >= dc); 0
+// when the chunk has at most k causal keys) and writes the entries with digit >= dc, in
+// position order, to its list.  The row's k-th key is at least every chunk's k-th key,
+// so the row's top-k entries all reach the lists, and only about k entries per chunk are
+// written instead of the whole score row.
+// ---------------------------------------------------------------------------
+constexpr int kSelMaxChunk = 16384;   // keys per chunk: their scores fill 64 KB of LDS
+
+// Digit of the krem-th largest entry of a 2048-bin LDS histogram, for 256 threads (8
+// bins each); the caller guarantees that the histogram holds at least krem entries.
+__device__ uint32_t block_digit256(const uint32_t* hist, uint32_t krem, uint32_t* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  uint32_t h[8], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    h[j] = hist[8 * tid + j];
+    tot += h[j];
+  }
+  // entries in the bins of higher threads: suffix sum over threads
+  uint32_t incl = tot;   // inclusive suffix within the wave (lanes >= this one)
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_down(incl, d);
+    if (lane + d < 64) incl += o;
+  }
+  if (lane == 0) sh[w] = incl;   // wave total
+  __syncthreads();
+  uint32_t above = incl - tot;
+  for (int i = w + 1; i < 4; ++i) above += sh[i];
+  if (above < krem && above + tot >= krem) {
+    uint32_t c = above;
+    int dd = 8 * tid;
+    for (int j = 7; j >= 0; --j) {
+      if (c + h[j] >= krem) { dd = 8 * tid + j; break; }
+      c += h[j];
+    }
+    sh[4] = (uint32_t)dd;
+  }
+  __syncthreads();
+  const uint32_t d = sh[4];
+  __syncthreads();
+  return d;
+}
+
+template <int DT, int HB>
+__global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, int k, ChunkLists L) {
+  __shared__ float lsc[kSelMaxChunk];
+  __shared__ uint32_t lhist[kRowHistBins];
+  __shared__ uint32_t sh[16];
+  constexpr int RB = IdxTraits<DT>::kRowBytes;
+  const int qrow = blockIdx.x / L.n_chunks;
+  const int chunk = blockIdx.x - qrow * L.n_chunks;
+  const int b = qrow / a.Lq, i = qrow - b * a.Lq;
+  const int p = a.Lk - a.Lq + i;
+  const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6, g = lane >> 4;
+  const int s_begin = chunk * L.chunk;
+  const int s_end = min(a.Lk, s_begin + L.chunk);
+
+  const uint8_t* qptr = reinterpret_cast<const uint8_t*>(a.q) + (size_t)qrow * a.H_I * RB;
+  Op<DT> A[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) A[hb] = load_op<DT>(qptr + (size_t)(hb * 16 + (lane & 15)) * RB, g);
+  const float qs = (DT == DSA_FP8_E4M3) ? a.q_scale[qrow] : 1.f;
+  f32x4 W[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) W[hb][ii] = a.w[(size_t)qrow * a.H_I + hb * 16 + 4 * g + ii] * qs;
+
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * RB;
+  const float* ksc = (DT == DSA_FP8_E4M3) ? a.k_scale + (size_t)b * a.Lk : nullptr;
+  for (int j = tid; j < kRowHistBins; j += 256) lhist[j] = 0;
+  __syncthreads();
+
+  const int s_first = s_begin + wv_id * kTileKeys;
+  const int s_causal_end = min(s_end, p + 1);      // keys past this are not candidates
+  constexpr int kStride = 4 * kTileKeys;           // the four waves interleave tiles
+  // key rows clamped into [s_begin, last] (see indexer_rowscan_kernel)
+  const int last = max(s_begin, s_causal_end - 1);
+  const int n_tiles = s_first < s_causal_end ? (s_causal_end - s_first + kStride - 1) / kStride : 0;
+  auto load_tile = [&](int t, Op<DT> (&Bk)[4], float& kscale) {
+    const int s0 = s_first + t * kStride;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(s0 + kb * 16 + (lane & 15), last);
+      Bk[kb] = load_op<DT>(kbase + (size_t)key * RB, g);
+    }
+    if (DT == DSA_FP8_E4M3) kscale = ksc[min(s0 + lane, last)];
+  };
+  // two tiles in flight in three buffers rotating by name (see indexer_rowscan_kernel)
+  Op<DT> B0[4], B1[4], B2[4];
+  float k0 = 1.f, k1 = 1.f, k2 = 1.f;
+  if (n_tiles > 0) {
+    load_tile(0, B0, k0);
+    load_tile(1, B1, k1);
+  }
+  auto step = [&](int t, const Op<DT> (&Bk)[4], float kk, Op<DT> (&Bl)[4], float& kl) {
+    load_tile(t + 2, Bl, kl);
+    if (t >= n_tiles) return;                      // wave-uniform
+    const int s = s_first + t * kStride + lane;
+    float val = tile_score<DT, HB>(A, Bk, W);
+    if (DT == DSA_FP8_E4M3) val *= kk;
+    if (s < s_causal_end) {
+      lsc[s - s_begin] = val;
+      atomicAdd(&lhist[order_key(val) >> 21], 1u);
+    }
+  };
+  for (int t = 0; t < n_tiles; t += 3) {
+    step(t, B0, k0, B2, k2);
+    step(t + 1, B1, k1, B0, k0);
+    step(t + 2, B2, k2, B1, k1);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the last prefetches (unused)
+  __syncthreads();
+
+  uint32_t* rh = L.row_hist + (size_t)qrow * kRowHistBins;
+  for (int j = tid; j < kRowHistBins; j += 256)
+    if (lhist[j]) atomicAdd(&rh[j], lhist[j]);
+  const int n_c = max(0, s_causal_end - s_begin);
+  const uint32_t dc = n_c > k ? block_digit256(lhist, (uint32_t)k, sh) : 0u;
+
+  // ordered compaction of the entries with digit >= dc: 1024 entries per round, one
+  // ballot per 256 (entry e0 + 256 u + tid), prefix over (u, wave) in LDS
+  const size_t slot = (size_t)qrow * L.row_stride + (size_t)chunk * L.chunk;
+  uint32_t* ok = L.keys + slot;
+  uint32_t* op = L.pos + slot;
+  uint32_t base = 0;
+  for (int e0 = 0; e0 < n_c; e0 += 1024) {
+    uint32_t key[4];
+    uint64_t m[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = e0 + 256 * u + tid;
+      key[u] = e < n_c ? order_key(lsc[e]) : 0u;
+      m[u] = ballot(e < n_c && (key[u] >> 21) >= dc);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sh[4 * u + wv_id] = (uint32_t)popc64(m[u]);
+    }
+    __syncthreads();
+    uint32_t before[4], run = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        if (ww == wv_id) before[u] = run;
+        run += sh[4 * u + ww];
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if ((m[u] >> lane) & 1ull) {
+        const uint32_t o = base + before[u] + rank_below(m[u]);
+        ok[o] = key[u];
+        op[o] = (uint32_t)(s_begin + e0 + 256 * u + tid);
+      }
+    }
+    base += run;
+    __syncthreads();
+  }
+  if (tid == 0) L.cnt[(size_t)qrow * L.n_chunks + chunk] = base;
+}
+
+// After every chunk of a row is scored: one workgroup per (chunk, row) finds the row's
+// k-th digit d1 from its histogram (the same rule as the row selection) and compacts the
+// chunk's list in place to its entries of digit >= d1, keeping their order (an entry
+// only moves to a lower slot, and a batch is read before any of it is written).
+__global__ __launch_bounds__(256) void lists_filter_kernel(ChunkLists L, int causal_Lq, int causal_Lk, int k) {
+  __shared__ __attribute__((aligned(16))) uint32_t hist[kRowHistBins];
+  __shared__ uint32_t sh[8 * 4];
+  const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nv = causal_Lk - causal_Lq + (row % causal_Lq) + 1;
+  if (nv <= k) return;                                  // short rows need no lists
+  const i32x4* rh = reinterpret_cast<const i32x4*>(L.row_hist + (size_t)row * kRowHistBins);
+  const i32x4 h0 = rh[2 * tid], h1 = rh[2 * tid + 1];
+  reinterpret_cast<i32x4*>(hist)[2 * tid] = h0;
+  reinterpret_cast<i32x4*>(hist)[2 * tid + 1] = h1;
+  __syncthreads();
+  const uint32_t d1 = block_digit256(hist, (uint32_t)k, sh);
+  uint32_t* cnt = L.cnt + (size_t)row * L.n_chunks + c;
+  const uint32_t m = *cnt;
+  const size_t base = (size_t)row * L.row_stride + (size_t)c * L.chunk;
+  uint32_t* keys = L.keys + base;
+  uint32_t* pos = L.pos + base;
+  constexpr int kU = 8;
+  uint32_t out_n = 0;
+  for (uint32_t j0 = 0; j0 < m; j0 += kU * 256) {
+    uint32_t key[kU], ps[kU];
+    uint64_t msk[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t j = j0 + 256 * u + tid;
+      key[u] = j < m ? keys[j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const uint32_t j = j0 + 256 * u + tid;
+      const bool take = j < m && (key[u] >> 21) >= d1;
+      ps[u] = take ? pos[j] : 0u;
+      msk[u] = ballot(take);
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < kU; ++u) sh[4 * u + w] = (uint32_t)popc64(msk[u]);
+    }
+    __syncthreads();                                   // the whole batch has been read
+    uint32_t before[kU], run = 0;
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) {
+        if (ww == w) before[u] = run;
+        run += sh[4 * u + ww];
+      }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      if ((msk[u] >> lane) & 1ull) {
+        const uint32_t o = out_n + before[u] + rank_below(msk[u]);
+        keys[o] = key[u];
+        pos[o] = ps[u];
+      }
+    }
+    out_n += run;
+    __syncthreads();                                   // sh reused by the next batch
+  }
+  if (tid == 0) *cnt = out_n;
 }
 
 // Reference-size fp32 path: one thread per (query, key); q row and weights in LDS.
@@ -794,6 +1037,59 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, float* scores, int64_t st
   }
   if (a.dtype == DSA_BF16) return rowscan_dispatch<DSA_BF16>(a, scores, stride, row_hist, s);
   return rowscan_dispatch<DSA_FP8_E4M3>(a, scores, stride, row_hist, s);
+}
+
+static ChunkLists plan_lists(int rows, int Lk) {
+  ChunkLists L{};
+  L.chunk = min(rowscan_chunk(rows, Lk), kSelMaxChunk);
+  L.n_chunks = (Lk + L.chunk - 1) / L.chunk;
+  L.row_stride = ((int64_t)Lk + 63) / 64 * 64 + kSelMaxChunk;
+  return L;
+}
+
+// Device-independent bound: n_chunks * chunk < Lk + kSelMaxChunk <= row_stride, and a
+// chunk has at least 64 keys.
+size_t chunk_lists_ws(int rows, int Lk) {
+  const size_t stride = ((size_t)Lk + 63) / 64 * 64 + kSelMaxChunk;
+  const size_t lists = ((size_t)rows * stride * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+  const size_t cnt = ((size_t)rows * ((Lk + 63) / 64) * sizeof(uint32_t) + 255) / 256 * 256;
+  const size_t hist = (size_t)rows * kRowHistBins * sizeof(uint32_t);
+  return lists + cnt + hist;
+}
+
+template <int DT>
+static void chunksel_dispatch(const IndexerArgs& a, int k, const ChunkLists& L, int rows, hipStream_t s) {
+  const dim3 grid((unsigned)(rows * L.n_chunks));
+  switch (a.H_I / 16) {
+    case 1: indexer_chunksel_kernel<DT, 1><<<grid, 256, 0, s>>>(a, k, L); break;
+    case 2: indexer_chunksel_kernel<DT, 2><<<grid, 256, 0, s>>>(a, k, L); break;
+    case 3: indexer_chunksel_kernel<DT, 3><<<grid, 256, 0, s>>>(a, k, L); break;
+    default: indexer_chunksel_kernel<DT, 4><<<grid, 256, 0, s>>>(a, k, L); break;
+  }
+}
+
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, int32_t* idx, void* ws, size_t ws_bytes,
+                                     hipStream_t s) {
+  const int rows = a.B * a.Lq;
+  if (ws_bytes < chunk_lists_ws(rows, a.Lk)) return hipErrorInvalidValue;
+  ChunkLists L = plan_lists(rows, a.Lk);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  const size_t lists = ((size_t)rows * L.row_stride * 2 * sizeof(uint32_t) + 255) / 256 * 256;
+  const size_t cnt = ((size_t)rows * ((a.Lk + 63) / 64) * sizeof(uint32_t) + 255) / 256 * 256;
+  L.keys = reinterpret_cast<uint32_t*>(w8);
+  L.pos = L.keys + (size_t)rows * L.row_stride;
+  L.cnt = reinterpret_cast<uint32_t*>(w8 + lists);
+  L.row_hist = reinterpret_cast<uint32_t*>(w8 + lists + cnt);
+  hipError_t e = launch_zero(L.row_hist, (size_t)rows * kRowHistBins * sizeof(uint32_t), s);
+  if (e != hipSuccess) return e;
+  if (a.dtype == DSA_BF16) chunksel_dispatch<DSA_BF16>(a, k, L, rows, s);
+  else chunksel_dispatch<DSA_FP8_E4M3>(a, k, L, rows, s);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  lists_filter_kernel<<<dim3(L.n_chunks, rows), 256, 0, s>>>(L, a.Lq, a.Lk, k);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_topk_lists_finish(L, rows, a.Lq, a.Lk, k, idx, s);
 }
 
 struct FusedPlan {

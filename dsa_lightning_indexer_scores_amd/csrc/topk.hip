@@ -375,6 +375,116 @@ __global__ __launch_bounds__(kTopBS) void topk_finish_kernel(const float* __rest
   select_emit_list(lkeys, lpos, min(nl, (uint32_t)kListCap), d1, a1, k, x, hist, sh, out, vout);
 }
 
+// Rows scored as chunk candidate lists (indexer_chunksel_kernel): the lists of a row,
+// concatenated in chunk order, are in position order and hold every entry of digit >= d1
+// (the row's k-th digit).  lists_filter_kernel drops their entries below d1;
+// topk_lists_finish_kernel then selects exactly in LDS, or, when the entries do not fit,
+// with the same rule over the lists in global memory (select_emit_lists_global).
+__device__ void select_emit_lists_global(const ChunkLists& L, int row, uint32_t d1, uint32_t a1, int k,
+                                         uint32_t* hist, uint32_t* sh, int32_t* out) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = d1 << 21, pmask = 0x7FFu << 21, krem = (uint32_t)k - a1, d, above;
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass == 0 ? 10 : 0;
+    const uint32_t dmask = pass == 0 ? 0x7FFu : 0x3FFu;
+    for (int j = tid; j < kTopBins; j += kTopBS) hist[j] = 0;
+    __syncthreads();
+    for (int c = 0; c < L.n_chunks; ++c) {
+      const uint32_t m = L.cnt[(size_t)row * L.n_chunks + c];
+      const uint32_t* kk = L.keys + (size_t)row * L.row_stride + (size_t)c * L.chunk;
+      for (uint32_t j = tid; j < m; j += kTopBS) {
+        const uint32_t key = kk[j];
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    block_find_digit(hist, kTopBins, krem, sh, d, above);
+    prefix |= d << shift;
+    pmask |= dmask << shift;
+    krem -= above;
+  }
+  const uint32_t theta = prefix, need_eq = krem;
+  uint32_t out_n = 0, eq_seen = 0;
+  for (int c = 0; c < L.n_chunks; ++c) {
+    const uint32_t m = L.cnt[(size_t)row * L.n_chunks + c];
+    const size_t base = (size_t)row * L.row_stride + (size_t)c * L.chunk;
+    for (uint32_t j0 = 0; j0 < m; j0 += kTopBS) {
+      const uint32_t j = j0 + tid;
+      const bool v = j < m;
+      const uint32_t key = v ? L.keys[base + j] : 0u;
+      const bool gt = v && key > theta, eq = v && key == theta;
+      uint32_t eq_tot;
+      const uint32_t eq_before = eq_seen + block_excl_scan(eq ? 1u : 0u, sh, eq_tot);
+      const bool take = gt || (eq && eq_before < need_eq);
+      uint32_t t_tot;
+      const uint32_t o = out_n + block_excl_scan(take ? 1u : 0u, sh, t_tot);
+      if (take) out[o] = (int32_t)L.pos[base + j];
+      out_n += t_tot;
+      eq_seen += eq_tot;
+    }
+  }
+}
+
+// One workgroup per row, after the filter: the lists hold exactly the row's entries of
+// digit >= d1 (a1 + h1 of them), in position order once concatenated by chunk.  They are
+// copied into LDS (flattened, chunk found from the offset table) and selected there;
+// when they do not fit, the selection runs over the lists in global memory.
+__global__ __launch_bounds__(kTopBS) void topk_lists_finish_kernel(ChunkLists L, int causal_Lq, int causal_Lk, int k,
+                                                                  int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kTopBins];
+  __shared__ uint32_t lkeys[kListCap];
+  __shared__ uint32_t lpos[kListCap];
+  __shared__ uint32_t offs[kTopBS + 1];
+  __shared__ uint32_t sh[kTopBS / 64 + 2];
+  const int row = blockIdx.x, tid = threadIdx.x;
+  const int nv = row_valid(row, causal_Lk, nullptr, causal_Lq, causal_Lk);
+  int32_t* out = idx + (size_t)row * k;
+  if (nv <= k) {
+    emit_short_row(nullptr, nv, k, out, nullptr);
+    return;
+  }
+  uint32_t d1, a1, h1;
+  row_top_digit(nullptr, nv, row, L.row_hist, k, hist, sh, d1, a1, h1);
+  if (a1 + h1 > (uint32_t)kListCap) {
+    select_emit_lists_global(L, row, d1, a1, k, hist, sh, out);
+    return;
+  }
+  // chunks in groups of kTopBS: offset table, then a flattened copy of the group's entries
+  uint32_t nl = 0;
+  for (int c0 = 0; c0 < L.n_chunks; c0 += kTopBS) {
+    const int nc = min(kTopBS, L.n_chunks - c0);
+    const uint32_t m = tid < nc ? L.cnt[(size_t)row * L.n_chunks + c0 + tid] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan(m, sh, tot);
+    if (tid < nc) offs[tid] = ex;
+    if (tid == 0) offs[nc] = tot;
+    __syncthreads();
+    for (uint32_t e = tid; e < tot; e += kTopBS) {
+      int lo = 0, hi = nc - 1;   // last chunk with offs[c] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (offs[mid] <= e) lo = mid;
+        else hi = mid - 1;
+      }
+      const uint32_t o = nl + e;
+      if (o < (uint32_t)kListCap) {   // holds: the lists hold a1 + h1 entries
+        const size_t src = (size_t)row * L.row_stride + (size_t)(c0 + lo) * L.chunk + (e - offs[lo]);
+        lkeys[o] = L.keys[src];
+        lpos[o] = L.pos[src];
+      }
+    }
+    nl += tot;
+    __syncthreads();
+  }
+  select_emit_list(lkeys, lpos, min(nl, (uint32_t)kListCap), d1, a1, k, nullptr, hist, sh, out, nullptr);
+}
+
+hipError_t launch_topk_lists_finish(const ChunkLists& L, int rows, int causal_Lq, int causal_Lk, int k,
+                                    int32_t* idx, hipStream_t s) {
+  topk_lists_finish_kernel<<<rows, kTopBS, 0, s>>>(L, causal_Lq, causal_Lk, k, idx);
+  return hipGetLastError();
+}
+
 // Top-11-bit key histogram of each row for the split path when the score kernel did not
 // provide one: each workgroup counts its range in LDS and adds the non-zero bins to the
 // row's global histogram (zeroed beforehand).

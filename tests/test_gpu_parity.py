@@ -139,6 +139,11 @@ FUSED_CASES = [
     ("bf16", 2, 333, 333, 64),         # ragged tail, batch
     ("fp8", 2, 64, 32768, 512),        # few queries, long keys: key segments + merge
     ("bf16", 1, 48, 20000, 1),         # k = 1
+    # fewer than 16 queries (decode): per-chunk candidate lists, then the row selection
+    ("fp8", 3, 1, 50000, 2048),
+    ("bf16", 2, 4, 9000, 512),
+    ("fp8", 2, 15, 3000, 2048),        # rows shorter and longer than k
+    ("fp8", 1, 1, 100, 64),            # one chunk
 ]
 
 
@@ -155,7 +160,7 @@ def test_fused_topk_equals_scores_then_topk(dtype, B, Lq, Lk, k):
     assert torch.equal(idx, idx2)                                     # run twice: identical
 
 
-@pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES[:5])
+@pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES[:5] + FUSED_CASES[6:7])
 def test_fused_topk_matches_oracle_sets(dtype, B, Lq, Lk, k):
     cfg = _cfg(dtype, Lk, k, Lq=Lq, B=B)
     ind = synth.indexer_inputs(cfg, device=DEV)
@@ -169,6 +174,37 @@ def test_fused_topk_matches_oracle_sets(dtype, B, Lq, Lk, k):
         ref = oracle.topk_rows(sc, nv, k)
         ok, nbad, msg = index_sets_agree(idx[b][rows], ref, sc, nv, k, TAU[dtype])
         assert ok, msg
+
+
+@pytest.mark.parametrize("Lq", [1, 3])
+def test_few_query_topk_heavy_ties_integer_exact(Lq):
+    """Integer-exact E4M3 inputs: every head's query is e_0, key s is v_s e_0 with v_s in
+    {1, 2}, w = 1/64, unit scales, so every score is exactly v_s.  Half the keys tie at
+    the top: the k-th digit's bin overflows the LDS list and the selection runs over the
+    chunk lists in global memory; ties go to the lower positions."""
+    B, Lk, k, H, D = 2, 40000, 2048, 64, 128
+    rng = np.random.default_rng(11)
+    q = np.zeros((B, Lq, H, D), np.uint8)
+    q[..., 0] = 0x38                                   # E4M3 1.0
+    kk = np.zeros((B, Lk, D), np.uint8)
+    kk[..., 0] = np.where(rng.random((B, Lk)) < 0.5, 0x40, 0x38)    # 2.0 or 1.0
+    ind = {"q": torch.from_numpy(q).to(DEV), "k": torch.from_numpy(kk).to(DEV),
+           "w": torch.full((B, Lq, H), 1.0 / 64, dtype=torch.float32, device=DEV),
+           "q_scale": torch.ones((B, Lq), dtype=torch.float32, device=DEV),
+           "k_scale": torch.ones((B, Lk), dtype=torch.float32, device=DEV), "dtype": "fp8", "H_I": H, "d_I": D}
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind))
+    nv = (torch.arange(Lq, device=DEV, dtype=torch.int32) + (Lk - Lq + 1)).repeat(B)
+    assert torch.equal(idx, dsa.topk(sc.reshape(B * Lq, Lk), k, n_valid=nv).reshape(B, Lq, k))
+    got = idx.cpu().numpy()
+    ora = indexer_to_oracle(ind)
+    for b in range(B):
+        rows = list(range(Lq))
+        osc = _oracle_rows(ora, b, rows, Lq, Lk)
+        assert set(np.unique(osc[np.isfinite(osc)])) <= {1.0, 2.0}
+        ref = oracle.topk_rows(osc, [Lk - Lq + r + 1 for r in rows], k)
+        assert np.array_equal(got[b], ref)
+        assert np.array_equal(got[b][0], np.flatnonzero(kk[b, :, 0] == 0x40)[:k])
 
 
 def test_rows_shorter_than_k_select_every_causal_key():
