@@ -9,10 +9,11 @@ Inputs are resident in HBM before the timed region starts.
 Also reported (same JSON line): decode at 64 x 200K (1 new token per sequence) step and
 per-token latency, the all-layers-Full comparator (every layer runs its own indexer),
 per-kernel HIP-event timings with their roofline fractions, an 80-layer stack run one call
-per layer under the FSSS, released (freq 4, offset 3) and all-Full schedules, and the CPU
-oracle timed on a bounded sample of query rows.
+per layer under the FSSS, released (freq 4, offset 3) and all-Full schedules, the per-token
+E4M3 quantization of the indexer operands (prefill q^I, decode k^I cache append), and the
+CPU oracle timed on a bounded sample of query rows.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-stack]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu] [--no-stack] [--no-quant]
 """
 import argparse
 import csv
@@ -40,7 +41,7 @@ TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_ker
                    "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
 PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
                '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
-               '--no-chunk1m --copy-calibration')
+               '--no-chunk1m --no-quant --copy-calibration')
 COPY_BYTES = 1 << 30
 
 
@@ -181,6 +182,7 @@ def parse():
     ap.add_argument("--no-allfull", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 80-layer stack at the prefill workload")
     ap.add_argument("--no-chunk1m", action="store_true")
+    ap.add_argument("--no-quant", action="store_true", help="skip the per-token E4M3 quantization measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -362,6 +364,9 @@ def main():
     if not args.no_chunk1m:
         result["chunk1m"] = bench_chunk1m(args, dsa, synth, accounting, torch, np, dev, stream)
 
+    if not args.no_quant:
+        result["quantize"] = bench_quantize(dsa, torch, np, dev, stream)
+
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg)
 
@@ -443,6 +448,46 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out
+
+
+def bench_quantize(dsa, torch, np, dev, stream):
+    """Per-token E4M3 quantization (the step before the path): the q^I of a 131072-token
+    prefill (64 heads x 128 dims, bf16 in, codes + per-token scales out; HBM-bound), and
+    one decode step's k^I append (64 sequences, one 128-dim row each, written straight
+    into their cache slots; launch-bound)."""
+    T, H, D = 131072, 64, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    x = torch.randn((T, H * D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    codes = torch.empty((T, H * D), dtype=torch.uint8, device=dev)
+    scales = torch.empty(T, dtype=torch.float32, device=dev)
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms = timed(lambda: dsa.quantize_e4m3(x, codes=codes, scales=scales))
+    nbytes = T * H * D * 2 + T * H * D + T * 4
+    del x, codes, scales
+    B, Lmax, p = 64, 200001, 200000
+    cache = torch.zeros((B, Lmax, D), dtype=torch.uint8, device=dev)
+    sc_cache = torch.zeros((B, Lmax), dtype=torch.float32, device=dev)
+    new = torch.randn((B, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    us_app = timed(lambda: dsa.quantize_e4m3(new, codes=cache[:, p], scales=sc_cache[:, p]), n=50) * 1e3
+    del cache, sc_cache
+    torch.cuda.empty_cache()
+    log(f"[bench] quantize: q^I prefill {ms:.3f} ms ({nbytes / (ms * 1e-3) / 1e9:.0f} GB/s), decode append {us_app:.1f} us")
+    return {"prefill_qI_tokens": T, "prefill_ms": round(ms, 4), "prefill_hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "prefill_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "decode_append_rows": B, "decode_append_us": round(us_app, 2)}
 
 
 def bench_chunk1m(args, dsa, synth, accounting, torch, np, dev, stream):
