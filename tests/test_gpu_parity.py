@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from oracle.formats import decode_e4m3
 import synth
 import dsa_lightning_indexer_scores_amd as dsa
 from tests._helpers import to_f64, indexer_to_oracle, attn_to_oracle, index_sets_agree
@@ -404,13 +405,15 @@ def _quant_inputs(dtype, T=37, H=64, D=128, seed=8):
     x[3] = 0.0                                    # all-zero token: scale 1, codes 0
     x[5] *= 1e-6                                  # subnormal codes
     x[7] *= 3e4
-    x[9, 0, :5] = torch.tensor([-0.0, 1.0, -1.0, 0.0, 2.0])
+    x[9, 0, :4] = torch.tensor([-0.0, 1.0, -1.0, 0.0])
     return x.to(torch.bfloat16) if dtype == "bf16" else x
 
 
+# token rows of 8192, 128, 12 and 16384 values
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quantize_e4m3_bit_exact(dtype):
-    x = _quant_inputs(dtype)
+@pytest.mark.parametrize("H,D", [(64, 128), (1, 128), (3, 4), (128, 128)])
+def test_quantize_e4m3_bit_exact(dtype, H, D):
+    x = _quant_inputs(dtype, H=H, D=D)
     codes, scales = dsa.quantize_e4m3(x.to(DEV))
     ref_c, ref_s = oracle.quantize_e4m3_per_token(x.float().numpy())
     assert np.array_equal(codes.cpu().numpy(), ref_c)
@@ -418,6 +421,36 @@ def test_quantize_e4m3_bit_exact(dtype):
     # the input generator's route (torch's cast) gives the same bytes
     syn_c, syn_s = synth.encode_e4m3_per_token(x.float())
     assert torch.equal(codes.cpu(), syn_c) and torch.equal(scales.cpu(), syn_s)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_e4m3_rounding_boundaries(dtype):
+    """Quotients on and next to E4M3 rounding boundaries, with scales that are not powers
+    of two (amax = 448 * 3 and 448 * 5 / 4): every midpoint between neighbouring codes
+    (normal and subnormal), and the neighbouring representable inputs, must round exactly as
+    the single-precision quotient does (ties to even)."""
+    grid = decode_e4m3(np.arange(0x7F, dtype=np.uint8))          # 0 .. 448
+    mids = (grid[:-1] + grid[1:]) / 2
+    rows = []
+    for c in (3.0, 1.25):
+        x = np.concatenate([mids * c, -mids * c]).astype(np.float32)
+        if dtype == "bf16":
+            x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+        near = np.concatenate([np.nextafter(x, np.float32(np.inf)), np.nextafter(x, np.float32(-np.inf))])
+        row = np.concatenate([[448.0 * c], x, near]).astype(np.float32)
+        rows.append(row)
+    n = max(len(r) for r in rows)
+    n = (n + 7) // 8 * 8
+    x = np.zeros((len(rows), n), np.float32)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = r
+    xt = torch.from_numpy(x)
+    if dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    codes, scales = dsa.quantize_e4m3(xt.to(DEV))
+    ref_c, ref_s = oracle.quantize_e4m3_per_token(xt.float().numpy())
+    assert np.array_equal(scales.cpu().numpy(), ref_s)
+    assert np.array_equal(codes.cpu().numpy(), ref_c)
 
 
 def test_quantize_appends_to_cache_slot():
