@@ -437,6 +437,35 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
     gather_bytes = cfg.B * k * cfg.Dqk * 2                 # selected latent rows per layer
     log(f"[bench] decode step {step_ms * 1e3:.1f} us (indexer+topk {idx_ms * 1e3:.1f} us, "
         f"attention {attn_ms * 1e3:.1f} us/layer)")
+    # the same caches as a variable-length batch: sequence b holds its first lens[b] keys,
+    # lengths seeded uniform in [Lk/2, Lk]; bandwidth over the keys actually held
+    lens_np = np.random.default_rng(5).integers(cfg.L // 2, cfg.L + 1, cfg.B).astype(np.int32)
+    lens = torch.from_numpy(lens_np).to(dev)
+
+    def step_varlen(ev):
+        ev[0].record(stream)
+        dsa.indexer_topk_varlen(ind["q"], ind["k"], ind["w"], k, lens, q_scale=ind["q_scale"],
+                                k_scale=ind["k_scale"], ws=ws, out=idx)
+        ev[1].record(stream)
+        for l in range(cfg.n_layers):
+            dsa.sparse_attn(layers[l], idx, ws=ws, out=outs[l])
+        ev[2].record(stream)
+
+    step_varlen([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    evv = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for s_ in range(n):
+        step_varlen(evv[s_])
+    torch.cuda.synchronize()
+    v_step = float(np.median([e[0].elapsed_time(e[2]) for e in evv]))
+    v_idx = float(np.median([e[0].elapsed_time(e[1]) for e in evv]))
+    v_bytes = int(lens_np.astype(np.int64).sum()) * (cfg.d_I + 4)
+    varlen = {"lengths": f"seeded uniform in [{cfg.L // 2}, {cfg.L}]", "mean_len": round(float(lens_np.mean()), 1),
+              "step_us": round(v_step * 1e3, 1), "indexer_topk_us": round(v_idx * 1e3, 1),
+              "indexer_hbm_gbs": round(v_bytes / (v_idx * 1e-3) / 1e9, 1),
+              "indexer_hbm_frac": round(v_bytes / (v_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] decode varlen (mean {lens_np.mean():.0f} keys) step {v_step * 1e3:.1f} us "
+        f"(indexer+topk {v_idx * 1e3:.1f} us)")
     out = {"workload": cfg.name, "B": cfg.B, "Lk": cfg.L, "step_us": round(step_ms * 1e3, 1),
            "us_per_token": round(step_ms * 1e3 / cfg.B, 2),
            "indexer_topk_us": round(idx_ms * 1e3, 1),
@@ -444,7 +473,8 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
            "indexer_hbm_frac": round(kI_bytes / (idx_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "attn_us_per_layer": round(attn_ms * 1e3, 1),
            "attn_gather_gbs": round(gather_bytes / (attn_ms * 1e-3) / 1e9, 1),
-           "attn_gather_frac": round(gather_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+           "attn_gather_frac": round(gather_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "varlen": varlen}
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out

@@ -70,6 +70,7 @@ def load_library():
     lib.dsa_indexer_scores.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, vp]
     lib.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.dsa_indexer_topk.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, i32, vp, vp, sz, vp]
+    lib.dsa_indexer_topk_varlen.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, i32, vp, vp, sz, vp]
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
@@ -77,8 +78,8 @@ def load_library():
     lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
-    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_sparse_attn", "dsa_layer_group",
-               "dsa_layer_schedule", "dsa_quantize_e4m3"):
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen", "dsa_sparse_attn",
+               "dsa_layer_group", "dsa_layer_schedule", "dsa_quantize_e4m3"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -182,6 +183,24 @@ def indexer_topk(q, k, w, topk_k, q_scale=None, k_scale=None, ws=None, out=None,
         out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=q.device)
     _check("dsa_indexer_topk", load_library().dsa_indexer_topk(
         ctypes.byref(s), B, Lq, Lk, topk_k, _ptr(out), _ptr(buf), nbytes, _stream(stream)))
+    return out
+
+
+def indexer_topk_varlen(q, k, w, topk_k, seq_lens, q_scale=None, k_scale=None, ws=None, out=None, stream=None):
+    """Decode indexer + top-k over caches of different lengths: k [B, Lk_max, d_I] of which
+    sequence b holds the first seq_lens[b] rows (seq_lens: int32 [B] on the device).
+    idx [B, Lq, topk_k] int32; Lq < 16."""
+    _require_cuda(seq_lens)
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (q.shape[0],):
+        raise ValueError("seq_lens must be int32 [B]")
+    s, B, Lq, Lk = _indexer_struct(q, k, w, q_scale, k_scale)
+    need = workspace_size(DSA_OP_INDEXER_TOPK, s.dtype, B, Lq, Lk, topk_k)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(need, q.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=q.device)
+    _check("dsa_indexer_topk_varlen", load_library().dsa_indexer_topk_varlen(
+        ctypes.byref(s), B, Lq, Lk, _ptr(seq_lens), topk_k, _ptr(out), _ptr(buf), nbytes, _stream(stream)))
     return out
 
 

@@ -131,7 +131,7 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
   hipError_t e;
   if (in->dtype != DSA_F32 && use_materialised(in->dtype, Lq)) {
     // few queries (decode): chunk candidate lists, no score rows
-    e = dsa::launch_indexer_topk_lists(a, k, idx, ws, ws_bytes, s);
+    e = dsa::launch_indexer_topk_lists(a, k, nullptr, idx, ws, ws_bytes, s);
   } else if (use_materialised(in->dtype, Lq)) {
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     float* scores = reinterpret_cast<float*>(w8);
@@ -209,6 +209,22 @@ int dsa_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
   return run_indexer_topk(in, B, Lq, Lk, k, idx, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+int dsa_indexer_topk_varlen(const dsa_indexer_in* in, int B, int Lq, int Lk_max, const int32_t* seq_lens, int k,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_indexer(in, B, Lq, Lk_max);
+  if (st != DSA_OK) return st;
+  if (!seq_lens || !idx || k <= 0 || k > kMaxFusedK) return DSA_ERR_ARG;
+  if (in->dtype == DSA_F32) return DSA_ERR_DTYPE;
+  if (Lq >= kMinFusedLq) return DSA_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(seq_lens, 4)) return DSA_ERR_ALIGN;
+  const size_t need = indexer_topk_ws(in->dtype, B, Lq, Lk_max, k);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_indexer_topk_lists(make_indexer_args(in, B, Lq, Lk_max), k, seq_lens, idx, ws,
+                                                      ws_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
 int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx, int64_t idx_q_stride, int k,

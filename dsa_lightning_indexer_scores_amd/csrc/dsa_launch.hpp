@@ -49,10 +49,16 @@ struct ChunkLists {
   uint32_t* pos;        // [rows][row_stride] positions
   uint32_t* cnt;        // [rows][n_chunks] entries per list
   uint32_t* row_hist;   // [rows][2048] top-11-bit histogram of the causal scores
+  const int32_t* seq_lens;  // [B] keys held by each sequence's cache (clamped to [0, Lk]), or
+                            // null: every sequence holds Lk
 };
+// Keys of sequence b (device side): seq_lens[b] clamped to [0, Lk], or Lk.
+__device__ __forceinline__ int chunk_lists_seq_len(const ChunkLists& L, int b, int Lk) {
+  return L.seq_lens ? min(max(L.seq_lens[b], 0), Lk) : Lk;
+}
 size_t chunk_lists_ws(int rows, int Lk);
-hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, int32_t* idx, void* ws, size_t ws_bytes,
-                                     hipStream_t s);
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, int32_t* idx, void* ws,
+                                     size_t ws_bytes, hipStream_t s);
 hipError_t launch_topk_lists_finish(const ChunkLists& L, int rows, int causal_Lq, int causal_Lk, int k,
                                     int32_t* idx, hipStream_t s);
 

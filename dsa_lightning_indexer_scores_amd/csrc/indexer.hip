@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, in
   const int qrow = blockIdx.x / L.n_chunks;
   const int chunk = blockIdx.x - qrow * L.n_chunks;
   const int b = qrow / a.Lq, i = qrow - b * a.Lq;
-  const int p = a.Lk - a.Lq + i;
+  const int p = chunk_lists_seq_len(L, b, a.Lk) - a.Lq + i;   // query position (< 0: no keys)
   const int tid = threadIdx.x, lane = tid & 63, wv_id = tid >> 6, g = lane >> 4;
   const int s_begin = chunk * L.chunk;
   const int s_end = min(a.Lk, s_begin + L.chunk);
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void lists_filter_kernel(ChunkLists L, int cau
   __shared__ __attribute__((aligned(16))) uint32_t hist[kRowHistBins];
   __shared__ uint32_t sh[8 * 4];
   const int row = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int nv = causal_Lk - causal_Lq + (row % causal_Lq) + 1;
+  const int nv = chunk_lists_seq_len(L, row / causal_Lq, causal_Lk) - causal_Lq + (row % causal_Lq) + 1;
   if (nv <= k) return;                                  // short rows need no lists
   const i32x4* rh = reinterpret_cast<const i32x4*>(L.row_hist + (size_t)row * kRowHistBins);
   const i32x4 h0 = rh[2 * tid], h1 = rh[2 * tid + 1];
@@ -1068,11 +1068,12 @@ static void chunksel_dispatch(const IndexerArgs& a, int k, const ChunkLists& L, 
   }
 }
 
-hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, int32_t* idx, void* ws, size_t ws_bytes,
-                                     hipStream_t s) {
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, int32_t* idx, void* ws,
+                                     size_t ws_bytes, hipStream_t s) {
   const int rows = a.B * a.Lq;
   if (ws_bytes < chunk_lists_ws(rows, a.Lk)) return hipErrorInvalidValue;
   ChunkLists L = plan_lists(rows, a.Lk);
+  L.seq_lens = seq_lens;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const size_t lists = ((size_t)rows * L.row_stride * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   const size_t cnt = ((size_t)rows * ((a.Lk + 63) / 64) * sizeof(uint32_t) + 255) / 256 * 256;

@@ -437,7 +437,7 @@ __global__ __launch_bounds__(kTopBS) void topk_lists_finish_kernel(ChunkLists L,
   __shared__ uint32_t offs[kTopBS + 1];
   __shared__ uint32_t sh[kTopBS / 64 + 2];
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int nv = row_valid(row, causal_Lk, nullptr, causal_Lq, causal_Lk);
+  const int nv = max(0, chunk_lists_seq_len(L, row / causal_Lq, causal_Lk) - causal_Lq + (row % causal_Lq) + 1);
   int32_t* out = idx + (size_t)row * k;
   if (nv <= k) {
     emit_short_row(nullptr, nv, k, out, nullptr);

@@ -168,14 +168,32 @@ int dsa_topk(const float* scores, int64_t row_stride, int rows, int n,
  * Fused indexer + top-k ([A]; the score tiles are filtered against a running per-query
  * threshold as they are produced, so the Lq x Lk score matrix is never written):
  * idx[b, i, 0..k) = top-k positions of scores[b, i, :] as defined by dsa_indexer_scores
- * and dsa_topk.  Requires 1 <= k <= 4096.  For DSA_F32, and for fewer than 16 queries
- * per sequence (decode), the scores of each query row are written to the workspace
- * (one row of Lk floats per query, never Lq x Lk for prefill) and selected by the dsa_topk
- * kernel; otherwise the fused streaming kernel runs.
+ * and dsa_topk.  Requires 1 <= k <= 4096.  For DSA_F32 the scores of each query row are
+ * written to the workspace and selected by the dsa_topk kernel.  For fewer than 16 queries
+ * per sequence (decode), each chunk of keys keeps its scores on chip and writes only its
+ * own top-k candidates to the workspace, from which each row is selected exactly.
+ * Otherwise the fused streaming kernel runs.  The score matrix is never written.
  * ws: dsa_workspace_size(DSA_OP_INDEXER_TOPK, in->dtype, B, Lq, Lk, k, 0) bytes.
  */
 int dsa_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k,
                      int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * dsa_indexer_topk for a decode batch whose sequences hold different numbers of keys
+ * (the causal rule of [A] "IndexShare" applied to each sequence on its own: a sequence
+ * with n cached keys sees keys [0, n), and its query i of Lq sits at position n - Lq + i).
+ * seq_lens: device int32 [B], caller-owned, n_b = seq_lens[b] clamped to [0, Lk_max].
+ * k^I and k_scale are [B, Lk_max, d_I] / [B, Lk_max] caches of which sequence b uses the
+ * first n_b rows (the rest are never read); q^I, q_scale and w are as in dsa_indexer_topk.
+ * idx[b, i] is what dsa_indexer_topk returns for sequence b alone with Lk = n_b: its
+ * top-k positions in ascending order, padded with -1 (all -1 when n_b - Lq + i < 0).
+ * Requires Lq < 16, dtype DSA_BF16 or DSA_FP8_E4M3, 1 <= k <= 4096.
+ * ws: dsa_workspace_size(DSA_OP_INDEXER_TOPK, in->dtype, B, Lq, Lk_max, k, 0) bytes.
+ * Returns DSA_OK, DSA_ERR_ARG (null seq_lens, idx or operand), DSA_ERR_DTYPE (DSA_F32),
+ * DSA_ERR_SHAPE (Lq >= 16), DSA_ERR_ALIGN, DSA_ERR_WORKSPACE or DSA_ERR_HIP.
+ */
+int dsa_indexer_topk_varlen(const dsa_indexer_in* in, int B, int Lq, int Lk_max, const int32_t* seq_lens,
+                            int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Sparse core attention over selected positions ([B], combined data-flow section):

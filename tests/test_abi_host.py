@@ -47,9 +47,9 @@ def test_status_strings():
 def test_workspace_sizes_are_host_arithmetic():
     ws = dsa.workspace_size
     assert ws(dsa.DSA_OP_TOPK, dsa.DSA_F32, 1, 16, 1000, 64) == 0
-    # fp32 / decode: one score row per query
+    # fp32: one score row per query; decode: one candidate slot (key, position) per key
     assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_F32, 1, 1024, 1024, 64) >= 1024 * 1024 * 4
-    assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_FP8_E4M3, 64, 1, 200001, 2048) >= 64 * 200001 * 4
+    assert ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_FP8_E4M3, 64, 1, 200001, 2048) >= 64 * 200001 * 8
     # fused: bounded per-workgroup candidate buffers, not Lq x Lk
     big = ws(dsa.DSA_OP_INDEXER_TOPK, dsa.DSA_FP8_E4M3, 1, 131072, 131072, 2048)
     assert 0 < big < 131072 * 131072 * 4 // 16
@@ -89,6 +89,23 @@ def test_indexer_argument_errors():
     assert lib.dsa_topk(None, 8, 1, 8, None, 4, 0x1000, None, None, 0, None) == E["arg"]
     assert lib.dsa_topk(0x1000, 4, 1, 8, None, 4, 0x2000, None, None, 0, None) == E["arg"]  # stride < n
     assert lib.dsa_topk(0x1002, 8, 1, 8, None, 4, 0x2000, None, None, 0, None) == E["align"]
+
+
+@host_only
+def test_indexer_varlen_argument_errors():
+    lib = dsa.load_library()
+    fp8 = _indexer_struct(dtype=dsa.DSA_FP8_E4M3, qs=0x6000, ks=0x7000)
+
+    def call(s, B=2, Lq=1, Lk=64, lens=0x5000, k=16, idx=0x4000, ws=0x10000, nbytes=1 << 40):
+        return lib.dsa_indexer_topk_varlen(ctypes.byref(s), B, Lq, Lk, lens, k, idx, ws, nbytes, None)
+    assert call(fp8, lens=0) == -1
+    assert call(fp8, idx=0) == -1
+    assert call(fp8, k=0) == -1
+    assert call(_indexer_struct(dtype=dsa.DSA_F32, H_I=4, d_I=32)) == -2
+    assert call(fp8, Lq=16) == -3
+    assert call(fp8, lens=0x5002) == -4
+    assert call(fp8, ws=0) == -5
+    assert call(fp8, nbytes=16) == -5
 
 
 def _attn_struct(dtype=dsa.DSA_BF16, H=32, Hkv=1, Dqk=576, Dv=512, q=0x1000, k=0x2000, v=0x2000,

@@ -110,6 +110,11 @@ def test_prefill128k_full_size_sampled_rows():
         _free()
 
 
+def _varlen_lengths(B, Lk):
+    """Seeded cache lengths of a variable-length decode batch: uniform in [Lk/2, Lk]."""
+    return np.random.default_rng(5).integers(Lk // 2, Lk + 1, B).astype(np.int32)
+
+
 def test_decode200k_full_size_and_mtp():
     cfg = synth.get_config("decode200k")
     B, Lk, k = cfg.B, cfg.L, cfg.topk
@@ -124,6 +129,18 @@ def test_decode200k_full_size_and_mtp():
     idx_np = idx[seqs, 0].cpu().numpy()
     nbad = _check_sets(idx_np, scs, pos, k)
     _say(f"decode200k: index sets of sequences {seqs} agree ({nbad} differ inside the band)")
+    # the same caches as a variable-length batch (the decode launch of the benchmark's
+    # varlen line): sequence b holds its first lens[b] keys; sampled sequences equal the
+    # call on their own cache
+    lens = torch.from_numpy(_varlen_lengths(B, Lk)).to(DEV)
+    idx_v = dsa.indexer_topk_varlen(ind["q"], ind["k"], ind["w"], k, lens, q_scale=ind["q_scale"],
+                                    k_scale=ind["k_scale"], ws=ws)
+    for b in seqs:
+        n = int(lens[b])
+        ref = dsa.indexer_topk(ind["q"][b:b + 1], ind["k"][b:b + 1, :n], ind["w"][b:b + 1], k,
+                               q_scale=ind["q_scale"][b:b + 1], k_scale=ind["k_scale"][b:b + 1, :n], ws=ws)
+        assert torch.equal(idx_v[b], ref[0]), b
+    _say(f"decode200k varlen: sequences {seqs} (lengths {[int(lens[b]) for b in seqs]}) equal their own calls")
     del ind
     _free()
     lay = synth.attention_inputs(cfg, layer=0, device=DEV)

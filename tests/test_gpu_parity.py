@@ -208,6 +208,38 @@ def test_few_query_topk_heavy_ties_integer_exact(Lq):
         assert np.array_equal(got[b][0], np.flatnonzero(kk[b, :, 0] == 0x40)[:k])
 
 
+@pytest.mark.parametrize("dtype,Lq,k", [("fp8", 1, 2048), ("bf16", 4, 512), ("fp8", 3, 64)])
+def test_varlen_decode_equals_each_sequence_alone(dtype, Lq, k):
+    """A decode batch whose caches hold different numbers of keys: each sequence's index
+    rows equal dsa_indexer_topk on that sequence's own cache (bit-exact).  Lengths include
+    the full cache, one key, no key, fewer than Lq keys, fewer and a few more than k."""
+    B, Lmax = 7, 30000
+    cfg = _cfg(dtype, Lmax, k, Lq=Lq, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    lens_l = [Lmax, 1, 0, max(Lq - 1, 0), k // 2, k + 5, 17777]
+    lens = torch.tensor(lens_l, dtype=torch.int32, device=DEV)
+    idx = dsa.indexer_topk_varlen(ind["q"], ind["k"], ind["w"], k, lens, **_ind_args(ind))
+    got = idx.cpu().numpy()
+    sc = lambda t, b, n: None if t is None else t[b:b + 1, :n]
+    for b, n in enumerate(lens_l):
+        if n >= Lq:
+            ref = dsa.indexer_topk(ind["q"][b:b + 1], ind["k"][b:b + 1, :n], ind["w"][b:b + 1], k,
+                                   q_scale=sc(ind["q_scale"], b, Lq), k_scale=sc(ind["k_scale"], b, n))
+            assert np.array_equal(got[b], ref.cpu().numpy()[0]), (b, n)
+        else:   # query i sits at n - Lq + i: only rows with a non-negative position see keys
+            for i in range(Lq):
+                p = n - Lq + i
+                want = list(range(p + 1)) + [-1] * (k - max(p + 1, 0))
+                assert got[b, i].tolist() == want[:k], (b, i)
+    # the longest sequence against the oracle
+    ora = indexer_to_oracle({key: (v[0:1] if torch.is_tensor(v) else v) for key, v in ind.items()})
+    rows = [0, Lq - 1]
+    osc = _oracle_rows(ora, 0, rows, Lq, Lmax)
+    nv = [Lmax - Lq + r + 1 for r in rows]
+    ok, _, msg = index_sets_agree(got[0][rows], oracle.topk_rows(osc, nv, k), osc, nv, k, TAU[dtype])
+    assert ok, msg
+
+
 def test_rows_shorter_than_k_select_every_causal_key():
     cfg = _cfg("fp8", 3000, 2048)
     ind = synth.indexer_inputs(cfg, device=DEV)
