@@ -466,6 +466,7 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
               "indexer_hbm_frac": round(v_bytes / (v_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] decode varlen (mean {lens_np.mean():.0f} keys) step {v_step * 1e3:.1f} us "
         f"(indexer+topk {v_idx * 1e3:.1f} us)")
+    paged = bench_decode_paged(dsa, torch, np, cfg, ind, layers, ws, stream, n, k, dev)
     out = {"workload": cfg.name, "B": cfg.B, "Lk": cfg.L, "step_us": round(step_ms * 1e3, 1),
            "us_per_token": round(step_ms * 1e3 / cfg.B, 2),
            "indexer_topk_us": round(idx_ms * 1e3, 1),
@@ -474,7 +475,7 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
            "attn_us_per_layer": round(attn_ms * 1e3, 1),
            "attn_gather_gbs": round(gather_bytes / (attn_ms * 1e-3) / 1e9, 1),
            "attn_gather_frac": round(gather_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "varlen": varlen}
+           "varlen": varlen, "paged": paged}
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out
@@ -518,6 +519,76 @@ def bench_quantize(dsa, torch, np, dev, stream):
     return {"prefill_qI_tokens": T, "prefill_ms": round(ms, 4), "prefill_hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "prefill_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "decode_append_rows": B, "decode_append_us": round(us_app, 2)}
+
+
+def bench_decode_paged(dsa, torch, np, cfg, ind, layers, ws, stream, n, k, dev, page=64):
+    """The decode step over paged caches: every sequence's k^I, key scales and latent rows
+    in 64-position pages of shared pools, pages placed by a seeded random permutation; the
+    Full layer's positions are translated to pool rows once (dsa_paged_rows) and the 4
+    attention layers gather from their pools.  The layers' contiguous caches are replaced by
+    their pools one by one (the work per step is that of the contiguous step)."""
+    B, L = cfg.B, cfg.L
+    max_pages = (L + page - 1) // page
+    pool_pages = B * max_pages
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(pool_pages).astype(np.int64)).to(dev)
+    table = perm.view(B, max_pages).to(torch.int32).contiguous()
+    # pool row of (b, position): table[b, pos / page] * page + pos % page; inverse map by scatter
+    pos = torch.arange(max_pages * page, device=dev)
+    src = torch.full((pool_pages * page,), -1, dtype=torch.int64, device=dev)
+    for b in range(B):
+        prow = perm[b * max_pages + pos // page] * page + pos % page
+        valid = pos < L
+        src[prow[valid]] = b * L + pos[valid]
+    del pos
+
+    def to_pool(cache):
+        flat = cache.reshape(B * L, -1)
+        out = flat[src.clamp(min=0)]
+        out[src < 0] = 0
+        return out.reshape((pool_pages * page,) + tuple(cache.shape[2:]))
+
+    kpool = to_pool(ind["k"])
+    spool = to_pool(ind["k_scale"][..., None])[:, 0].contiguous()
+    pools = []
+    for l in range(len(layers)):
+        kv = layers[l].pop("kv")
+        pl = dict(layers[l])
+        pl["q"] = layers[l]["q"].reshape(1, B, cfg.H, cfg.Dqk)
+        pl["kv"] = to_pool(kv)[None]
+        del kv
+        torch.cuda.empty_cache()
+        pools.append(pl)
+    del src
+    lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    rows = torch.empty_like(idx)
+    outs = [torch.empty((1, B, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in pools]
+
+    def step(ev):
+        ev[0].record(stream)
+        dsa.indexer_topk_paged(ind["q"], kpool, ind["w"], k, lens, table, page, q_scale=ind["q_scale"],
+                               k_scale_pool=spool, ws=ws, out=idx)
+        dsa.paged_rows(idx, table, page, pool_pages, out=rows)
+        ev[1].record(stream)
+        for l, pl in enumerate(pools):
+            dsa.sparse_attn(pl, rows.view(1, B, k), ws=ws, out=outs[l])
+        ev[2].record(stream)
+
+    step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for s_ in range(n):
+        step(evs[s_])
+    torch.cuda.synchronize()
+    st = float(np.median([e[0].elapsed_time(e[2]) for e in evs]))
+    ix = float(np.median([e[0].elapsed_time(e[1]) for e in evs]))
+    at = float(np.median([e[1].elapsed_time(e[2]) for e in evs])) / len(pools)
+    log(f"[bench] decode paged (page {page}) step {st * 1e3:.1f} us (indexer+topk+rows {ix * 1e3:.1f} us, "
+        f"attention {at * 1e3:.1f} us/layer)")
+    del kpool, spool, pools, outs, idx, rows
+    torch.cuda.empty_cache()
+    return {"page": page, "placement": "seeded random page permutation", "step_us": round(st * 1e3, 1),
+            "indexer_topk_rows_us": round(ix * 1e3, 1), "attn_us_per_layer": round(at * 1e3, 1)}
 
 
 def bench_chunk1m(args, dsa, synth, accounting, torch, np, dev, stream):

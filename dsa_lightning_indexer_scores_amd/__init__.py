@@ -71,6 +71,9 @@ def load_library():
     lib.dsa_topk.argtypes = [vp, i64, i32, i32, vp, i32, vp, vp, vp, sz, vp]
     lib.dsa_indexer_topk.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, i32, vp, vp, sz, vp]
     lib.dsa_indexer_topk_varlen.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, i32, vp, vp, sz, vp]
+    lib.dsa_indexer_topk_paged.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, vp, vp, i32, i32, i32, i32, vp, vp,
+                                           sz, vp]
+    lib.dsa_paged_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, vp, vp]
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
@@ -78,8 +81,9 @@ def load_library():
     lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
-    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen", "dsa_sparse_attn",
-               "dsa_layer_group", "dsa_layer_schedule", "dsa_quantize_e4m3"):
+    for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
+               "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_layer_group",
+               "dsa_layer_schedule", "dsa_quantize_e4m3"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -201,6 +205,46 @@ def indexer_topk_varlen(q, k, w, topk_k, seq_lens, q_scale=None, k_scale=None, w
         out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=q.device)
     _check("dsa_indexer_topk_varlen", load_library().dsa_indexer_topk_varlen(
         ctypes.byref(s), B, Lq, Lk, _ptr(seq_lens), topk_k, _ptr(out), _ptr(buf), nbytes, _stream(stream)))
+    return out
+
+
+def indexer_topk_paged(q, k_pool, w, topk_k, seq_lens, block_table, page_size, q_scale=None, k_scale_pool=None,
+                       ws=None, out=None, stream=None):
+    """Decode indexer + top-k over paged caches: k_pool [pool_pages * page_size, d_I] (and
+    k_scale_pool [pool_pages * page_size] for fp8), block_table int32 [B, max_pages] of
+    page ids, seq_lens int32 [B].  Returns positions idx [B, Lq, topk_k] int32; Lq < 16."""
+    _require_cuda(seq_lens, block_table)
+    B = q.shape[0]
+    if seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,):
+        raise ValueError("seq_lens must be int32 [B]")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages]")
+    if k_pool.dim() != 2 or k_pool.shape[0] % page_size:
+        raise ValueError("k_pool must be [pool_pages * page_size, d_I]")
+    max_pages, pool_pages = block_table.shape[1], k_pool.shape[0] // page_size
+    s, _, Lq, _ = _indexer_struct(q, k_pool[None], w, q_scale, None if k_scale_pool is None else k_scale_pool[None])
+    need = workspace_size(DSA_OP_INDEXER_TOPK, s.dtype, B, Lq, max_pages * page_size, topk_k)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(need, q.device)
+    if out is None:
+        out = torch.empty((B, Lq, topk_k), dtype=torch.int32, device=q.device)
+    _check("dsa_indexer_topk_paged", load_library().dsa_indexer_topk_paged(
+        ctypes.byref(s), B, Lq, _ptr(seq_lens), _ptr(block_table), max_pages, page_size, pool_pages, topk_k,
+        _ptr(out), _ptr(buf), nbytes, _stream(stream)))
+    return out
+
+
+def paged_rows(idx, block_table, page_size, pool_pages, out=None, stream=None):
+    """Positions idx [B, Lq, k] -> pool rows [B, Lq, k] (dsa_paged_rows), for dsa_sparse_attn
+    over a latent page pool (call it with the queries as one batch of B * Lq)."""
+    _require_cuda(idx, block_table)
+    B, Lq, k = idx.shape
+    if out is None:
+        out = torch.empty_like(idx)
+    _check("dsa_paged_rows", load_library().dsa_paged_rows(
+        _ptr(idx), B, Lq, k, _ptr(block_table), block_table.shape[1], page_size, pool_pages, _ptr(out),
+        _stream(stream)))
     return out
 
 

@@ -131,7 +131,7 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
   hipError_t e;
   if (in->dtype != DSA_F32 && use_materialised(in->dtype, Lq)) {
     // few queries (decode): chunk candidate lists, no score rows
-    e = dsa::launch_indexer_topk_lists(a, k, nullptr, idx, ws, ws_bytes, s);
+    e = dsa::launch_indexer_topk_lists(a, k, nullptr, dsa::PagedCache{}, idx, ws, ws_bytes, s);
   } else if (use_materialised(in->dtype, Lq)) {
     uint8_t* w8 = static_cast<uint8_t*>(ws);
     float* scores = reinterpret_cast<float*>(w8);
@@ -222,8 +222,55 @@ int dsa_indexer_topk_varlen(const dsa_indexer_in* in, int B, int Lq, int Lk_max,
   const size_t need = indexer_topk_ws(in->dtype, B, Lq, Lk_max, k);
   if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
   if (!aligned(ws, 256)) return DSA_ERR_ALIGN;
-  const hipError_t e = dsa::launch_indexer_topk_lists(make_indexer_args(in, B, Lq, Lk_max), k, seq_lens, idx, ws,
-                                                      ws_bytes, static_cast<hipStream_t>(stream));
+  const hipError_t e = dsa::launch_indexer_topk_lists(make_indexer_args(in, B, Lq, Lk_max), k, seq_lens,
+                                                      dsa::PagedCache{}, idx, ws, ws_bytes,
+                                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+namespace {
+// page_size: a power of two, a multiple of 64, at most 2^20; returns log2 or -1
+int page_log2_of(int page_size) {
+  if (page_size < 64 || page_size > (1 << 20) || (page_size & (page_size - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < page_size) ++l;
+  return l;
+}
+}  // namespace
+
+int dsa_indexer_topk_paged(const dsa_indexer_in* in, int B, int Lq, const int32_t* seq_lens,
+                           const int32_t* block_table, int max_pages, int page_size, int pool_pages, int k,
+                           int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+  if (!in || !block_table || !seq_lens || max_pages <= 0 || pool_pages <= 0) return DSA_ERR_ARG;
+  const int lp = page_log2_of(page_size);
+  if (lp < 0 || (int64_t)max_pages * page_size > (int64_t)1 << 30 || (int64_t)pool_pages * page_size > (int64_t)1 << 30)
+    return DSA_ERR_SHAPE;
+  const int Lk_max = max_pages * page_size;
+  int st = check_indexer(in, B, Lq, Lk_max);
+  if (st != DSA_OK) return st;
+  if (!idx || k <= 0 || k > kMaxFusedK) return DSA_ERR_ARG;
+  if (in->dtype == DSA_F32) return DSA_ERR_DTYPE;
+  if (Lq >= kMinFusedLq) return DSA_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(seq_lens, 4) || !aligned(block_table, 4)) return DSA_ERR_ALIGN;
+  const size_t need = indexer_topk_ws(in->dtype, B, Lq, Lk_max, k);
+  if (!ws || ws_bytes < need) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return DSA_ERR_ALIGN;
+  const dsa::PagedCache pc{block_table, max_pages, lp, pool_pages};
+  const hipError_t e = dsa::launch_indexer_topk_lists(make_indexer_args(in, B, Lq, Lk_max), k, seq_lens, pc, idx,
+                                                      ws, ws_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_paged_rows(const int32_t* idx, int B, int Lq, int k, const int32_t* block_table, int max_pages,
+                   int page_size, int pool_pages, int32_t* rows_out, void* stream) {
+  if (!idx || !block_table || !rows_out || B <= 0 || Lq <= 0 || k <= 0 || max_pages <= 0 || pool_pages <= 0)
+    return DSA_ERR_ARG;
+  const int lp = page_log2_of(page_size);
+  if (lp < 0 || (int64_t)max_pages * page_size > (int64_t)1 << 30 || (int64_t)pool_pages * page_size > (int64_t)1 << 30)
+    return DSA_ERR_SHAPE;
+  if (!aligned(idx, 4) || !aligned(block_table, 4) || !aligned(rows_out, 4)) return DSA_ERR_ALIGN;
+  const dsa::PagedCache pc{block_table, max_pages, lp, pool_pages};
+  const hipError_t e = dsa::launch_paged_rows(idx, B, Lq, k, pc, rows_out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

@@ -51,14 +51,26 @@ struct ChunkLists {
   uint32_t* row_hist;   // [rows][2048] top-11-bit histogram of the causal scores
   const int32_t* seq_lens;  // [B] keys held by each sequence's cache (clamped to [0, Lk]), or
                             // null: every sequence holds Lk
+  // paged caches (block_table null: k^I / k_scale are [B, Lk] arrays): position s of
+  // sequence b is row block_table[b * max_pages + s / page] * page + s % page of the pools
+  // (page ids clamped to [0, pool_pages)); page is a power of two, a multiple of 64
+  const int32_t* block_table;
+  int max_pages, page_log2, pool_pages;
 };
 // Keys of sequence b (device side): seq_lens[b] clamped to [0, Lk], or Lk.
 __device__ __forceinline__ int chunk_lists_seq_len(const ChunkLists& L, int b, int Lk) {
   return L.seq_lens ? min(max(L.seq_lens[b], 0), Lk) : Lk;
 }
 size_t chunk_lists_ws(int rows, int Lk);
-hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, int32_t* idx, void* ws,
-                                     size_t ws_bytes, hipStream_t s);
+struct PagedCache {
+  const int32_t* block_table;   // null: contiguous [B, Lk] caches
+  int max_pages, page_log2, pool_pages;
+};
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, const PagedCache& pc,
+                                     int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s);
+// idx positions of a paged batch -> physical pool rows (-1 for -1 and out-of-range entries)
+hipError_t launch_paged_rows(const int32_t* idx, int B, int Lq, int k, const PagedCache& pc, int32_t* rows_out,
+                             hipStream_t s);
 hipError_t launch_topk_lists_finish(const ChunkLists& L, int rows, int causal_Lq, int causal_Lk, int k,
                                     int32_t* idx, hipStream_t s);
 

@@ -322,6 +322,7 @@ __global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, in
   __shared__ float lsc[kSelMaxChunk];
   __shared__ uint32_t lhist[kRowHistBins];
   __shared__ uint32_t sh[16];
+  __shared__ int lpage[kSelMaxChunk / 64 + 1];     // paged: physical page of each chunk page
   constexpr int RB = IdxTraits<DT>::kRowBytes;
   const int qrow = blockIdx.x / L.n_chunks;
   const int chunk = blockIdx.x - qrow * L.n_chunks;
@@ -342,10 +343,10 @@ __global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, in
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) W[hb][ii] = a.w[(size_t)qrow * a.H_I + hb * 16 + 4 * g + ii] * qs;
 
-  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * RB;
-  const float* ksc = (DT == DSA_FP8_E4M3) ? a.k_scale + (size_t)b * a.Lk : nullptr;
+  const bool paged = L.block_table != nullptr;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.k) + (paged ? 0 : (size_t)b * a.Lk * RB);
+  const float* ksc = (DT == DSA_FP8_E4M3) ? a.k_scale + (paged ? 0 : (size_t)b * a.Lk) : nullptr;
   for (int j = tid; j < kRowHistBins; j += 256) lhist[j] = 0;
-  __syncthreads();
 
   const int s_first = s_begin + wv_id * kTileKeys;
   const int s_causal_end = min(s_end, p + 1);      // keys past this are not candidates
@@ -353,14 +354,32 @@ __global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, in
   // key rows clamped into [s_begin, last] (see indexer_rowscan_kernel)
   const int last = max(s_begin, s_causal_end - 1);
   const int n_tiles = s_first < s_causal_end ? (s_causal_end - s_first + kStride - 1) / kStride : 0;
+  // paged: the physical pages of the chunk's positions [s_begin, last] go to LDS once
+  const int pg0 = s_begin >> L.page_log2;
+  if (paged && s_begin < s_causal_end) {
+    const int n_pg = (last >> L.page_log2) - pg0 + 1;
+    for (int j = tid; j < n_pg; j += 256) {
+      const int pg = L.block_table[(size_t)b * L.max_pages + pg0 + j];
+      lpage[j] = min(max(pg, 0), L.pool_pages - 1);
+    }
+  }
+  __syncthreads();
+  // A 64-key tile lies in one page (pages are multiples of 64 keys, tiles 64-aligned, and
+  // clamped keys stay in the page of min(tile start, last)): one LDS lookup per tile.
   auto load_tile = [&](int t, Op<DT> (&Bk)[4], float& kscale) {
     const int s0 = s_first + t * kStride;
+    int64_t shift = 0;                               // physical row - position, this tile
+    if (paged) {
+      const int kt = min(s0, last);
+      const int lp = kt >> L.page_log2;
+      shift = ((int64_t)lpage[lp - pg0] - lp) << L.page_log2;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int key = min(s0 + kb * 16 + (lane & 15), last);
-      Bk[kb] = load_op<DT>(kbase + (size_t)key * RB, g);
+      Bk[kb] = load_op<DT>(kbase + (size_t)(key + shift) * RB, g);
     }
-    if (DT == DSA_FP8_E4M3) kscale = ksc[min(s0 + lane, last)];
+    if (DT == DSA_FP8_E4M3) kscale = ksc[(size_t)(min(s0 + lane, last) + shift)];
   };
   // two tiles in flight in three buffers rotating by name (see indexer_rowscan_kernel)
   Op<DT> B0[4], B1[4], B2[4];
@@ -1068,12 +1087,16 @@ static void chunksel_dispatch(const IndexerArgs& a, int k, const ChunkLists& L, 
   }
 }
 
-hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, int32_t* idx, void* ws,
-                                     size_t ws_bytes, hipStream_t s) {
+hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t* seq_lens, const PagedCache& pc,
+                                     int32_t* idx, void* ws, size_t ws_bytes, hipStream_t s) {
   const int rows = a.B * a.Lq;
   if (ws_bytes < chunk_lists_ws(rows, a.Lk)) return hipErrorInvalidValue;
   ChunkLists L = plan_lists(rows, a.Lk);
   L.seq_lens = seq_lens;
+  L.block_table = pc.block_table;
+  L.max_pages = pc.max_pages;
+  L.page_log2 = pc.block_table ? pc.page_log2 : 0;
+  L.pool_pages = pc.pool_pages;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   const size_t lists = ((size_t)rows * L.row_stride * 2 * sizeof(uint32_t) + 255) / 256 * 256;
   const size_t cnt = ((size_t)rows * ((a.Lk + 63) / 64) * sizeof(uint32_t) + 255) / 256 * 256;
@@ -1091,6 +1114,29 @@ hipError_t launch_indexer_topk_lists(const IndexerArgs& a, int k, const int32_t*
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_topk_lists_finish(L, rows, a.Lq, a.Lk, k, idx, s);
+}
+
+__global__ __launch_bounds__(256) void paged_rows_kernel(const int32_t* __restrict__ idx, int64_t n, int Lq, int k,
+                                                         PagedCache pc, int32_t* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const int b = (int)(e / ((int64_t)Lq * k));
+  const int v = idx[e];
+  const int lp = v >> pc.page_log2;
+  int r = -1;
+  if (v >= 0 && lp < pc.max_pages) {
+    const int pg = pc.block_table[(size_t)b * pc.max_pages + lp];
+    if (pg >= 0 && pg < pc.pool_pages) r = (pg << pc.page_log2) | (v & ((1 << pc.page_log2) - 1));
+  }
+  out[e] = r;
+}
+
+hipError_t launch_paged_rows(const int32_t* idx, int B, int Lq, int k, const PagedCache& pc, int32_t* rows_out,
+                             hipStream_t s) {
+  const int64_t n = (int64_t)B * Lq * k;
+  if (n == 0) return hipSuccess;
+  paged_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(idx, n, Lq, k, pc, rows_out);
+  return hipGetLastError();
 }
 
 struct FusedPlan {

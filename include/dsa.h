@@ -196,6 +196,39 @@ int dsa_indexer_topk_varlen(const dsa_indexer_in* in, int B, int Lq, int Lk_max,
                             int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_indexer_topk_varlen over paged caches ([B] section 5.2: per-layer caches; the
+ * serving layout stores them in fixed-size pages).  Position s of sequence b is row
+ *   block_table[b * max_pages + s / page_size] * page_size + s % page_size
+ * of the page pools in->k ([pool_pages * page_size, d_I]) and in->k_scale
+ * ([pool_pages * page_size]); page ids outside [0, pool_pages) are clamped into it (a
+ * precondition violation: the result is then unspecified but every read stays in the
+ * pools).  seq_lens (device int32 [B]) as in dsa_indexer_topk_varlen, clamped to
+ * [0, max_pages * page_size]; only table entries of pages below ceil(n_b / page_size) are
+ * read.  page_size: a power of two, a multiple of 64, at most 2^20.  idx holds positions
+ * (not pool rows) and equals dsa_indexer_topk_varlen on the same caches laid out
+ * contiguously.
+ * ws: dsa_workspace_size(DSA_OP_INDEXER_TOPK, in->dtype, B, Lq, max_pages * page_size, k, 0).
+ * Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE (DSA_F32), DSA_ERR_SHAPE (Lq >= 16, a page size
+ * or pool beyond the limits above), DSA_ERR_ALIGN, DSA_ERR_WORKSPACE or DSA_ERR_HIP.
+ */
+int dsa_indexer_topk_paged(const dsa_indexer_in* in, int B, int Lq, const int32_t* seq_lens,
+                           const int32_t* block_table, int max_pages, int page_size, int pool_pages, int k,
+                           int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Positions to pool rows for paged attention caches: rows_out[b, i, j] = the pool row of
+ * position idx[b, i, j] of sequence b (block_table / page_size / pool_pages as in
+ * dsa_indexer_topk_paged), or -1 where idx is -1, past max_pages * page_size, or on a page
+ * id outside [0, pool_pages).  idx, rows_out: device int32 [B, Lq, k], caller-owned.  The
+ * layers of a group share the block table, so one call serves all of them: dsa_sparse_attn
+ * then runs with B = 1, Lq = B * Lq, Lk = pool_pages * page_size, k = the latent page pool
+ * and idx = rows_out.  Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_SHAPE, DSA_ERR_ALIGN or
+ * DSA_ERR_HIP.
+ */
+int dsa_paged_rows(const int32_t* idx, int B, int Lq, int k, const int32_t* block_table, int max_pages,
+                   int page_size, int pool_pages, int32_t* rows_out, void* stream);
+
+/*
  * Sparse core attention over selected positions ([B], combined data-flow section):
  * for query (b, i), head h, with S = the entries of its idx row that lie in [0, Lk)
  * (-1 and out-of-range entries are skipped):

@@ -108,6 +108,30 @@ def test_indexer_varlen_argument_errors():
     assert call(fp8, nbytes=16) == -5
 
 
+@host_only
+def test_paged_argument_errors():
+    lib = dsa.load_library()
+    fp8 = _indexer_struct(dtype=dsa.DSA_FP8_E4M3, qs=0x6000, ks=0x7000)
+
+    def call(s, B=2, Lq=1, lens=0x5000, table=0x8000, max_pages=4, page=64, pool=16, k=16, idx=0x4000,
+             ws=0x10000, nbytes=1 << 40):
+        return lib.dsa_indexer_topk_paged(ctypes.byref(s), B, Lq, lens, table, max_pages, page, pool, k, idx, ws,
+                                          nbytes, None)
+    assert call(fp8, table=0) == -1
+    assert call(fp8, lens=0) == -1
+    assert call(fp8, pool=0) == -1
+    for bad_page in (32, 96, 100, 1 << 21):
+        assert call(fp8, page=bad_page) == -3
+    assert call(fp8, Lq=16, max_pages=1) == -3
+    assert call(_indexer_struct(dtype=dsa.DSA_F32, H_I=4, d_I=32)) == -2
+    assert call(fp8, table=0x8002) == -4
+    assert call(fp8, nbytes=16) == -5
+    rows = lib.dsa_paged_rows
+    assert rows(0, 1, 1, 8, 0x8000, 4, 64, 16, 0x9000, None) == -1
+    assert rows(0x4000, 1, 1, 8, 0x8000, 4, 48, 16, 0x9000, None) == -3
+    assert rows(0x4002, 1, 1, 8, 0x8000, 4, 64, 16, 0x9000, None) == -4
+
+
 def _attn_struct(dtype=dsa.DSA_BF16, H=32, Hkv=1, Dqk=576, Dv=512, q=0x1000, k=0x2000, v=0x2000,
                  ks=576, vs=576, out=0x3000):
     return dsa._AttnIn(q, k, ks, v, vs, out, None, H, Hkv, Dqk, Dv, 0.04, dtype)

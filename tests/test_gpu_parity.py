@@ -240,6 +240,54 @@ def test_varlen_decode_equals_each_sequence_alone(dtype, Lq, k):
     assert ok, msg
 
 
+def _to_pool(cache, table, page, pool_pages):
+    """Contiguous per-sequence rows [B, Lmax, ...] -> a page pool [pool_pages * page, ...]
+    laid out by the block table (unused pool pages hold garbage)."""
+    B, max_pages = table.shape
+    pool = torch.full((pool_pages * page,) + tuple(cache.shape[2:]), 0x3C if cache.dtype == torch.uint8 else 7,
+                      dtype=cache.dtype, device=cache.device)
+    for b in range(B):
+        for j in range(max_pages):
+            pg = int(table[b, j])
+            pool[pg * page:(pg + 1) * page] = cache[b, j * page:(j + 1) * page]
+    return pool
+
+
+@pytest.mark.parametrize("dtype,Lq,page", [("fp8", 1, 64), ("bf16", 3, 256)])
+def test_paged_decode_equals_contiguous_caches(dtype, Lq, page):
+    """Paged k^I / latent caches with a random page permutation (and spare pool pages):
+    the index rows equal dsa_indexer_topk_varlen on the contiguous caches, and attention
+    over the latent pool through dsa_paged_rows equals attention on the contiguous cache,
+    bit for bit."""
+    B, Lmax, k = 5, 12800, 512
+    cfg = _cfg(dtype, Lmax, k, Lq=Lq, B=B)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    lens = torch.tensor([Lmax, 1, 0, 3000, Lmax - 1], dtype=torch.int32, device=DEV)
+    max_pages = Lmax // page
+    pool_pages = B * max_pages + 7
+    rng = np.random.default_rng(21)
+    table = torch.from_numpy(rng.permutation(pool_pages)[:B * max_pages].reshape(B, max_pages)
+                             .astype(np.int32)).to(DEV)
+    kpool = _to_pool(ind["k"], table, page, pool_pages)
+    spool = None if ind["k_scale"] is None else _to_pool(ind["k_scale"], table, page, pool_pages)
+    idx_v = dsa.indexer_topk_varlen(ind["q"], ind["k"], ind["w"], k, lens, **_ind_args(ind))
+    idx_p = dsa.indexer_topk_paged(ind["q"], kpool, ind["w"], k, lens, table, page, q_scale=ind["q_scale"],
+                                   k_scale_pool=spool)
+    assert torch.equal(idx_p, idx_v)
+    rows = dsa.paged_rows(idx_v, table, page, pool_pages)
+    iv = idx_v.cpu().numpy()
+    tb = table.cpu().numpy()
+    want = np.where(iv >= 0, tb[np.arange(B)[:, None, None], np.maximum(iv, 0) // page] * page + iv % page, -1)
+    assert np.array_equal(rows.cpu().numpy(), want)
+    lay = synth.attention_inputs(cfg, layer=0, device=DEV, Lq=Lq)
+    ref = dsa.sparse_attn(lay, idx_v, out_dtype=torch.float32)
+    lay_pool = dict(lay)
+    lay_pool["q"] = lay["q"].reshape(1, B * Lq, cfg.H, cfg.Dqk)
+    lay_pool["kv"] = _to_pool(lay["kv"], table, page, pool_pages)[None]
+    got = dsa.sparse_attn(lay_pool, rows.reshape(1, B * Lq, k), out_dtype=torch.float32)
+    assert torch.equal(got.reshape(ref.shape), ref)
+
+
 def test_rows_shorter_than_k_select_every_causal_key():
     cfg = _cfg("fp8", 3000, 2048)
     ind = synth.indexer_inputs(cfg, device=DEV)
