@@ -280,6 +280,22 @@ def main():
                         "gathered_gb": round(attn_gather_gb, 2),
                         "gather_gbs": round(attn_gather_gb / (attn_ms * 1e-3), 1)},
     }
+    if cfg.attn == "mla" and not args.no_decode:
+        # one layer over an FP8 latent cache (E4M3 codes + per-row scales) at the same shapes
+        lay8 = synth.fp8_latent(layers[1])
+        dsa.sparse_attn(lay8, idx, ws=ws, out=outs[1])
+        torch.cuda.synchronize()
+        f0 = torch.cuda.Event(enable_timing=True)
+        f1 = torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        for _ in range(3):
+            dsa.sparse_attn(lay8, idx, ws=ws, out=outs[1])
+        f1.record(stream)
+        torch.cuda.synchronize()
+        kernels["sparse_attn_fp8_latent"] = {"ms_per_layer": round(f0.elapsed_time(f1) / 3, 4)}
+        log(f"[bench] fp8 latent attention {f0.elapsed_time(f1) / 3:.2f} ms/layer")
+        del lay8
+        torch.cuda.empty_cache()
     # roofline object: the kernel with the larger share of the step
     if idx_ms >= attn_ms * cfg.n_layers:
         roof = {"kernel": "indexer_topk", "bound": "mfma", "achieved": round(idx_tfs, 2),
@@ -466,6 +482,34 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
               "indexer_hbm_frac": round(v_bytes / (v_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] decode varlen (mean {lens_np.mean():.0f} keys) step {v_step * 1e3:.1f} us "
         f"(indexer+topk {v_idx * 1e3:.1f} us)")
+    # FP8 latent caches (E4M3 codes + one fp32 scale per row): the same step with every
+    # layer's attention reading 580 bytes per selected row instead of 1152
+    layers8 = [synth.fp8_latent(lay) for lay in layers]
+
+    def step_kv8(ev):
+        ev[0].record(stream)
+        dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"], k_scale=ind["k_scale"],
+                         ws=ws, out=idx)
+        ev[1].record(stream)
+        for l in range(cfg.n_layers):
+            dsa.sparse_attn(layers8[l], idx, ws=ws, out=outs[l])
+        ev[2].record(stream)
+
+    step_kv8([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    ev8 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for s_ in range(n):
+        step_kv8(ev8[s_])
+    torch.cuda.synchronize()
+    k8_step = float(np.median([e[0].elapsed_time(e[2]) for e in ev8]))
+    k8_attn = float(np.median([e[1].elapsed_time(e[2]) for e in ev8])) / cfg.n_layers
+    g8 = cfg.B * k * (cfg.Dqk + 4)
+    fp8_kv = {"step_us": round(k8_step * 1e3, 1), "attn_us_per_layer": round(k8_attn * 1e3, 1),
+              "gathered_mb": round(g8 / 1e6, 1), "attn_gather_gbs": round(g8 / (k8_attn * 1e-3) / 1e9, 1),
+              "attn_gather_frac": round(g8 / (k8_attn * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"[bench] decode fp8 latent step {k8_step * 1e3:.1f} us (attention {k8_attn * 1e3:.1f} us/layer)")
+    del layers8
+    torch.cuda.empty_cache()
     paged = bench_decode_paged(dsa, torch, np, cfg, ind, layers, ws, stream, n, k, dev)
     out = {"workload": cfg.name, "B": cfg.B, "Lk": cfg.L, "step_us": round(step_ms * 1e3, 1),
            "us_per_token": round(step_ms * 1e3 / cfg.B, 2),
@@ -475,7 +519,7 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
            "attn_us_per_layer": round(attn_ms * 1e3, 1),
            "attn_gather_gbs": round(gather_bytes / (attn_ms * 1e-3) / 1e9, 1),
            "attn_gather_frac": round(gather_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "varlen": varlen, "paged": paged}
+           "varlen": varlen, "fp8_latent": fp8_kv, "paged": paged}
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out

@@ -75,6 +75,7 @@ def load_library():
                                            sz, vp]
     lib.dsa_paged_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, vp, vp]
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
+    lib.dsa_sparse_attn_kv8.argtypes = [ctypes.POINTER(_AttnIn), vp, i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
     lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
@@ -82,7 +83,7 @@ def load_library():
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
-               "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_layer_group",
+               "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_sparse_attn_kv8", "dsa_layer_group",
                "dsa_layer_schedule", "dsa_quantize_e4m3"):
         getattr(lib, fn).restype = i32
     _lib = lib
@@ -271,7 +272,8 @@ def sparse_attn(layer, idx, idx_q_stride=None, return_lse=False, ws=None, out=No
     """Sparse attention of one layer over the positions in idx.
 
     layer: dict with q [B,Lq,H,Dqk], sm_scale, and either kv [B,Lk,576] (MLA latent, V = first
-    512 dims) or k [B,Lk,Hkv,Dqk] and v [B,Lk,Hkv,Dv].  idx: [B,Lq,k] int32, or [B,1,k] with
+    512 dims; uint8 E4M3 codes with kv_scale [B,Lk] float32 for an FP8 latent cache) or
+    k [B,Lk,Hkv,Dqk] and v [B,Lk,Hkv,Dv].  idx: [B,Lq,k] int32, or [B,1,k] with
     idx_q_stride=0 (all queries share the row, the MTP-draft case).  out_dtype: torch.float32
     keeps the fp32 result; default is q's dtype.
     """
@@ -289,8 +291,16 @@ def sparse_attn(layer, idx, idx_q_stride=None, return_lse=False, ws=None, out=No
     need = workspace_size(DSA_OP_SPARSE_ATTN, s.dtype, B, Lq, Lk, k, H)
     ws = ws or Workspace()
     buf, nbytes = ws.get(need, q.device)
-    _check("dsa_sparse_attn", load_library().dsa_sparse_attn(
-        ctypes.byref(s), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _ptr(buf), nbytes, _stream(stream)))
+    if layer.get("kv_scale") is not None:
+        sc = layer["kv_scale"]
+        _require_cuda(sc)
+        if layer["kv"].dtype != torch.uint8 or sc.dtype != torch.float32 or tuple(sc.shape) != tuple(layer["kv"].shape[:2]):
+            raise ValueError("an FP8 latent cache is uint8 codes [B, Lk, 576] with float32 kv_scale [B, Lk]")
+        _check("dsa_sparse_attn_kv8", load_library().dsa_sparse_attn_kv8(
+            ctypes.byref(s), _ptr(sc), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _ptr(buf), nbytes, _stream(stream)))
+    else:
+        _check("dsa_sparse_attn", load_library().dsa_sparse_attn(
+            ctypes.byref(s), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _ptr(buf), nbytes, _stream(stream)))
     return (out, lse) if return_lse else out
 
 

@@ -103,6 +103,8 @@ dsa::AttnArgs make_attn_args(const dsa_attn_in* in, int B, int Lq, int Lk, const
   a.idx = idx;
   a.idx_q_stride = idx_q_stride;
   a.topk = k;
+  a.kv8 = 0;
+  a.kv_scale = nullptr;
   return a;
 }
 
@@ -283,6 +285,29 @@ int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t*
   if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
   const hipError_t e = dsa::launch_sparse_attn(make_attn_args(in, B, Lq, Lk, idx, idx_q_stride, k), ws, ws_bytes,
                                                static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_sparse_attn_kv8(const dsa_attn_in* in, const float* kv_scale, int B, int Lq, int Lk, const int32_t* idx,
+                        int64_t idx_q_stride, int k, void* ws, size_t ws_bytes, void* stream) {
+  if (!in || !kv_scale) return DSA_ERR_ARG;
+  if (in->dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  // the bf16 checks cover q, out, idx and the shapes; the cache rows are checked as codes
+  dsa_attn_in as_bf16 = *in;
+  as_bf16.k_row_stride = as_bf16.v_row_stride = 576;
+  int st = check_attn(&as_bf16, B, Lq, Lk, idx, idx_q_stride, k);
+  if (st != DSA_OK) return st;
+  if (in->H > 32) return DSA_ERR_SHAPE;
+  if (in->v != in->k || in->v_row_stride != in->k_row_stride) return DSA_ERR_SHAPE;
+  if (in->k_row_stride < 576 || (in->k_row_stride % 16) != 0) return DSA_ERR_ALIGN;
+  if (!aligned(kv_scale, 4)) return DSA_ERR_ALIGN;
+  const size_t need = dsa::sparse_attn_ws(B, Lq, k, in->H, idx_q_stride, in->dtype);
+  if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
+  if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
+  dsa::AttnArgs a = make_attn_args(in, B, Lq, Lk, idx, idx_q_stride, k);
+  a.kv8 = 1;
+  a.kv_scale = kv_scale;
+  const hipError_t e = dsa::launch_sparse_attn(a, ws, ws_bytes, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

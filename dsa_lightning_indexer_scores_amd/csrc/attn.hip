@@ -371,17 +371,29 @@ __device__ __forceinline__ void wait_vm_at_most(int n) {
 // prefill grids); NB = 4 takes most of the LDS for one workgroup per CU with three blocks
 // (108 KB) in flight, for the few long-latency workgroups of decode.  The idx ring runs
 // 2 NB - 2 blocks ahead, so a block's entries have landed before its rows are requested.
-template <bool SPLIT, int NB>
+//
+// KV8: the latent cache holds OCP E4M3 codes (576 per row) and one fp32 scale per row.
+// The gathered code rows (18 KB per block) land in NB staging buffers with the block's 32
+// scales; after the block barrier every thread converts its share of the block exactly to
+// bf16 (hardware fp8 -> f32 conversion, then bf16, both exact) into one swizzled bf16
+// buffer that the unchanged QK and PV code reads.  The scale of key s factors out of its
+// dot products: it multiplies the key's score, and the key's probability enters the value
+// product as p * scale (the denominator l sums p).
+template <bool SPLIT, int NB, bool KV8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 2 : 1)))
 void mla_attn32_kernel(MlaParams P) {
   constexpr int NW = 4;
   constexpr int kDt = 16;                        // 16-dim output tiles per wave (256 dims)
   constexpr int kQSteps = 18;                    // 32-dim QK steps over the 576 latent dims
-  constexpr int kSlots = kDmaPerBlk2 / NW;       // 9 loads per wave per block
+  constexpr int kDma = KV8 ? kDmaPerBlk2 / 2 : kDmaPerBlk2;   // 1 KB loads per block (18 / 36)
+  constexpr int kSlots = (kDma + NW - 1) / NW;   // per wave (5, 5, 4, 4 / 9)
   constexpr int kKeyAhead = 2 * NB - 2;          // idx blocks requested ahead of compute
   constexpr int kKeyBufs2 = NB == 2 ? 4 : 8;     // ring slots (j .. j + kKeyAhead in use)
   static_assert((NB & (NB - 1)) == 0 && kKeyBufs2 > kKeyAhead, "ring sizes");
-  __shared__ __attribute__((aligned(16))) uint8_t kvs[NB][kBlk2Bytes];
+  constexpr int kStgBytes = kBlk2Bytes / 2;      // 32 rows of 576 codes
+  constexpr int kRowLds = KV8 ? NB * kStgBytes + kBlk2Bytes : NB * kBlk2Bytes;
+  __shared__ __attribute__((aligned(16))) uint8_t lrows[kRowLds];
+  __shared__ __attribute__((aligned(16))) float sclring[KV8 ? kKeyBufs2 : 1][kBlk2];
   __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs2][kBlk2];
   __shared__ __attribute__((aligned(16))) float xm[NW][64];     // block maxima, then l
   __shared__ __attribute__((aligned(16))) i32x4 xp[NW][64];     // packed (hi, lo) p
@@ -409,8 +421,14 @@ void mla_attn32_kernel(MlaParams P) {
   const int blk_begin = split * P.blocks_per_split;
   const int blk_end = min(n_blk_total, blk_begin + P.blocks_per_split);
   const int nb = blk_end - blk_begin;
-  const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride * 2;
-  const uint32_t row_bytes32 = (uint32_t)(a.k_row_stride * 2);
+  constexpr int kElemBytes = KV8 ? 1 : 2;
+  const uint8_t* kvbase = reinterpret_cast<const uint8_t*>(a.k) + (size_t)b * a.Lk * a.k_row_stride * kElemBytes;
+  const uint32_t row_bytes32 = (uint32_t)(a.k_row_stride * kElemBytes);
+  const float* sclbase = KV8 ? a.kv_scale + (size_t)b * a.Lk : nullptr;
+  // DMA target of block t's rows (buffer t % NB), and the bf16 block the math reads
+  auto dma_buf = [&](int buf) { return lrows + buf * (KV8 ? kStgBytes : kBlk2Bytes); };
+  auto math_buf = [&](int buf) -> const uint8_t* { return KV8 ? lrows + NB * kStgBytes : lrows + buf * kBlk2Bytes; };
+  const int my_loads = KV8 ? (wv_id + (kSlots - 1) * NW < kDma ? kSlots : kSlots - 1) + 1 : kSlots;
 
   // idx entries of the t-th block of this range into ring slot t % 4 (lanes 0..31; every
   // wave issues the same load); positions past topk are -1
@@ -422,32 +440,43 @@ void mla_attn32_kernel(MlaParams P) {
       else slot[lane] = -1;
     }
   };
-  // the block's 32 latent rows (row r at r * 1152, 16-byte chunks swizzled as swz(r, c))
+  // the block's 32 latent rows: bf16 rows land at r * 1152 with 16-byte chunks swizzled
+  // as swz(r, c); E4M3 rows land unswizzled at r * 576 (36 chunks per row)
+  constexpr int kRowChunks = KV8 ? kChunks / 2 : kChunks;
   int dma_row[kSlots];
   uint32_t dma_off[kSlots];
 #pragma unroll
   for (int u = 0; u < kSlots; ++u) {
     const int piece = (wv_id + u * NW) * 64 + lane;
-    const int r = piece / kChunks;
+    const int r = min(piece / kRowChunks, kBlk2 - 1);   // loads past the block are skipped
     dma_row[u] = r;
-    dma_off[u] = 16 * swz(r, piece - r * kChunks);
+    dma_off[u] = 16 * (KV8 ? piece - r * kRowChunks : swz(r, piece - r * kRowChunks));
   }
-  // loads u0 .. u1-1 of this wave for the t-th block
+  // loads u0 .. u1-1 of this wave for the t-th block (KV8: the first part also gathers the
+  // block's 32 scales, every wave the same)
   auto issue_rows = [&](int t, int buf, auto u0c, auto u1c) {
     constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
     const int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
+    if constexpr (KV8 && u0 == 0) {
+      if (lane < kBlk2) {
+        const uint32_t kk = (uint32_t)slot[lane] < (uint32_t)a.Lk ? (uint32_t)slot[lane] : 0u;
+        dma_4(sclbase + kk, lds_offset(&sclring[t & (kKeyBufs2 - 1)][0]));
+      }
+    }
     int key[u1 - u0];
 #pragma unroll
     for (int u = u0; u < u1; ++u) key[u - u0] = slot[dma_row[u]];
 #pragma unroll
     for (int u = u0; u < u1; ++u) {
-      const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
-      dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(&kvs[buf][(wv_id + u * NW) * 1024]));
+      if (wv_id + u * NW < kDma) {                     // wave-uniform
+        const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
+        dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(dma_buf(buf) + (wv_id + u * NW) * 1024));
+      }
     }
   };
   using C0 = Phase<0>;
-  using C3 = Phase<3>;
-  using C6 = Phase<6>;
+  using C3 = Phase<KV8 ? 2 : 3>;
+  using C6 = Phase<KV8 ? 4 : 6>;
   using C9 = Phase<kSlots>;
 
   for (int t = 0; t < kKeyAhead && t < nb; ++t) issue_keys(t);
@@ -498,18 +527,45 @@ void mla_attn32_kernel(MlaParams P) {
 #pragma unroll
       for (int d = NB - 2; d >= 1; --d) {
         const int t = j - d;
-        after += (t + NB - 1 < nb) ? kSlots : 0;
+        after += (t + NB - 1 < nb) ? my_loads : 0;
         after += (t >= 0 && t + kKeyAhead < nb) ? 1 : 0;
       }
-      wait_vm_at_most<(NB - 2) * (kSlots + 1)>(uniform(after));
+      wait_vm_at_most<(NB - 2) * (kSlots + (KV8 ? 2 : 1))>(uniform(after));
     }
     __syncthreads();                                     // B1: landed for all; buffer of j-1 free
     // the next block's rows go out in three parts spread over the block (every wave of
     // the CU would otherwise queue all of its loads at the same moment)
     if (j + kKeyAhead < nb) issue_keys(j + kKeyAhead);
     if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C0{}, C3{});
-    const uint8_t* kb = kvs[buf];
+    if constexpr (KV8) {
+      // the block's codes to bf16: piece p (16 codes of row p / 36) -> chunks 2c, 2c + 1
+      const uint8_t* stg = dma_buf(buf);
+      uint8_t* dst = lrows + NB * kStgBytes;
+#pragma unroll
+      for (int u = 0; u < (kStgBytes / 16 + 255) / 256; ++u) {
+        const int pc = tid + 256 * u;
+        if (pc < kStgBytes / 16) {
+          const int r = pc / kRowChunks, c = pc - r * kRowChunks;
+          const i32x4 w = *reinterpret_cast<const i32x4*>(stg + 16 * pc);
+          i32x4 lo, hi;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            const f32x2 f0 = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], false);
+            const f32x2 f1 = __builtin_amdgcn_cvt_pk_f32_fp8(w[e], true);
+            const int v0 = (int)pack_bf16x2(f0.x, f0.y), v1 = (int)pack_bf16x2(f1.x, f1.y);
+            if (e < 2) { lo[2 * e] = v0; lo[2 * e + 1] = v1; }
+            else { hi[2 * e - 4] = v0; hi[2 * e - 3] = v1; }
+          }
+          *reinterpret_cast<i32x4*>(dst + r * kRowBytes + 16 * swz(r, 2 * c)) = lo;
+          *reinterpret_cast<i32x4*>(dst + r * kRowBytes + 16 * swz(r, 2 * c + 1)) = hi;
+        }
+      }
+      __syncthreads();                                   // B1b: the bf16 block is complete
+    }
+    const uint8_t* kb = math_buf(buf);
     float sv[4];
+    f32x4 kscale4 = {1.f, 1.f, 1.f, 1.f};           // KV8: the scales of this lane's keys
     float own_max = -INFINITY;
     if (wave_active) {
       // S^T of sub-block ds: two independent chains (even and odd steps)
@@ -534,10 +590,18 @@ void mla_attn32_kernel(MlaParams P) {
       const f32x4 s = s0 + s1;
       // lane holds head h, keys 16 ds + 4 g + jj of the block
       const int4 kk4 = *reinterpret_cast<const int4*>(&keyring[j & (kKeyBufs2 - 1)][16 * ds + 4 * g]);
-      sv[0] = s[0] * sl2;
-      sv[1] = s[1] * sl2;
-      sv[2] = s[2] * sl2;
-      sv[3] = s[3] * sl2;
+      if constexpr (KV8) {
+        kscale4 = *reinterpret_cast<const f32x4*>(&sclring[j & (kKeyBufs2 - 1)][16 * ds + 4 * g]);
+        sv[0] = s[0] * kscale4[0] * sl2;
+        sv[1] = s[1] * kscale4[1] * sl2;
+        sv[2] = s[2] * kscale4[2] * sl2;
+        sv[3] = s[3] * kscale4[3] * sl2;
+      } else {
+        sv[0] = s[0] * sl2;
+        sv[1] = s[1] * sl2;
+        sv[2] = s[2] * sl2;
+        sv[3] = s[3] * sl2;
+      }
       const uint32_t kmax = max(max((uint32_t)kk4.x, (uint32_t)kk4.y), max((uint32_t)kk4.z, (uint32_t)kk4.w));
       if (ballot(kmax >= (uint32_t)a.Lk)) {      // some entry invalid (rare)
         sv[0] = (uint32_t)kk4.x < (uint32_t)a.Lk ? sv[0] : -INFINITY;
@@ -566,6 +630,7 @@ void mla_attn32_kernel(MlaParams P) {
       for (int jj = 0; jj < 4; ++jj) {
         pj[jj] = __builtin_amdgcn_exp2f(sv[jj] - m_use);
         l_lane += pj[jj];
+        if constexpr (KV8) pj[jj] *= kscale4[jj];      // weight of the key's code row
       }
       // p = hi + lo, hi = RNE_bf16(p), lo = RNE_bf16(p - hi)
       const uint32_t h01 = pack_bf16x2(pj[0], pj[1]), h23 = pack_bf16x2(pj[2], pj[3]);
@@ -809,12 +874,20 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   P.part_ml = reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + pl.off_ml);
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
-  if (pl.k32 && pl.deep) {
-    if (split) mla_attn32_kernel<true, 4><<<grid, 256, 0, s>>>(P);
-    else mla_attn32_kernel<false, 4><<<grid, 256, 0, s>>>(P);
+  if (a.kv8) {   // E4M3 latent rows: the 32-key kernel only (checked by the caller)
+    if (pl.deep) {
+      if (split) mla_attn32_kernel<true, 4, true><<<grid, 256, 0, s>>>(P);
+      else mla_attn32_kernel<false, 4, true><<<grid, 256, 0, s>>>(P);
+    } else {
+      if (split) mla_attn32_kernel<true, 2, true><<<grid, 256, 0, s>>>(P);
+      else mla_attn32_kernel<false, 2, true><<<grid, 256, 0, s>>>(P);
+    }
+  } else if (pl.k32 && pl.deep) {
+    if (split) mla_attn32_kernel<true, 4, false><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 4, false><<<grid, 256, 0, s>>>(P);
   } else if (pl.k32) {
-    if (split) mla_attn32_kernel<true, 2><<<grid, 256, 0, s>>>(P);
-    else mla_attn32_kernel<false, 2><<<grid, 256, 0, s>>>(P);
+    if (split) mla_attn32_kernel<true, 2, false><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 2, false><<<grid, 256, 0, s>>>(P);
   } else if (pl.nw <= 4) {
     if (split) mla_attn_kernel<4, 2, 3, true, 2><<<grid, 256, 0, s>>>(P);
     else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);

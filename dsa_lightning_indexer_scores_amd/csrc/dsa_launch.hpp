@@ -105,6 +105,8 @@ struct AttnArgs {
   const int32_t* idx;
   int64_t idx_q_stride;
   int topk;          // entries per idx row
+  int kv8;           // latent rows are E4M3 codes (k_row_stride in bytes) ...
+  const float* kv_scale;   // ... with one fp32 scale per row, [B, Lk]
 };
 size_t sparse_attn_ws(int B, int Lq, int k, int H, int64_t idx_q_stride, int dtype);
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s);

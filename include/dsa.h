@@ -196,6 +196,22 @@ int dsa_indexer_topk_varlen(const dsa_indexer_in* in, int B, int Lq, int Lk_max,
                             int k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_sparse_attn over an FP8 latent cache ([B] section 5.5: the training and serving
+ * stack keeps the KV cache in FP8; [B] discussion section 4: FP8 KV for high-concurrency
+ * decode).  in->k (== in->v, k_row_stride == v_row_stride in BYTES, a multiple of 16, at
+ * least 576) holds OCP E4M3 codes, the first 576 of a row used, and kv_scale (device fp32
+ * [B, Lk], caller-owned) one positive scale per row: the latent row of key s is
+ * code[s] * kv_scale[s] (K all 576 dims, V the first 512).  q, out, lse, idx and every
+ * other argument as in dsa_sparse_attn with in->dtype = DSA_BF16 and H = 16 or 32; the
+ * result is dsa_sparse_attn's on the decoded rows.  The codes and scales are what
+ * dsa_quantize_e4m3 writes for 576-value rows.
+ * ws: dsa_workspace_size(DSA_OP_SPARSE_ATTN, DSA_BF16, B, Lq, Lk, k, in->H) bytes.
+ * Returns as dsa_sparse_attn (DSA_ERR_ARG for a null kv_scale).
+ */
+int dsa_sparse_attn_kv8(const dsa_attn_in* in, const float* kv_scale, int B, int Lq, int Lk, const int32_t* idx,
+                        int64_t idx_q_stride, int k, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * dsa_indexer_topk_varlen over paged caches ([B] section 5.2: per-layer caches; the
  * serving layout stores them in fixed-size pages).  Position s of sequence b is row
  *   block_table[b * max_pages + s / page_size] * page_size + s % page_size

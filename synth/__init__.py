@@ -112,6 +112,25 @@ def encode_e4m3_per_token(x):
     return codes, scale.to(torch.float32)
 
 
+def fp8_latent(layer, chunk_rows=1 << 20):
+    """A copy of an MLA layer dict whose latent cache is stored as OCP E4M3 codes with one
+    fp32 scale per row (amax/448, the encoding of encode_e4m3_per_token), encoded from
+    the layer's bf16 rows in row chunks."""
+    kv = layer["kv"]
+    B, Lk, D = kv.shape
+    flat = kv.reshape(B * Lk, D)
+    codes = torch.empty((B * Lk, D), dtype=torch.uint8, device=kv.device)
+    scales = torch.empty(B * Lk, dtype=torch.float32, device=kv.device)
+    for r0 in range(0, B * Lk, chunk_rows):
+        c, sc = encode_e4m3_per_token(flat[r0:r0 + chunk_rows].float())
+        codes[r0:r0 + chunk_rows] = c
+        scales[r0:r0 + chunk_rows] = sc
+    out = dict(layer)
+    out["kv"] = codes.reshape(B, Lk, D)
+    out["kv_scale"] = scales.reshape(B, Lk)
+    return out
+
+
 def _randn_rows(g, shape, device, std, dtype_out, chunk_rows=8192, gain_rows=None, gain=1.0):
     """Draw N(0, std^2) in row chunks (bounded temporaries), optionally scaling planted rows."""
     T = shape[0]

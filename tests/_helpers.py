@@ -30,6 +30,8 @@ def attn_to_oracle(lay):
     """Synthetic attention dict (torch) -> oracle layer dict (float64)."""
     if "kv" in lay:
         kv = to_f64(lay["kv"])                      # [B, Lk, 576]
+        if lay.get("kv_scale") is not None:         # E4M3 codes times their row's scale
+            kv = kv * to_f64(lay["kv_scale"])[..., None]
         k = kv[:, :, None, :]                       # Hkv = 1, K = whole latent row
         v = kv[:, :, None, : lay["Dv"]]             # V = first Dv dims
         return {"q": to_f64(lay["q"]), "k": k, "v": v, "sm_scale": lay["sm_scale"], "Hkv": 1}

@@ -402,6 +402,51 @@ def test_mla_deep_ring_edge_cases(B, Lq, Lk, k, seed):
     assert torch.equal(out_bf, out.to(torch.bfloat16))
 
 
+# FP8 latent cache: E4M3 codes with one fp32 scale per row (dsa_sparse_attn_kv8), the
+# two-buffer (prefill) and four-buffer split (decode) forms, against the oracle on the
+# exactly decoded rows
+@pytest.mark.parametrize("B,Lq,Lk,k", [(1, 1500, 1500, 256), (3, 1, 5000, 2048), (2, 1, 900, 520)])
+def test_mla_fp8_latent_attention_parity(B, Lq, Lk, k):
+    cfg = synth.get_config("decode200k", L=Lk, B=B)
+    lay = synth.fp8_latent(synth.attention_inputs(cfg, layer=2, device=DEV, Lq=Lq))
+    rng = np.random.default_rng(B + k)
+    idx = np.stack([np.sort(rng.permutation(min(Lk, Lk - Lq + 1 + i))[:k]) if min(Lk, Lk - Lq + 1 + i) >= k
+                    else np.concatenate([np.arange(Lk - Lq + 1 + i), -np.ones(k - (Lk - Lq + 1 + i), np.int64)])
+                    for _ in range(B) for i in range(Lq)]).reshape(B, Lq, k).astype(np.int32)
+    idx[0, 0, ::11] = -1
+    idx[-1, -1, 2::9] = Lk + 5                     # out of range: skipped
+    idx_t = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_attn(lay, idx_t, return_lse=True, out_dtype=torch.float32)
+    ol_idx = idx.copy()
+    ol_idx[ol_idx >= Lk] = -1
+    for b in range(B):
+        _attn_check(lay, ol_idx, out, lse, sorted({0, Lq // 2, Lq - 1}), b=b)
+    assert torch.equal(out, dsa.sparse_attn(lay, idx_t, out_dtype=torch.float32))     # deterministic
+    assert torch.equal(dsa.sparse_attn(lay, idx_t), out.to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("B,Lq,Lk,k", [(1, 700, 700, 128), (4, 1, 3000, 2048)])
+def test_mla_fp8_latent_equals_bf16_on_decoded_rows(B, Lq, Lk, k):
+    """With power-of-two row scales the decoded rows are exact in bf16 and every scaling
+    in the FP8 path is exact while the probabilities stay normal numbers (codes of at most
+    2 and scales 2^-3 .. 2 keep the logits within a few units), so its output equals the
+    bf16 path's on the decoded rows bit for bit."""
+    cfg = synth.get_config("decode200k", L=Lk, B=B)
+    lay = synth.attention_inputs(cfg, layer=3, device=DEV, Lq=Lq)
+    rng = np.random.default_rng(7)
+    codes = torch.from_numpy((rng.integers(0, 0x41, (B, Lk, 576)) | (rng.integers(0, 2, (B, Lk, 576)) << 7))
+                             .astype(np.uint8))
+    scale = torch.from_numpy(2.0 ** rng.integers(-3, 2, (B, Lk)).astype(np.float32))
+    dec = (codes.view(torch.float8_e4m3fn).float() * scale[..., None]).to(torch.bfloat16)
+    lay8 = dict(lay, kv=codes.to(DEV), kv_scale=scale.to(DEV))
+    layb = dict(lay, kv=dec.to(DEV))
+    idx = torch.from_numpy(np.stack([np.sort(rng.permutation(Lk)[:k]) for _ in range(B * Lq)])
+                           .reshape(B, Lq, k).astype(np.int32)).to(DEV)
+    got = dsa.sparse_attn(lay8, idx, out_dtype=torch.float32)
+    ref = dsa.sparse_attn(layb, idx, out_dtype=torch.float32)
+    assert torch.equal(got, ref)
+
+
 def test_tiny_mha_fp32_attention_parity():
     cfg = synth.get_config("tiny")
     ind = synth.indexer_inputs(cfg, device=DEV)
