@@ -160,6 +160,22 @@ def test_attention_argument_errors():
 
 
 @host_only
+def test_fp8_latent_attention_argument_errors():
+    lib = dsa.load_library()
+
+    def call(s, scale=0x7000, idx=0x5000, ws=0x100000, nbytes=1 << 40, B=1, Lq=4, Lk=64, k=16):
+        return lib.dsa_sparse_attn_kv8(ctypes.byref(s), scale, B, Lq, Lk, idx, k, k, ws, nbytes, None)
+    assert call(_attn_struct(), scale=0) == -1
+    assert call(_attn_struct(), idx=0) == -1
+    assert call(_attn_struct(dtype=dsa.DSA_F32, H=4, Hkv=4, Dqk=64, Dv=64, ks=256, vs=256)) == -2
+    assert call(_attn_struct(H=48)) == -3                       # 16 or 32 heads only
+    assert call(_attn_struct(v=0x9000)) == -3
+    assert call(_attn_struct(ks=584, vs=584)) == -4             # code rows: multiple of 16 bytes
+    assert call(_attn_struct(), scale=0x7002) == -4
+    assert call(_attn_struct(), ws=0, nbytes=0, B=2, Lq=1, k=2048) == -5
+
+
+@host_only
 def test_layer_group_argument_errors():
     lib = dsa.load_library()
     full = _indexer_struct()
