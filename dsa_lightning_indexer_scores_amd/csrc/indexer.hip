@@ -716,12 +716,16 @@ __device__ uint32_t compact_ge(uint32_t* keys, uint32_t* pos, uint32_t n, uint32
 }
 
 // Exact top-k of a candidate list: afterwards keys/pos[0..min(n,k)) hold the k largest
-// keys (ties to the earlier entry), in their original order.
-__device__ uint32_t reduce_to_k(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t k, uint32_t* hist) {
+// keys (ties to the earlier entry), in their original order.  kth receives the k-th
+// largest key when the list held more than k entries, else 0.
+__device__ uint32_t reduce_to_k(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t k, uint32_t* hist,
+                                uint32_t& kth) {
+  kth = 0u;
   if (n <= k) return n;
   __threadfence_block();
   uint32_t th, ne;
   select_exact(keys, n, k, hist, th, ne);
+  kth = th;
   const uint32_t r = compact_exact(keys, pos, n, th, ne);
   __threadfence_block();
   return r;
@@ -779,9 +783,23 @@ __device__ uint32_t flush_stage(const uint32_t* sk, const uint32_t* sp, uint32_t
   return cnt + n;
 }
 
+// Speculative starting threshold (one key segment per row only).  A row of the item a
+// workgroup processes next starts its filter at kSpecMargin times the smallest k-th score
+// of the workgroup's previous item instead of admitting every key.  If at least k keys pass
+// a threshold, the row's k-th largest key passes it, so the exact selection over the
+// admitted keys is the row's top-k (ties included).  A row that admits fewer than
+// min(k, its causal keys) sends its item to a second launch, which recomputes the item's
+// rows without speculation.  Rows with fewer than kSpecMinKeys causal keys never speculate.
+constexpr float kSpecMargin = 0.6f;
+constexpr int kSpecMinKeys = 8192;
+
 struct FusedParams {
   IndexerArgs a;
   int k, cap, S, seg_len, nqb, n_items;
+  int pass;             // 0: every item, speculative thresholds; 1: the failed items, exact
+  int* fail_count;      // items recorded by pass 0
+  int* fail_items;      // [n_items * 8]: one entry per failing token (repeats are harmless)
+  int* counter2;        // work counter of pass 1
   int32_t* idx;
   uint32_t* row_keys;   // [grid * TQ * cap]
   uint32_t* row_pos;
@@ -811,16 +829,31 @@ void indexer_topk_kernel(FusedParams P) {
   __shared__ uint32_t stg_key[TQ][kStage];
   __shared__ uint32_t stg_pos[TQ][kStage];
   __shared__ int item_sh;
+  __shared__ uint32_t spec_sh, item_min_sh;   // previous item's smallest k-th key; this item's
 
   const IndexerArgs& a = P.a;
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int wv_id = uniform((int)(threadIdx.x >> 6));
   const bool fp8 = (DT == DSA_FP8_E4M3);
 
+  if (threadIdx.x == 0) item_min_sh = 0xFFFFFFFFu;
   for (;;) {
-    if (threadIdx.x == 0) item_sh = atomicAdd(P.counter, 1);
+    __syncthreads();   // every wave is done with the previous item (its k-th keys recorded)
+    if (threadIdx.x == 0) {
+      int it;
+      if (P.pass == 0) {
+        it = atomicAdd(P.counter, 1);
+      } else {
+        const int j = atomicAdd(P.counter2, 1);
+        it = j < *P.fail_count ? P.fail_items[j] : P.n_items;
+      }
+      item_sh = it;
+      spec_sh = item_min_sh;
+      item_min_sh = 0xFFFFFFFFu;
+    }
     __syncthreads();
     const int item = item_sh;
+    const uint32_t spec_key = spec_sh;
     __syncthreads();
     if (item >= P.n_items) break;
     const int seg = item % P.S;
@@ -890,10 +923,14 @@ void indexer_topk_kernel(FusedParams P) {
     float theta_f[TW];  // the float whose order key is theta (-inf: admit every key)
     uint32_t* rk[TW];
     uint32_t* rp[TW];
+    // speculative start: a positive k-th score of the previous item, one segment per row
+    const float spec_f = (P.pass == 0 && P.S == 1 && spec_key != 0xFFFFFFFFu) ? key_to_float(spec_key) : 0.f;
+    bool spec[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
-      theta[tt] = 0u;
-      theta_f[tt] = -INFINITY;
+      spec[tt] = spec_f > 0.f && p_t[tt] + 1 >= kSpecMinKeys;
+      theta[tt] = spec[tt] ? order_key(spec_f * kSpecMargin) : 0u;
+      theta_f[tt] = spec[tt] ? spec_f * kSpecMargin : -INFINITY;
       scnt[tt] = 0u;
       cnt[tt] = 0u;
       rk[tt] = P.row_keys + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
@@ -960,7 +997,14 @@ void indexer_topk_kernel(FusedParams P) {
     for (int tt = 0; tt < TW; ++tt) {
       const int t = t0 + wv_id * TW + tt;
       if (t >= a.Lq) continue;
-      cnt[tt] = reduce_to_k(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id]);
+      const int n_causal = max(0, min(p_t[tt] + 1, s_hi) - s_lo);
+      if (spec[tt] && cnt[tt] < (uint32_t)min(P.k, n_causal)) {
+        // too few keys passed the speculative threshold: the item is recomputed exactly
+        if (lane == 0) P.fail_items[atomicAdd(P.fail_count, 1)] = item;
+      }
+      uint32_t kth;
+      cnt[tt] = reduce_to_k(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id], kth);
+      if (kth != 0u && lane == 0) atomicMin(&item_min_sh, kth);
       const size_t row = (size_t)b * a.Lq + t;
       if (P.S == 1) {
         int32_t* out = P.idx + row * P.k;
@@ -1007,7 +1051,8 @@ __global__ __launch_bounds__(256) void merge_segments_kernel(uint32_t* seg_keys,
     }
     n += c;
   }
-  n = reduce_to_k(bk, bp, n, (uint32_t)k, hist[wv_id]);
+  uint32_t kth;
+  n = reduce_to_k(bk, bp, n, (uint32_t)k, hist[wv_id], kth);
   int32_t* out = idx + (size_t)row * k;
   for (int j = lane; j < k; j += 64) out[j] = j < (int)n ? (int32_t)bp[j] : -1;
 }
@@ -1141,7 +1186,7 @@ hipError_t launch_paged_rows(const int32_t* idx, int B, int Lq, int k, const Pag
 
 struct FusedPlan {
   int TQ, nqb, S, seg_len, n_items, grid, cap, seg_stride;
-  size_t off_rowbuf, off_seg, off_cnt, total;
+  size_t off_rowbuf, off_seg, off_cnt, off_fail, total;
 };
 
 static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
@@ -1174,6 +1219,9 @@ static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
   off = (off + 255) / 256 * 256;
   p.off_cnt = off;
   if (S > 1) off += (size_t)B * Lq * S * sizeof(int32_t);
+  off = (off + 255) / 256 * 256;
+  p.off_fail = off;                  // failed items of the speculative pass (one segment)
+  if (S == 1) off += (size_t)p.n_items * 8 * sizeof(int32_t);
   p.total = (off + 255) / 256 * 256;
   return p;
 }
@@ -1212,12 +1260,23 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.seg_stride = pl.seg_stride;
   P.seg_pos = P.seg_keys + (size_t)a.B * a.Lq * pl.seg_stride;
   P.seg_cnt = reinterpret_cast<int32_t*>(w8 + pl.off_cnt);
-  P.counter = reinterpret_cast<int*>(w8);
-  zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 1);
+  P.counter = reinterpret_cast<int*>(w8);      // [0] work counter, [1] pass-1 counter, [2] failures
+  P.counter2 = P.counter + 1;
+  P.fail_count = P.counter + 2;
+  P.fail_items = reinterpret_cast<int*>(w8 + pl.off_fail);
+  P.pass = 0;
+  zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 3);
   if (a.dtype == DSA_BF16) fused_dispatch<DSA_BF16>(P, pl.grid, a.H_I / 16, s);
   else fused_dispatch<DSA_FP8_E4M3>(P, pl.grid, a.H_I / 16, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (pl.S == 1) {   // recompute the items whose speculative threshold admitted too few keys
+    P.pass = 1;
+    if (a.dtype == DSA_BF16) fused_dispatch<DSA_BF16>(P, pl.grid, a.H_I / 16, s);
+    else fused_dispatch<DSA_FP8_E4M3>(P, pl.grid, a.H_I / 16, s);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (pl.S > 1) {
     const int rows = a.B * a.Lq;
     merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k, pl.seg_stride, idx);
