@@ -783,13 +783,19 @@ __device__ uint32_t flush_stage(const uint32_t* sk, const uint32_t* sp, uint32_t
   return cnt + n;
 }
 
-// Speculative starting threshold (one key segment per row only).  A row of the item a
-// workgroup processes next starts its filter at kSpecMargin times the smallest k-th score
-// of the workgroup's previous item instead of admitting every key.  If at least k keys pass
-// a threshold, the row's k-th largest key passes it, so the exact selection over the
-// admitted keys is the row's top-k (ties included).  A row that admits fewer than
+// Speculative starting threshold.  A row of the item a workgroup processes next starts its
+// filter at kSpecMargin times the smallest k-th score of the workgroup's previous item
+// instead of admitting every key.  If at least k keys of a row pass a threshold, the row's
+// k-th largest key passes it, so the exact selection over the admitted keys is the row's
+// top-k (ties included).  With one key segment per row, a row that admits fewer than
 // min(k, its causal keys) sends its item to a second launch, which recomputes the item's
-// rows without speculation.  Rows with fewer than kSpecMinKeys causal keys never speculate.
+// rows without speculation.  With several key segments, a row's segments are separate
+// items started from different thresholds; the merge takes the largest of them, Theta, and
+// accepts the row only if at least min(k, its causal keys) of its list entries exceed
+// Theta (then the row's k-th key exceeds every segment's threshold, so each top-k key was
+// admitted in its segment); otherwise it sends every segment item of the row's query
+// block to the second launch.  Rows with fewer than kSpecMinKeys causal keys never
+// speculate.
 constexpr float kSpecMargin = 0.6f;
 constexpr int kSpecMinKeys = 8192;
 
@@ -800,6 +806,7 @@ struct FusedParams {
   int* fail_count;      // items recorded by pass 0
   int* fail_items;      // [n_items * 8]: one entry per failing token (repeats are harmless)
   int* counter2;        // work counter of pass 1
+  uint32_t* seg_spec;   // [B * Lq * S] starting threshold (order key, 0: none) of each segment (S > 1)
   int32_t* idx;
   uint32_t* row_keys;   // [grid * TQ * cap]
   uint32_t* row_pos;
@@ -924,7 +931,7 @@ void indexer_topk_kernel(FusedParams P) {
     uint32_t* rk[TW];
     uint32_t* rp[TW];
     // speculative start: a positive k-th score of the previous item, one segment per row
-    const float spec_f = (P.pass == 0 && P.S == 1 && spec_key != 0xFFFFFFFFu) ? key_to_float(spec_key) : 0.f;
+    const float spec_f = (P.pass == 0 && spec_key != 0xFFFFFFFFu) ? key_to_float(spec_key) : 0.f;
     bool spec[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
@@ -998,7 +1005,7 @@ void indexer_topk_kernel(FusedParams P) {
       const int t = t0 + wv_id * TW + tt;
       if (t >= a.Lq) continue;
       const int n_causal = max(0, min(p_t[tt] + 1, s_hi) - s_lo);
-      if (spec[tt] && cnt[tt] < (uint32_t)min(P.k, n_causal)) {
+      if (P.S == 1 && spec[tt] && cnt[tt] < (uint32_t)min(P.k, n_causal)) {
         // too few keys passed the speculative threshold: the item is recomputed exactly
         if (lane == 0) P.fail_items[atomicAdd(P.fail_count, 1)] = item;
       }
@@ -1016,7 +1023,10 @@ void indexer_topk_kernel(FusedParams P) {
           ok[j] = rk[tt][j];
           op[j] = rp[tt][j];
         }
-        if (lane == 0) P.seg_cnt[row * P.S + seg] = (int32_t)cnt[tt];
+        if (lane == 0) {
+          P.seg_cnt[row * P.S + seg] = (int32_t)cnt[tt];
+          P.seg_spec[row * P.S + seg] = spec[tt] ? order_key(spec_f * kSpecMargin) : 0u;
+        }
       }
     }
   }
@@ -1024,17 +1034,35 @@ void indexer_topk_kernel(FusedParams P) {
 
 // Merge of per-segment top-k lists (segments are in position order, so their
 // concatenation is in ascending position order).  One wave per query row.
+// Speculation check of the merge (mode 1, after the first fused launch): a row whose
+// segment lists hold fewer than min(k, its causal keys) entries is flagged, and every
+// segment item of its query block is recorded for the second fused launch; mode 2 (after
+// it) merges only the flagged rows.
+struct MergeSpec {
+  int mode;             // 1: check and record failures; 2: flagged rows only
+  int Lq, Lk, nqb, TQ;
+  const uint32_t* seg_spec;
+  int* fail_count;
+  int* fail_items;
+  int* row_flag;        // [rows], zeroed before mode 1
+};
+
 __global__ __launch_bounds__(256) void merge_segments_kernel(uint32_t* seg_keys, uint32_t* seg_pos,
                                                              const int32_t* seg_cnt, int rows, int S, int k, int stride,
-                                                             int32_t* idx) {
+                                                             int32_t* idx, MergeSpec M) {
   __shared__ uint32_t hist[4][kBins];
   const int lane = threadIdx.x & 63, wv_id = threadIdx.x >> 6;
   const int row = blockIdx.x * 4 + wv_id;
   if (row >= rows) return;
+  if (M.mode == 2 && M.row_flag[row] == 0) return;
+  uint32_t theta_max = 0;   // largest starting threshold among the row's segments
+  if (M.mode == 1)
+    for (int sg = 0; sg < S; ++sg) theta_max = max(theta_max, M.seg_spec[(size_t)row * S + sg]);
   uint32_t* bk = seg_keys + (size_t)row * stride;
   uint32_t* bp = seg_pos + (size_t)row * stride;
-  // pack the lists contiguously at the start of the row's region (moves only downwards)
-  uint32_t n = 0;
+  // pack the lists contiguously at the start of the row's region (moves only downwards),
+  // counting the entries above theta_max
+  uint32_t n = 0, above = 0;
   for (int sg = 0; sg < S; ++sg) {
     const uint32_t c = (uint32_t)seg_cnt[(size_t)row * S + sg];
     for (uint32_t j0 = 0; j0 < c; j0 += 64) {
@@ -1048,8 +1076,22 @@ __global__ __launch_bounds__(256) void merge_segments_kernel(uint32_t* seg_keys,
         bk[n + j] = kk;
         bp[n + j] = pp;
       }
+      above += (uint32_t)popc64(ballot(j < c && kk > theta_max));
     }
     n += c;
+  }
+  if (M.mode == 1 && theta_max != 0u) {
+    const int n_causal = M.Lk - M.Lq + (row % M.Lq) + 1;
+    if (above < (uint32_t)min(k, n_causal)) {
+      // a top-k key may lie below some segment's threshold: recompute the row's block
+      if (lane == 0) {
+        M.row_flag[row] = 1;
+        const int b = row / M.Lq, qb = (row % M.Lq) / M.TQ;
+        const int r = b * M.nqb + (M.nqb - 1 - qb);
+        for (int sg = 0; sg < S; ++sg) M.fail_items[atomicAdd(M.fail_count, 1)] = r * S + sg;
+      }
+      return;
+    }
   }
   uint32_t kth;
   n = reduce_to_k(bk, bp, n, (uint32_t)k, hist[wv_id], kth);
@@ -1186,7 +1228,7 @@ hipError_t launch_paged_rows(const int32_t* idx, int B, int Lq, int k, const Pag
 
 struct FusedPlan {
   int TQ, nqb, S, seg_len, n_items, grid, cap, seg_stride;
-  size_t off_rowbuf, off_seg, off_cnt, off_fail, total;
+  size_t off_rowbuf, off_seg, off_cnt, off_fail, off_flag, total;
 };
 
 static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
@@ -1218,10 +1260,13 @@ static FusedPlan plan_fused(int B, int Lq, int Lk, int k, int dtype) {
   if (S > 1) off += (size_t)B * Lq * p.seg_stride * sizeof(uint32_t) * 2;
   off = (off + 255) / 256 * 256;
   p.off_cnt = off;
-  if (S > 1) off += (size_t)B * Lq * S * sizeof(int32_t);
+  if (S > 1) off += (size_t)B * Lq * S * sizeof(int32_t) * 2;   // counts, then starting thresholds
   off = (off + 255) / 256 * 256;
-  p.off_fail = off;                  // failed items of the speculative pass (one segment)
-  if (S == 1) off += (size_t)p.n_items * 8 * sizeof(int32_t);
+  p.off_fail = off;                  // failed items of the speculative pass, then row flags
+  off += (size_t)p.n_items * 8 * sizeof(int32_t);
+  off = (off + 255) / 256 * 256;
+  p.off_flag = off;
+  if (S > 1) off += (size_t)B * Lq * sizeof(int32_t);
   p.total = (off + 255) / 256 * 256;
   return p;
 }
@@ -1265,23 +1310,32 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.fail_count = P.counter + 2;
   P.fail_items = reinterpret_cast<int*>(w8 + pl.off_fail);
   P.pass = 0;
+  const int rows = a.B * a.Lq;
+  P.seg_spec = reinterpret_cast<uint32_t*>(P.seg_cnt + (size_t)a.B * a.Lq * pl.S);
+  MergeSpec M{1, a.Lq, a.Lk, pl.nqb, pl.TQ, P.seg_spec, P.fail_count, P.fail_items,
+              reinterpret_cast<int*>(w8 + pl.off_flag)};
   zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 3);
-  if (a.dtype == DSA_BF16) fused_dispatch<DSA_BF16>(P, pl.grid, a.H_I / 16, s);
-  else fused_dispatch<DSA_FP8_E4M3>(P, pl.grid, a.H_I / 16, s);
   hipError_t e = hipGetLastError();
+  if (e == hipSuccess && pl.S > 1) e = launch_zero(M.row_flag, (size_t)rows * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
-  if (pl.S == 1) {   // recompute the items whose speculative threshold admitted too few keys
-    P.pass = 1;
+  auto fused = [&]() {
     if (a.dtype == DSA_BF16) fused_dispatch<DSA_BF16>(P, pl.grid, a.H_I / 16, s);
     else fused_dispatch<DSA_FP8_E4M3>(P, pl.grid, a.H_I / 16, s);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (pl.S > 1) {
-    const int rows = a.B * a.Lq;
-    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k, pl.seg_stride, idx);
-    e = hipGetLastError();
-  }
+    return hipGetLastError();
+  };
+  auto merge = [&](int mode) {
+    M.mode = mode;
+    merge_segments_kernel<<<(rows + 3) / 4, 256, 0, s>>>(P.seg_keys, P.seg_pos, P.seg_cnt, rows, pl.S, k,
+                                                         pl.seg_stride, idx, M);
+    return hipGetLastError();
+  };
+  // pass 0 (speculative thresholds), the merge's check when the keys are segmented, pass 1
+  // over the recorded items (exact), and the merge of the rows it recomputed
+  e = fused();
+  if (e == hipSuccess && pl.S > 1) e = merge(1);
+  P.pass = 1;
+  if (e == hipSuccess) e = fused();
+  if (e == hipSuccess && pl.S > 1) e = merge(2);
   return e;
 }
 

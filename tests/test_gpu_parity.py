@@ -149,6 +149,7 @@ FUSED_CASES = [
     # threshold taken from the workgroup's previous item
     ("fp8", 1, 20000, 20000, 256),
     ("bf16", 1, 12000, 12000, 512),
+    ("fp8", 1, 2048, 65536, 256),      # 8 key segments, 2048 items: checked by the merge
 ]
 
 
@@ -165,24 +166,26 @@ def test_fused_topk_equals_scores_then_topk(dtype, B, Lq, Lk, k):
     assert torch.equal(idx, idx2)                                     # run twice: identical
 
 
-@pytest.mark.parametrize("dtype,L,k", [("fp8", 20000, 256), ("bf16", 12000, 512)])
-def test_fused_topk_speculation_failures_are_recomputed(dtype, L, k):
+@pytest.mark.parametrize("dtype,Lq,L,k", [("fp8", 20000, 20000, 256), ("bf16", 12000, 12000, 512),
+                                          ("fp8", 2048, 65536, 256)])
+def test_fused_topk_speculation_failures_are_recomputed(dtype, Lq, L, k):
     """Blocks of consecutive queries get score scales of 100 or 1/100 at random, so a
     threshold carried over from a workgroup's previous item is often far too high: those
     rows admit fewer than k keys and the second pass recomputes their items.  The result
-    must still equal dsa_topk(dsa_indexer_scores) bit for bit."""
-    cfg = _cfg(dtype, L, k, Lq=L, B=1)
+    must still equal dsa_topk(dsa_indexer_scores) bit for bit (with key segments the merge
+    finds the failing rows)."""
+    cfg = _cfg(dtype, L, k, Lq=Lq, B=1)
     ind = synth.indexer_inputs(cfg, device=DEV)
     rng = np.random.default_rng(13)
-    f = torch.from_numpy(np.repeat(rng.choice([0.01, 1.0, 100.0], L // 8 + 1), 8)[:L].astype(np.float32)).to(DEV)
+    f = torch.from_numpy(np.repeat(rng.choice([0.01, 1.0, 100.0], Lq // 8 + 1), 8)[:Lq].astype(np.float32)).to(DEV)
     if dtype == "fp8":
         ind["q_scale"] = (ind["q_scale"] * f[None]).contiguous()
     else:
         ind["w"] = (ind["w"] * f[None, :, None]).contiguous()
     idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
     sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind))
-    nv = torch.arange(1, L + 1, device=DEV, dtype=torch.int32)
-    assert torch.equal(idx, dsa.topk(sc.reshape(L, L), k, n_valid=nv).reshape(1, L, k))
+    nv = torch.arange(L - Lq + 1, L + 1, device=DEV, dtype=torch.int32)
+    assert torch.equal(idx, dsa.topk(sc.reshape(Lq, L), k, n_valid=nv).reshape(1, Lq, k))
 
 
 @pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES[:5] + FUSED_CASES[6:7])
