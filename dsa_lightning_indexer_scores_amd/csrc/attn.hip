@@ -354,17 +354,6 @@ constexpr int kBlk2 = 32;                        // keys per block
 constexpr int kBlk2Bytes = 2 * kBlkBytes;        // 36864
 constexpr int kDmaPerBlk2 = kBlk2Bytes / 1024;   // 36 wave-wide 1 KB direct-to-LDS loads
 
-// s_waitcnt vmcnt(m) for the largest m <= n in [0, C] (n is wave-uniform); waiting for
-// fewer outstanding loads than n is always safe.
-template <int C>
-__device__ __forceinline__ void wait_vm_at_most(int n) {
-  if constexpr (C == 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    if (n >= C) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C) : "memory");
-    else wait_vm_at_most<C - 1>(n);
-  }
-}
 
 // NB = latent row buffers: block j is computed from buffer j % NB while the rows of
 // blocks j+1 .. j+NB-1 are in flight.  NB = 2 leaves room for two workgroups per CU (the

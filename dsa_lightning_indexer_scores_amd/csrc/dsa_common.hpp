@@ -113,6 +113,20 @@ __device__ __forceinline__ void dma_4(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory");
 }
 
+// s_waitcnt vmcnt(m) for the largest m <= n in [0, C] (n is wave-uniform); waiting for
+// fewer outstanding loads than n is always safe.  Vector memory loads complete in issue
+// order, so vmcnt(n) with n = the loads issued after a group means that group has landed
+// (stores issued in between only raise the count, which waits longer).
+template <int C>
+__device__ __forceinline__ void wait_vm_at_most(int n) {
+  if constexpr (C == 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    if (n >= C) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(C) : "memory");
+    else wait_vm_at_most<C - 1>(n);
+  }
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();

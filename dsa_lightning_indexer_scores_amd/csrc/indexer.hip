@@ -18,6 +18,7 @@
 // already held).  When the buffer nears capacity the wave radix-selects the k-th key,
 // sets theta to it and compacts the buffer in place, keeping positions in order and
 // the lowest positions among keys equal to theta.
+#include <type_traits>
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
 #include "../../include/dsa.h"
@@ -106,6 +107,14 @@ __device__ __forceinline__ f32x4 dot16<DSA_BF16>(const Op<DSA_BF16>& a, const Op
   return c;
 }
 
+// ReLU as one integer max of the bit pattern: a float with its sign bit set is a negative
+// int32, and non-negative floats order like their bit patterns.  Equal to fmaxf(x, 0) for
+// every non-NaN x (-0 gives +0); fmaxf itself costs a second instruction that quiets
+// signalling NaNs first.
+__device__ __forceinline__ float relu_bits(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // Scores of TW tokens against a 64-key tile.  a[tt][hb]: token tt's heads
 // 16hb..16hb+15; b[kb]: keys 16kb..16kb+15 of the tile; wv[tt][hb][i] = w'[16hb + 4g + i].
 // Returns, in lane l of out[tt], sum_j w'_j ReLU(q_j . k_{s0+l}) (before the fp8 key
@@ -132,10 +141,10 @@ __device__ __forceinline__ void tile_scores(const Op<DT> (&a)[TW][HB], const Op<
       float acc = 0.f;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        acc = fmaf(wv[tt][hb][0], fmaxf(d[kb][tt][hb][0], 0.f), acc);
-        acc = fmaf(wv[tt][hb][1], fmaxf(d[kb][tt][hb][1], 0.f), acc);
-        acc = fmaf(wv[tt][hb][2], fmaxf(d[kb][tt][hb][2], 0.f), acc);
-        acc = fmaf(wv[tt][hb][3], fmaxf(d[kb][tt][hb][3], 0.f), acc);
+        acc = fmaf(wv[tt][hb][0], relu_bits(d[kb][tt][hb][0]), acc);
+        acc = fmaf(wv[tt][hb][1], relu_bits(d[kb][tt][hb][1]), acc);
+        acc = fmaf(wv[tt][hb][2], relu_bits(d[kb][tt][hb][2]), acc);
+        acc = fmaf(wv[tt][hb][3], relu_bits(d[kb][tt][hb][3]), acc);
       }
       p[tt][kb] = acc;
     }
@@ -769,23 +778,34 @@ __device__ uint32_t shrink_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint3
 // ---------------------------------------------------------------------------
 constexpr int kStage = 256;   // staged candidates per token before a bulk append
 
-// Appends the n staged candidates (LDS, in position order) to the global list after its
-// cnt entries; returns the new count.
-__device__ uint32_t flush_stage(const uint32_t* sk, const uint32_t* sp, uint32_t n, uint32_t* keys,
-                                uint32_t* pos, uint32_t cnt) {
-  const int lane = lane_id();
+// Appends the n <= kStage staged candidates (LDS, in position order; each the score's
+// float bits and its position) to the global list after its cnt entries, as order keys;
+// returns the new count.  All reads are issued before the first store.
+__device__ uint32_t flush_stage(const uint2* st, uint32_t n, uint32_t* keys, uint32_t* pos, uint32_t cnt) {
+  const uint32_t lane = (uint32_t)lane_id();
   wave_lds_fence();
-  for (uint32_t j = lane; j < n; j += 64) {
-    keys[cnt + j] = sk[j];
-    pos[cnt + j] = sp[j];
+  uint2 e[kStage / 64];
+#pragma unroll
+  for (int u = 0; u < kStage / 64; ++u)
+    if (lane + 64u * u < n) e[u] = st[lane + 64u * u];
+#pragma unroll
+  for (int u = 0; u < kStage / 64; ++u) {
+    const uint32_t j = lane + 64u * u;
+    if (j < n) {
+      keys[cnt + j] = order_key(__uint_as_float(e[u].x));
+      pos[cnt + j] = e[u].y;
+    }
   }
   wave_lds_fence();  // the stage is refilled only after these reads
   return cnt + n;
 }
 
-// Speculative starting threshold.  A row of the item a workgroup processes next starts its
-// filter at kSpecMargin times the smallest k-th score of the workgroup's previous item
-// instead of admitting every key.  If at least k keys of a row pass a threshold, the row's
+// Speculative starting threshold.  Before its main pass, an item scores a sample of
+// kSampleTiles key tiles spread over the keys that are causal for all its tokens, and each
+// token starts its filter at the j-th largest of its m = 64 kSampleTiles sample keys
+// instead of admitting every key, with j = mu + 4 sqrt(mu) + 1 and mu = m k / n the number
+// of sample keys expected above the k-th of the token's n causal keys (about twice k keys
+// then pass it).  Whatever the threshold, if at least k keys of a row pass it, the row's
 // k-th largest key passes it, so the exact selection over the admitted keys is the row's
 // top-k (ties included).  With one key segment per row, a row that admits fewer than
 // min(k, its causal keys) sends its item to a second launch, which recomputes the item's
@@ -794,10 +814,11 @@ __device__ uint32_t flush_stage(const uint32_t* sk, const uint32_t* sp, uint32_t
 // accepts the row only if at least min(k, its causal keys) of its list entries exceed
 // Theta (then the row's k-th key exceeds every segment's threshold, so each top-k key was
 // admitted in its segment); otherwise it sends every segment item of the row's query
-// block to the second launch.  Rows with fewer than kSpecMinKeys causal keys never
-// speculate.
-constexpr float kSpecMargin = 0.6f;
+// block to the second launch.  Rows with fewer than kSpecMinKeys causal keys, and items
+// whose common causal keys span fewer than kSampleMinSpan, never speculate.
 constexpr int kSpecMinKeys = 8192;
+constexpr int kSampleTiles = 16;
+constexpr int kSampleMinSpan = 4 * kSampleTiles * 64;
 
 struct FusedParams {
   IndexerArgs a;
@@ -827,23 +848,25 @@ void indexer_topk_kernel(FusedParams P) {
   constexpr int kChunks = RB / 16;                 // 16-byte chunks per key row
   constexpr int kTileBytes = kTileKeys * RB;
   constexpr int kDmaPerWave = kTileBytes / 1024 / 4;
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileBytes];
-  __shared__ __attribute__((aligned(16))) float kscl[2][kTileKeys];
+  // Key tile ring: tile t is scored from buffer t % kBufs while the next kBufs - 1 tiles
+  // load.  Three buffers (two tiles in flight) for fp8 keys; bf16 tiles are twice the
+  // size and keep two, which leaves room for two workgroups per CU.
+  constexpr int kBufs = (DT == DSA_FP8_E4M3) ? 3 : 2;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[kBufs][kTileBytes];
+  __shared__ __attribute__((aligned(16))) float kscl[kBufs][kTileKeys];
   __shared__ __attribute__((aligned(16))) float wsh[TQ * H_I];
   __shared__ uint32_t hist[4][kBins];
-  // per-token staging of admitted candidates: appends are LDS writes, and the global
-  // list receives them in bulk (tile loads then never wait for candidate stores)
-  __shared__ uint32_t stg_key[TQ][kStage];
-  __shared__ uint32_t stg_pos[TQ][kStage];
+  // per-token staging of admitted candidates (score bits, position): appends are LDS
+  // writes, and the global list receives them in bulk, as order keys (tile loads then
+  // never wait for candidate stores)
+  __shared__ __attribute__((aligned(8))) uint2 stg[TQ][kStage];
   __shared__ int item_sh;
-  __shared__ uint32_t spec_sh, item_min_sh;   // previous item's smallest k-th key; this item's
 
   const IndexerArgs& a = P.a;
   const int lane = threadIdx.x & 63, g = lane >> 4;
   const int wv_id = uniform((int)(threadIdx.x >> 6));
   const bool fp8 = (DT == DSA_FP8_E4M3);
 
-  if (threadIdx.x == 0) item_min_sh = 0xFFFFFFFFu;
   for (;;) {
     __syncthreads();   // every wave is done with the previous item (its k-th keys recorded)
     if (threadIdx.x == 0) {
@@ -855,12 +878,9 @@ void indexer_topk_kernel(FusedParams P) {
         it = j < *P.fail_count ? P.fail_items[j] : P.n_items;
       }
       item_sh = it;
-      spec_sh = item_min_sh;
-      item_min_sh = 0xFFFFFFFFu;
     }
     __syncthreads();
     const int item = item_sh;
-    const uint32_t spec_key = spec_sh;
     __syncthreads();
     if (item >= P.n_items) break;
     const int seg = item % P.S;
@@ -890,6 +910,7 @@ void indexer_topk_kernel(FusedParams P) {
       }
       if (fp8 && wv_id == 0) dma_4(kscale + min(s0 + lane, a.Lk - 1), lds_offset(&kscl[buf][0]));
     };
+    const int tile_loads = kDmaPerWave + ((fp8 && wv_id == 0) ? 1 : 0);   // per issue_tile, this wave
 
     // query operands of this wave's tokens (rows past Lq reuse row t0; never appended)
     Op<DT> A[TW][HB];
@@ -930,27 +951,91 @@ void indexer_topk_kernel(FusedParams P) {
     float theta_f[TW];  // the float whose order key is theta (-inf: admit every key)
     uint32_t* rk[TW];
     uint32_t* rp[TW];
-    // speculative start: a positive k-th score of the previous item, one segment per row
-    const float spec_f = (P.pass == 0 && spec_key != 0xFFFFFFFFu) ? key_to_float(spec_key) : 0.f;
     bool spec[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
-      spec[tt] = spec_f > 0.f && p_t[tt] + 1 >= kSpecMinKeys;
-      theta[tt] = spec[tt] ? order_key(spec_f * kSpecMargin) : 0u;
-      theta_f[tt] = spec[tt] ? spec_f * kSpecMargin : -INFINITY;
+      spec[tt] = false;
+      theta[tt] = 0u;
+      theta_f[tt] = -INFINITY;
       scnt[tt] = 0u;
       cnt[tt] = 0u;
       rk[tt] = P.row_keys + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
       rp[tt] = P.row_pos + ((size_t)blockIdx.x * TQ + wv_id * TW + tt) * P.cap;
     }
 
-    if (n_tiles > 0) issue_tile(s_lo, 0);
+    // Sample pass (speculative pass only): tiles at s_lo + j * step, all causal for every
+    // token of the item; the order keys of this wave's tokens go to its histogram area
+    // (TW * 64 * kSampleTiles entries), in the same tile ring as the main pass.
+    const int samp_hi = min(s_hi, a.Lk - a.Lq + t0 + 1);
+    if (P.pass == 0 && samp_hi - s_lo >= kSampleMinSpan) {   // workgroup-uniform
+      const int step = (samp_hi - s_lo - kTileKeys) / (kSampleTiles - 1);
+      uint32_t* skeys = hist[wv_id];
+#pragma unroll
+      for (int u = 0; u < kBufs - 1; ++u) issue_tile(s_lo + u * step, u);
+      int cb = 0;
+      for (int j = 0; j < kSampleTiles; ++j) {
+        if (kBufs == 3 && j + 1 < kSampleTiles) wait_vm_at_most<kDmaPerWave + 1>(tile_loads);
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int nb = cb == 0 ? kBufs - 1 : cb - 1;
+        if (j + kBufs - 1 < kSampleTiles) issue_tile(s_lo + (j + kBufs - 1) * step, nb);
+        Op<DT> Bk[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) Bk[kb] = load_op_tile<DT>(ktile[cb], kb * 16 + (lane & 15), g);
+        const float ks = fp8 ? kscl[cb][lane] : 1.f;
+        float sc[TW];
+        tile_scores<DT, HB, TW>(A, Bk, W, sc);
+#pragma unroll
+        for (int tt = 0; tt < TW; ++tt) skeys[(tt * kSampleTiles + j) * 64 + lane] = order_key(sc[tt] * ks);
+        cb = cb + 1 == kBufs ? 0 : cb + 1;
+      }
+      __syncthreads();   // every wave is done with the ring before the main pass refills it
+      wave_lds_fence();
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt) {
+        const int n = p_t[tt] + 1;   // the token's causal keys (all segments)
+        if (n < kSpecMinKeys) continue;
+        const float mu = (float)(64 * kSampleTiles) * (float)P.k / (float)n;
+        const int jj = (int)ceilf(mu + 4.f * sqrtf(mu) + 1.f);
+        if (jj > 64 * kSampleTiles) continue;
+        uint32_t v[kSampleTiles];
+#pragma unroll
+        for (int q = 0; q < kSampleTiles; ++q) v[q] = skeys[(tt * kSampleTiles + q) * 64 + lane];
+        // the largest 16-bit key prefix with at least jj sample keys at or above it is at
+        // most the jj-th largest sample key
+        uint32_t pre = 0u;
+        for (int bit = 31; bit >= 16; --bit) {
+          const uint32_t cand = pre | (1u << bit);
+          int c = 0;
+#pragma unroll
+          for (int q = 0; q < kSampleTiles; ++q) c += popc64(ballot(v[q] >= cand));
+          if (c >= jj) pre = cand;
+        }
+        // a positive finite threshold only (then val > theta_f is key > theta)
+        if (pre > 0x80000000u && pre < 0xFF800000u) {
+          spec[tt] = true;
+          theta[tt] = pre;
+          theta_f[tt] = key_to_float(pre);
+        }
+      }
+      wave_lds_fence();   // the histogram area is reused by the list selections
+    }
+    uint32_t theta0[TW];   // starting thresholds (recorded for the merge when S > 1)
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) theta0[tt] = theta[tt];
+
+#pragma unroll
+    for (int u = 0; u < kBufs - 1; ++u)
+      if (u < n_tiles) issue_tile(s_lo + u * kTileKeys, u);
+    int cur = 0;   // it % kBufs
     for (int it = 0; it < n_tiles; ++it) {
       const int s0 = s_lo + it * kTileKeys;
-      const int cur = it & 1;
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this tile has landed
-      __syncthreads();                                     // ... for every wave; other buffer free
-      if (it + 1 < n_tiles) issue_tile(s0 + kTileKeys, cur ^ 1);
+      // this tile has landed (the loads of the later tiles already issued may be pending)
+      if (kBufs == 3 && it + 1 < n_tiles) wait_vm_at_most<kDmaPerWave + 1>(tile_loads);
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // ... for every wave; the buffer of tile it - 1 is free
+      const int nxt = cur == 0 ? kBufs - 1 : cur - 1;   // (it + kBufs - 1) % kBufs
+      if (it + kBufs - 1 < n_tiles) issue_tile(s0 + (kBufs - 1) * kTileKeys, nxt);
 
       Op<DT> Bk[4];
 #pragma unroll
@@ -958,47 +1043,58 @@ void indexer_topk_kernel(FusedParams P) {
       const float ks = fp8 ? kscl[cur][lane] : 1.f;
       const int s = s0 + lane;
 
-      int p_last = p_t[0];
+      int p_last = p_t[0], p_first = p_t[0];   // the wave's largest / smallest causal end
 #pragma unroll
-      for (int tt = 1; tt < TW; ++tt) p_last = max(p_last, p_t[tt]);
-      if (p_last < s0) continue;  // wave-uniform: every token past its causal range / absent
+      for (int tt = 1; tt < TW; ++tt) {
+        p_last = max(p_last, p_t[tt]);
+        p_first = min(p_first, p_t[tt]);
+      }
+      if (p_last < s0) {   // wave-uniform: every token past its causal range / absent
+        cur = cur + 1 == kBufs ? 0 : cur + 1;
+        continue;
+      }
       float sc[TW];
       tile_scores<DT, HB, TW>(A, Bk, W, sc);
+      // Admission: val > theta_f is key > theta (the order-key map is strictly increasing
+      // on floats with -0 = +0).  Positions are checked only in a tile that crosses a
+      // token's causal edge or the segment end (a separate copy of the loop body, so the
+      // other tiles carry no masking).
+      auto admit = [&](auto edge_tag) {
+        constexpr bool kEdge = decltype(edge_tag)::value;
+#pragma unroll
+        for (int tt = 0; tt < TW; ++tt) {
+          if (p_t[tt] < s0) continue;  // wave-uniform: token past its causal range / absent
+          const float val = sc[tt] * ks;
+          bool pred = val > theta_f[tt];
+          if constexpr (kEdge) pred = pred && (s <= p_t[tt]) && (s < s_hi);
+          const uint64_t m = ballot(pred);
+          if (m) {
+            if (pred) stg[wv_id * TW + tt][scnt[tt] + rank_below(m)] = make_uint2(__float_as_uint(val), (uint32_t)s);
+            scnt[tt] += popc64(m);
+          }
+        }
+      };
+      if (s0 + kTileKeys - 1 > p_first || s0 + kTileKeys > s_hi) admit(std::true_type{});
+      else admit(std::false_type{});
 #pragma unroll
       for (int tt = 0; tt < TW; ++tt) {
-        if (p_t[tt] < s0) continue;  // wave-uniform: token past its causal range / absent
-        const float val = sc[tt] * ks;
-        // val > theta_f is key > theta (the order-key map is strictly increasing on
-        // floats with -0 = +0); positions are checked only in a tile that crosses the
-        // causal edge or the segment end
-        bool pred = val > theta_f[tt];
-        if (s0 + kTileKeys - 1 > p_t[tt] || s0 + kTileKeys > s_hi) pred = pred && (s <= p_t[tt]) && (s < s_hi);
-        const uint64_t m = ballot(pred);
-        if (m) {
-          uint32_t* sk = stg_key[wv_id * TW + tt];
-          uint32_t* sp = stg_pos[wv_id * TW + tt];
-          if (pred) {
-            sk[scnt[tt] + rank_below(m)] = order_key(val);
-            sp[scnt[tt] + rank_below(m)] = (uint32_t)s;
-          }
-          scnt[tt] += popc64(m);
-          if (scnt[tt] > (uint32_t)(kStage - kTileKeys)) {
-            cnt[tt] = flush_stage(sk, sp, scnt[tt], rk[tt], rp[tt], cnt[tt]);
-            scnt[tt] = 0;
-            if (cnt[tt] > (uint32_t)(P.cap - kStage)) {
-              cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
-                                    hist[wv_id], theta[tt]);
-              theta_f[tt] = key_to_float(theta[tt]);
-            }
+        if (scnt[tt] > (uint32_t)(kStage - kTileKeys)) {
+          cnt[tt] = flush_stage(stg[wv_id * TW + tt], scnt[tt], rk[tt], rp[tt], cnt[tt]);
+          scnt[tt] = 0;
+          if (cnt[tt] > (uint32_t)(P.cap - kStage)) {
+            cnt[tt] = shrink_list(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, (uint32_t)(P.cap + P.k) / 2,
+                                  hist[wv_id], theta[tt]);
+            theta_f[tt] = key_to_float(theta[tt]);
           }
         }
       }
+      cur = cur + 1 == kBufs ? 0 : cur + 1;
     }
 
     // finalize this wave's rows
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt)
-      cnt[tt] = flush_stage(stg_key[wv_id * TW + tt], stg_pos[wv_id * TW + tt], scnt[tt], rk[tt], rp[tt], cnt[tt]);
+      cnt[tt] = flush_stage(stg[wv_id * TW + tt], scnt[tt], rk[tt], rp[tt], cnt[tt]);
     __threadfence_block();
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
@@ -1011,7 +1107,6 @@ void indexer_topk_kernel(FusedParams P) {
       }
       uint32_t kth;
       cnt[tt] = reduce_to_k(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id], kth);
-      if (kth != 0u && lane == 0) atomicMin(&item_min_sh, kth);
       const size_t row = (size_t)b * a.Lq + t;
       if (P.S == 1) {
         int32_t* out = P.idx + row * P.k;
@@ -1025,7 +1120,7 @@ void indexer_topk_kernel(FusedParams P) {
         }
         if (lane == 0) {
           P.seg_cnt[row * P.S + seg] = (int32_t)cnt[tt];
-          P.seg_spec[row * P.S + seg] = spec[tt] ? order_key(spec_f * kSpecMargin) : 0u;
+          P.seg_spec[row * P.S + seg] = spec[tt] ? theta0[tt] : 0u;
         }
       }
     }

@@ -145,8 +145,8 @@ FUSED_CASES = [
     ("bf16", 2, 4, 9000, 512),
     ("fp8", 2, 15, 3000, 2048),        # rows shorter and longer than k
     ("fp8", 1, 1, 100, 64),            # one chunk
-    # more work items than persistent workgroups: later items start from a speculative
-    # threshold taken from the workgroup's previous item
+    # more work items than persistent workgroups; long rows start from a speculative
+    # threshold estimated from a sample of the item's keys
     ("fp8", 1, 20000, 20000, 256),
     ("bf16", 1, 12000, 12000, 512),
     ("fp8", 1, 2048, 65536, 256),      # 8 key segments, 2048 items: checked by the merge
@@ -166,26 +166,31 @@ def test_fused_topk_equals_scores_then_topk(dtype, B, Lq, Lk, k):
     assert torch.equal(idx, idx2)                                     # run twice: identical
 
 
-@pytest.mark.parametrize("dtype,Lq,L,k", [("fp8", 20000, 20000, 256), ("bf16", 12000, 12000, 512),
-                                          ("fp8", 2048, 65536, 256)])
+@pytest.mark.parametrize("dtype,Lq,L,k", [("fp8", 20000, 20000, 256), ("bf16", 12000, 12000, 256),
+                                          ("fp8", 2048, 65536, 2048)])
 def test_fused_topk_speculation_failures_are_recomputed(dtype, Lq, L, k):
-    """Blocks of consecutive queries get score scales of 100 or 1/100 at random, so a
-    threshold carried over from a workgroup's previous item is often far too high: those
-    rows admit fewer than k keys and the second pass recomputes their items.  The result
-    must still equal dsa_topk(dsa_indexer_scores) bit for bit (with key segments the merge
-    finds the failing rows)."""
+    """About one 64-key block in 64 gets a score scale of 100.  The rows hold too few such
+    hot keys to fill their top k, so an item whose sample tiles meet a hot block starts its
+    rows from a threshold far above their k-th score: they admit fewer than k keys and the
+    second pass recomputes the item (with key segments the merge finds the failing rows).
+    The launch must have recorded failures (the workspace's third int32 counts them), and
+    the result must still equal dsa_topk(dsa_indexer_scores) bit for bit."""
     cfg = _cfg(dtype, L, k, Lq=Lq, B=1)
     ind = synth.indexer_inputs(cfg, device=DEV)
     rng = np.random.default_rng(13)
-    f = torch.from_numpy(np.repeat(rng.choice([0.01, 1.0, 100.0], Lq // 8 + 1), 8)[:Lq].astype(np.float32)).to(DEV)
+    hot = np.repeat(np.where(rng.random(L // 64 + 1) < 1 / 64, 100.0, 1.0), 64)[:L].astype(np.float32)
+    f = torch.from_numpy(hot).to(DEV)
     if dtype == "fp8":
-        ind["q_scale"] = (ind["q_scale"] * f[None]).contiguous()
+        ind["k_scale"] = (ind["k_scale"] * f[None]).contiguous()
     else:
-        ind["w"] = (ind["w"] * f[None, :, None]).contiguous()
-    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+        ind["k"] = (ind["k"].float() * f[None, :, None]).to(torch.bfloat16).contiguous()
+    ws = dsa.Workspace()
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, ws=ws, **_ind_args(ind))
+    fails = int(ws.buf[8:12].view(torch.int32).item())
     sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind))
     nv = torch.arange(L - Lq + 1, L + 1, device=DEV, dtype=torch.int32)
     assert torch.equal(idx, dsa.topk(sc.reshape(Lq, L), k, n_valid=nv).reshape(1, Lq, k))
+    assert fails > 0
 
 
 @pytest.mark.parametrize("dtype,B,Lq,Lk,k", FUSED_CASES[:5] + FUSED_CASES[6:7])
