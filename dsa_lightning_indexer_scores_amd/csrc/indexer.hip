@@ -803,9 +803,9 @@ __device__ uint32_t flush_stage(const uint2* st, uint32_t n, uint32_t* keys, uin
 // Speculative starting threshold.  Before its main pass, an item scores a sample of
 // kSampleTiles key tiles spread over the keys that are causal for all its tokens, and each
 // token starts its filter at the j-th largest of its m = 64 kSampleTiles sample keys
-// instead of admitting every key, with j = mu + 4 sqrt(mu) + 1 and mu = m k / n the number
+// instead of admitting every key, with j = mu + z sqrt(mu) + 1 and mu = m k / n the number
 // of sample keys expected above the k-th of the token's n causal keys (about twice k keys
-// then pass it).  Whatever the threshold, if at least k keys of a row pass it, the row's
+// then pass it); z = 4, or 6 with key segments.  Whatever the threshold, if at least k keys of a row pass it, the row's
 // k-th largest key passes it, so the exact selection over the admitted keys is the row's
 // top-k (ties included).  With one key segment per row, a row that admits fewer than
 // min(k, its causal keys) sends its item to a second launch, which recomputes the item's
@@ -835,7 +835,7 @@ struct FusedParams {
   uint32_t* seg_keys;   // [B * Lq * seg_stride]   (S > 1)
   uint32_t* seg_pos;
   int32_t* seg_cnt;     // [B * Lq * S]
-  int* counter;
+  int* counter;         // work counters (the launch zeroes 16 ints)
 };
 
 template <int DT, int HB>
@@ -871,7 +871,24 @@ void indexer_topk_kernel(FusedParams P) {
     __syncthreads();   // every wave is done with the previous item (its k-th keys recorded)
     if (threadIdx.x == 0) {
       int it;
-      if (P.pass == 0) {
+      if (P.pass == 0 && P.S > 1) {
+        // XCD-local queues: the items, ordered by (segment, query block), are cut into
+        // eight ranges, and a workgroup takes items from the range of its XCD (workgroups
+        // are dealt to the eight XCDs round-robin), so the workgroups sharing an L2 stream
+        // the same segment's keys together; an exhausted range sends it to the others.
+        const int rows_s = P.n_items / P.S;
+        it = P.n_items;
+        for (int v = 0; v < 8; ++v) {
+          const int x = (int)((blockIdx.x + v) & 7);
+          const int lo = (int)((long long)P.n_items * x / 8), hi = (int)((long long)P.n_items * (x + 1) / 8);
+          const int j = atomicAdd(P.counter + 8 + x, 1);
+          if (lo + j < hi) {
+            const int i = lo + j;
+            it = (i % rows_s) * P.S + i / rows_s;
+            break;
+          }
+        }
+      } else if (P.pass == 0) {
         it = atomicAdd(P.counter, 1);
       } else {
         const int j = atomicAdd(P.counter2, 1);
@@ -996,7 +1013,9 @@ void indexer_topk_kernel(FusedParams P) {
         const int n = p_t[tt] + 1;   // the token's causal keys (all segments)
         if (n < kSpecMinKeys) continue;
         const float mu = (float)(64 * kSampleTiles) * (float)P.k / (float)n;
-        const int jj = (int)ceilf(mu + 4.f * sqrtf(mu) + 1.f);
+        // margin: 4 standard deviations, 6 when the merge takes the largest of a row's
+        // segment thresholds (a failing row costs a second pass as long as one item)
+        const int jj = (int)ceilf(mu + (P.S > 1 ? 6.f : 4.f) * sqrtf(mu) + 1.f);
         if (jj > 64 * kSampleTiles) continue;
         uint32_t v[kSampleTiles];
 #pragma unroll
@@ -1400,7 +1419,8 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.seg_stride = pl.seg_stride;
   P.seg_pos = P.seg_keys + (size_t)a.B * a.Lq * pl.seg_stride;
   P.seg_cnt = reinterpret_cast<int32_t*>(w8 + pl.off_cnt);
-  P.counter = reinterpret_cast<int*>(w8);      // [0] work counter, [1] pass-1 counter, [2] failures
+  // [0] work counter, [1] pass-1 counter, [2] failures, [8..15] per-XCD work counters (S > 1)
+  P.counter = reinterpret_cast<int*>(w8);
   P.counter2 = P.counter + 1;
   P.fail_count = P.counter + 2;
   P.fail_items = reinterpret_cast<int*>(w8 + pl.off_fail);
@@ -1409,7 +1429,7 @@ hipError_t launch_indexer_topk_fused(const IndexerArgs& a, int k, int32_t* idx, 
   P.seg_spec = reinterpret_cast<uint32_t*>(P.seg_cnt + (size_t)a.B * a.Lq * pl.S);
   MergeSpec M{1, a.Lq, a.Lk, pl.nqb, pl.TQ, P.seg_spec, P.fail_count, P.fail_items,
               reinterpret_cast<int*>(w8 + pl.off_flag)};
-  zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 3);
+  zero_ints_kernel<<<1, 64, 0, s>>>(P.counter, 16);
   hipError_t e = hipGetLastError();
   if (e == hipSuccess && pl.S > 1) e = launch_zero(M.row_flag, (size_t)rows * sizeof(int32_t), s);
   if (e != hipSuccess) return e;
