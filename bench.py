@@ -182,7 +182,7 @@ def parse():
     ap.add_argument("--no-allfull", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 80-layer stack at the prefill workload")
     ap.add_argument("--no-chunk1m", action="store_true")
-    ap.add_argument("--no-quant", action="store_true", help="skip the per-token E4M3 quantization measurement")
+    ap.add_argument("--no-quant", action="store_true", help="skip the step-before-the-path measurements (projections, per-token E4M3 quantization)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -382,6 +382,7 @@ def main():
 
     if not args.no_quant:
         result["quantize"] = bench_quantize(dsa, torch, np, dev, stream)
+        result["projections"] = bench_projections(dsa, torch, np, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg)
@@ -563,6 +564,45 @@ def bench_quantize(dsa, torch, np, dev, stream):
     return {"prefill_qI_tokens": T, "prefill_ms": round(ms, 4), "prefill_hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "prefill_hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "decode_append_rows": B, "decode_append_us": round(us_app, 2)}
+
+
+def bench_projections(dsa, torch, np, dev, stream):
+    """The indexer's projections (the step before the path) for one 4096-token prefill
+    chunk: q^I = h W_Q (64 x 128 outputs), k^I = h W_K (128) and w = h W_w (64) from
+    hidden states of width D = 6144 (a stand-in: the pages give no width), bf16 in, fp32
+    out, then the per-token E4M3 quantization of q^I and k^I.  The q^I map is the
+    MFMA-bound part; its rate is reported against the bf16 peak."""
+    T, D, H_I, d_I = 4096, 6144, 64, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    h = torch.randn((T, D), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    wq = (torch.randn((H_I * d_I, D), generator=g, device=dev, dtype=torch.float32) * D ** -0.5).to(torch.bfloat16)
+    wk = (torch.randn((d_I, D), generator=g, device=dev, dtype=torch.float32) * D ** -0.5).to(torch.bfloat16)
+    ww = (torch.randn((H_I, D), generator=g, device=dev, dtype=torch.float32) * D ** -0.5).to(torch.bfloat16)
+    yq = torch.empty((T, H_I * d_I), dtype=torch.float32, device=dev)
+
+    def timed(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_q = timed(lambda: dsa.linear_bf16(h, wq, out=yq))
+    ms_all = timed(lambda: dsa.indexer_projections(h, wq, wk, ww, H_I))
+    fl_q = 2.0 * T * H_I * d_I * D
+    tf_q = fl_q / (ms_q * 1e-3) / 1e12
+    del h, wq, wk, ww, yq
+    torch.cuda.empty_cache()
+    log(f"[bench] projections: q^I map {ms_q:.3f} ms ({tf_q:.0f} TFLOP/s, {tf_q / MFMA_PEAK_TFLOPS['bf16'] * 100:.1f}% "
+        f"of bf16 peak); q^I + k^I + w with quantization {ms_all:.3f} ms per {T} tokens")
+    return {"tokens": T, "hidden": D, "qI_map_ms": round(ms_q, 4), "qI_map_tflops": round(tf_q, 1),
+            "qI_map_frac": round(tf_q / MFMA_PEAK_TFLOPS["bf16"], 4), "all_ms": round(ms_all, 4)}
 
 
 def bench_decode_paged(dsa, torch, np, cfg, ind, layers, ws, stream, n, k, dev, page=64):

@@ -17,7 +17,7 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
     "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
-    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "Workspace",
+    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "Workspace",
 ]
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
@@ -80,11 +80,12 @@ def load_library():
                                     i32, i32, vp, vp, sz, vp]
     lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
     lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
+    lib.dsa_linear_bf16.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, i64, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
                "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_sparse_attn_kv8", "dsa_layer_group",
-               "dsa_layer_schedule", "dsa_quantize_e4m3"):
+               "dsa_layer_schedule", "dsa_quantize_e4m3", "dsa_linear_bf16"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -420,3 +421,42 @@ def quantize_e4m3(x, codes=None, scales=None, stream=None):
         _ptr(x2), DSA_BF16 if x.dtype == torch.bfloat16 else DSA_F32, T, n, x2.stride(0), _ptr(c2), c2.stride(0),
         _ptr(scales), scales.stride(0), _stream(stream)))
     return codes, scales
+
+
+def linear_bf16(x, w, out=None, stream=None):
+    """y = x w^T (dsa_linear_bf16): x bfloat16 [M, K] with contiguous rows, w bfloat16
+    [N, K] (a linear layer's weight), K a multiple of 64; returns float32 [M, N].  Rows may
+    be strided (views of wider tensors) but their elements must be contiguous."""
+    if not (x.is_cuda and w.is_cuda):
+        raise ValueError("x and w must be on the GPU")
+    if x.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("x and w must be bfloat16")
+    if x.dim() != 2 or w.dim() != 2 or x.shape[1] != w.shape[1] or x.stride(1) != 1 or w.stride(1) != 1:
+        raise ValueError("x [M, K] and w [N, K] with contiguous rows are required")
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (M, N) or out.stride(1) != 1:
+        raise ValueError("out must be float32 [M, N] with contiguous rows")
+    _check("dsa_linear_bf16", load_library().dsa_linear_bf16(
+        _ptr(x), x.stride(0), _ptr(w), w.stride(0), M, N, K, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def indexer_projections(h, wq, wk, ww, H_I, stream=None):
+    """The indexer's operands from hidden states h bfloat16 [T, D]: q^I = h wq^T
+    (wq [H_I * d_I, D]) and k^I = h wk^T (wk [d_I, D]) in fp32, each quantized per token to
+    E4M3 (dsa_quantize_e4m3), and the head weights w = h ww^T (ww [H_I, D]) in fp32.
+    Returns dict(q [T, H_I, d_I] uint8, q_scale [T], k [T, d_I] uint8, k_scale [T],
+    w [T, H_I] float32) -- the per-sequence operands of indexer_topk after a [None]."""
+    T = h.shape[0]
+    d_I = wk.shape[0]
+    if wq.shape[0] != H_I * d_I or ww.shape[0] != H_I:
+        raise ValueError("wq must be [H_I * d_I, D] and ww [H_I, D]")
+    q32 = linear_bf16(h, wq, stream=stream)
+    k32 = linear_bf16(h, wk, stream=stream)
+    w32 = linear_bf16(h, ww, stream=stream)
+    q, q_scale = quantize_e4m3(q32.view(T, H_I, d_I), stream=stream)
+    k, k_scale = quantize_e4m3(k32, stream=stream)
+    return {"q": q, "q_scale": q_scale, "k": k, "k_scale": k_scale, "w": w32}

@@ -356,6 +356,18 @@ int dsa_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
+int dsa_linear_bf16(const void* x, int64_t x_row_stride, const void* w, int64_t w_row_stride, int M, int N, int K,
+                    float* y, int64_t y_row_stride, void* stream) {
+  if (!x || !w || !y) return DSA_ERR_ARG;
+  if (M <= 0 || N <= 0 || K <= 0 || (K % 64) != 0) return DSA_ERR_SHAPE;
+  if (x_row_stride < K || w_row_stride < K || y_row_stride < N) return DSA_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(w, 16) || (x_row_stride % 8) != 0 || (w_row_stride % 8) != 0) return DSA_ERR_ALIGN;
+  if (!aligned(y, 4)) return DSA_ERR_ALIGN;
+  const hipError_t e = dsa::launch_linear_bf16(x, x_row_stride, w, w_row_stride, M, N, K, y, y_row_stride,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
 int dsa_layer_schedule(int n_layers, int freq, int offset, const char* pattern, int32_t* anchor_out) {
   if (n_layers < 0 || !anchor_out) return DSA_ERR_ARG;
   int n_full = 0, last_full = -1;

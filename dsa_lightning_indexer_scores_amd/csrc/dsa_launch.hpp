@@ -88,6 +88,10 @@ hipError_t launch_topk_rows(const float* scores, int64_t row_stride, int rows, i
 hipError_t launch_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64_t x_stride,
                                 uint8_t* codes, int64_t c_stride, float* scales, int64_t s_stride, hipStream_t s);
 
+// --- bf16 linear map (indexer projections): y[M, N] fp32 = x[M, K] . w[N, K]^T ----
+hipError_t launch_linear_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, int M, int N, int K, float* y,
+                              int64_t ldy, hipStream_t s);
+
 // --- sparse attention --------------------------------------------------------
 struct AttnArgs {
   const void* q;

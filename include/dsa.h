@@ -301,6 +301,26 @@ int dsa_quantize_e4m3(const void* x, int x_dtype, int rows, int row_elems, int64
                       int64_t code_row_stride, float* scales, int64_t scale_stride, void* stream);
 
 /*
+ * bf16 linear map for the indexer's projections, the step before dsa_quantize_e4m3 ([B]
+ * discussion section "DSA 与 IndexShare 的组合数据流": the indexer keeps its own light
+ * projections W_Q^I, W_K^I beside the MLA path; [A] "IndexShare": per-head gating weights
+ * w^I).  The pages give neither the projections' input nor their widths; they are read as
+ * linear maps of the layer's hidden state h.  For the hidden states h of M
+ * tokens it computes q^I = h W_Q^I (N = H_I * d_I), k^I = h W_K^I (N = d_I) and
+ * w = h W_w (N = H_I), one call per weight:
+ *   y[m * y_row_stride + n] = sum_k x[m * x_row_stride + k] * w[n * w_row_stride + k],
+ * i.e. x [M, K] and w [N, K] are row-major bf16 (w in the layout of a linear layer's
+ * weight) and y [M, N] is fp32, each output one dot product accumulated in fp32 by the
+ * bf16 matrix cores (the products are exact in fp32; the sum order is the kernel's).
+ * All pointers are caller-owned device memory.  K must be a positive multiple of 64;
+ * x_row_stride, w_row_stride >= K and multiples of 8, y_row_stride >= N; x and w 16-byte
+ * aligned, y 4-byte aligned.  Returns DSA_OK, DSA_ERR_ARG (null pointer), DSA_ERR_SHAPE,
+ * DSA_ERR_ALIGN or DSA_ERR_HIP.
+ */
+int dsa_linear_bf16(const void* x, int64_t x_row_stride, const void* w, int64_t w_row_stride, int M, int N, int K,
+                    float* y, int64_t y_row_stride, void* stream);
+
+/*
  * Layer schedule of an IndexShare stack ([B] section 5.2: the released configuration
  * sets index_topk_freq = 4, index_skip_topk_offset = 3 and no explicit pattern, and
  * after the offset the indexer types repeat full, shared, shared, shared; [A] section

@@ -36,6 +36,7 @@ from .dsa import (
     layer_group,
 )
 from .schedule import indexer_types, anchors
+from .projections import linear, indexer_projections
 from .accounting import (
     causal_pairs,
     selected_pairs,
@@ -49,4 +50,5 @@ __all__ = [
     "causal_position", "indexer_scores", "indexer_scores_rows", "topk_row", "topk_rows",
     "sparse_attention_rows", "layer_group",
     "causal_pairs", "selected_pairs", "indexer_flops", "attention_flops", "cost_model",
+    "linear", "indexer_projections",
 ]

@@ -222,3 +222,20 @@ def test_layer_schedule_errors(args):
 def test_quantize_argument_errors(args, st):
     lib = dsa.load_library()
     assert lib.dsa_quantize_e4m3(*args, None) == st
+
+
+@host_only
+@pytest.mark.parametrize("args,st", [
+    ((None, 64, 0x2000, 64, 4, 4, 64, 0x3000, 4), -1),          # null x
+    ((0x1000, 64, 0x2000, 64, 4, 4, 64, None, 4), -1),          # null y
+    ((0x1000, 96, 0x2000, 96, 4, 4, 96, 0x3000, 4), -3),        # K not a multiple of 64
+    ((0x1000, 64, 0x2000, 64, 0, 4, 64, 0x3000, 4), -3),        # M = 0
+    ((0x1000, 32, 0x2000, 64, 4, 4, 64, 0x3000, 4), -3),        # x row stride < K
+    ((0x1000, 64, 0x2000, 64, 4, 8, 64, 0x3000, 4), -3),        # y row stride < N
+    ((0x1008, 64, 0x2000, 64, 4, 4, 64, 0x3000, 4), -4),        # x not 16-byte aligned
+    ((0x1000, 68, 0x2000, 64, 4, 4, 64, 0x3000, 4), -4),        # x row stride not a multiple of 8
+    ((0x1000, 64, 0x2000, 64, 4, 4, 64, 0x3002, 4), -4),        # y not 4-byte aligned
+])
+def test_linear_argument_errors(args, st):
+    lib = dsa.load_library()
+    assert lib.dsa_linear_bf16(*args, None) == st

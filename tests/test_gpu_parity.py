@@ -651,3 +651,73 @@ def test_cache_filled_by_quantize_gives_the_indexer_its_operands():
                                q_scale=qs_ref.to(DEV).reshape(1, 1),
                                k_scale=ks_ref.to(DEV).reshape(1, Lk))
     assert torch.equal(idx, idx_ref)
+
+
+# ---------------------------------------------------------------------------
+# The step before the path: bf16 linear maps for the indexer's projections
+# ---------------------------------------------------------------------------
+def _bf16_strided(rows, cols, pad, gen, scale=1.0, ints=False):
+    """Seeded bf16 [rows, cols] on the device as a view with row stride cols + pad."""
+    if ints:
+        full = torch.randint(-8, 9, (rows, cols + pad), generator=gen).float()
+    else:
+        full = torch.randn(rows, cols + pad, generator=gen) * scale
+    return full.to(torch.bfloat16).to(DEV)[:, :cols]
+
+
+@pytest.mark.parametrize("M,N,K,pad", [(300, 200, 192, 0), (128, 128, 64, 0), (1, 64, 640, 8),
+                                       (257, 8192, 256, 16), (4096, 128, 1536, 0)])
+def test_linear_bf16_parity(M, N, K, pad):
+    """Every output against the oracle's float64 dot product, within the bound of K
+    fp32 roundings of the exact products: |y - ref| <= K 2^-24 sum_k |x_k w_k|.  Shapes
+    span ragged edges in M and N, one and several K steps, and strided rows."""
+    g = torch.Generator().manual_seed(M * 31 + N * 7 + K)
+    x = _bf16_strided(M, K, pad, g)
+    w = _bf16_strided(N, K, pad, g, scale=0.05)
+    y = dsa.linear_bf16(x, w).cpu().numpy().astype(np.float64)
+    xo, wo = to_f64(x), to_f64(w)
+    ref = oracle.linear(xo, wo)
+    bound = K * 2.0 ** -24 * (np.abs(xo) @ np.abs(wo).T) * 1.01 + 1e-30
+    err = np.abs(y - ref)
+    assert np.all(err <= bound), f"worst excess {np.max(err - bound)}"
+
+
+def test_linear_bf16_integer_exact():
+    """Small-integer operands: every product and partial sum is an integer below 2^24, so
+    any fp32 summation order is exact and the result equals the oracle bit for bit."""
+    g = torch.Generator().manual_seed(5)
+    M, N, K = 200, 136, 512
+    x = _bf16_strided(M, K, 0, g, ints=True)
+    w = _bf16_strided(N, K, 0, g, ints=True)
+    y = dsa.linear_bf16(x, w).cpu().numpy().astype(np.float64)
+    np.testing.assert_array_equal(y, oracle.linear(to_f64(x), to_f64(w)))
+
+
+def test_indexer_projections_bit_exact_on_integer_data():
+    """The composed projections (three linear maps, then the per-token E4M3 quantization
+    of q^I and k^I) equal the oracle's codes, scales and weights exactly when the linear
+    maps are exact (integer data), and the operands run through the fused indexer."""
+    g = torch.Generator().manual_seed(9)
+    T, D, H_I, d_I = 96, 256, 64, 128
+    h = _bf16_strided(T, D, 0, g, ints=True)
+    wq = _bf16_strided(H_I * d_I, D, 0, g, ints=True)
+    wk = _bf16_strided(d_I, D, 0, g, ints=True)
+    ww = _bf16_strided(H_I, D, 0, g, ints=True)
+    out = dsa.indexer_projections(h, wq, wk, ww, H_I)
+    ref = oracle.indexer_projections(to_f64(h), to_f64(wq), to_f64(wk), to_f64(ww), H_I)
+    for name in ("q", "k"):
+        np.testing.assert_array_equal(out[name].cpu().numpy(), ref[name])
+        np.testing.assert_array_equal(out[name + "_scale"].cpu().numpy(), ref[name + "_scale"])
+    np.testing.assert_array_equal(out["w"].cpu().numpy().astype(np.float64), ref["w"])
+    ind = {"q": out["q"][None], "k": out["k"][None], "w": out["w"][None].contiguous(),
+           "q_scale": out["q_scale"][None], "k_scale": out["k_scale"][None]}
+    k = 32
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, q_scale=ind["q_scale"],
+                           k_scale=ind["k_scale"]).cpu().numpy()[0]
+    ora = indexer_to_oracle(ind)
+    rows = list(range(T))
+    sc = oracle.indexer_scores_rows(ora["q"][0], ora["k"][0], ora["w"][0], rows, T, ora["q_scale"][0],
+                                    ora["k_scale"][0], T)
+    ok, _, msg = index_sets_agree(idx, oracle.topk_rows(sc, [r + 1 for r in rows], k), sc, [r + 1 for r in rows], k,
+                                  TAU["fp8"])
+    assert ok, msg
