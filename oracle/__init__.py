@@ -37,6 +37,7 @@ from .dsa import (
 )
 from .schedule import indexer_types, anchors
 from .projections import linear, indexer_projections
+from .objective import attention_centroid_rows, indexer_kl_rows
 from .accounting import (
     causal_pairs,
     selected_pairs,
@@ -50,5 +51,5 @@ __all__ = [
     "causal_position", "indexer_scores", "indexer_scores_rows", "topk_row", "topk_rows",
     "sparse_attention_rows", "layer_group",
     "causal_pairs", "selected_pairs", "indexer_flops", "attention_flops", "cost_model",
-    "linear", "indexer_projections",
+    "linear", "indexer_projections", "attention_centroid_rows", "indexer_kl_rows",
 ]
