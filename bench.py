@@ -41,7 +41,7 @@ TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_ker
                    "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
 PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
                '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
-               '--no-chunk1m --no-quant --copy-calibration')
+               '--no-chunk1m --no-quant --no-train --copy-calibration')
 COPY_BYTES = 1 << 30
 
 
@@ -182,6 +182,7 @@ def parse():
     ap.add_argument("--no-allfull", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 80-layer stack at the prefill workload")
     ap.add_argument("--no-chunk1m", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the indexer-training (centroid, KL backward) measurement")
     ap.add_argument("--no-quant", action="store_true", help="skip the step-before-the-path measurements (projections, per-token E4M3 quantization)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB device-to-device copy (HBM counter scale)")
@@ -383,6 +384,8 @@ def main():
     if not args.no_quant:
         result["quantize"] = bench_quantize(dsa, torch, np, dev, stream)
         result["projections"] = bench_projections(dsa, torch, np, dev, stream)
+    if not args.no_train:
+        result["indexer_training"] = bench_objective(dsa, synth, torch, dev, stream)
 
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(cfg)
@@ -603,6 +606,58 @@ def bench_projections(dsa, torch, np, dev, stream):
         f"of bf16 peak); q^I + k^I + w with quantization {ms_all:.3f} ms per {T} tokens")
     return {"tokens": T, "hidden": D, "qI_map_ms": round(ms_q, 4), "qI_map_tflops": round(tf_q, 1),
             "qI_map_frac": round(tf_q / MFMA_PEAK_TFLOPS["bf16"], 4), "all_ms": round(ms_all, 4)}
+
+
+def bench_objective(dsa, synth, torch, dev, stream):
+    """Training of the kept indexer at the 16K bf16 prefill (L = 16384, H_I = 64, d_I = 128,
+    k = 2048, 4 MLA layers of 32 heads): the group centroid of the 4 layers' head-averaged
+    distributions on each index row (dsa_attn_probs per layer, from the lse of its sparse
+    attention), then the KL backward of the indexer (loss, dq, dw, dk).  Work: the centroid
+    rescores every selected (query, key) pair per layer, 2 * 32 * 576 flops; the backward
+    scores each pair twice and runs the dq and dk contractions, 4 * 2 * 64 * 128 flops."""
+    cfg = synth.get_config("prefill16k")
+    ind = synth.indexer_inputs(cfg, device=dev)
+    layers = [synth.attention_inputs(cfg, layer=l, device=dev) for l in range(cfg.n_layers)]
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], cfg.topk)
+    lses = [dsa.sparse_attn(lay, idx, return_lse=True)[1] for lay in layers]
+    pbar = torch.zeros(idx.shape, dtype=torch.float32, device=dev)
+    dk = torch.zeros(ind["k"].shape, dtype=torch.float32, device=dev)
+
+    def centroid():
+        pbar.zero_()
+        dsa.attention_centroid(layers, idx, lses, out=pbar)
+
+    def backward():
+        dk.zero_()
+        return dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar, dk=dk)
+
+    def timed(fn, n=3):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_c = timed(centroid)
+    ms_b = timed(backward)
+    sel = int((idx >= 0).sum())
+    fl_c = 2.0 * cfg.H * cfg.Dqk * sel * len(layers)
+    fl_b = 4 * 2.0 * cfg.H_I * cfg.d_I * sel
+    tf_c, tf_b = fl_c / (ms_c * 1e-3) / 1e12, fl_b / (ms_b * 1e-3) / 1e12
+    loss = float(backward()["loss"].mean())
+    del ind, layers, idx, lses, pbar, dk
+    torch.cuda.empty_cache()
+    log(f"[bench] indexer training (16K bf16): centroid of 4 layers {ms_c:.2f} ms ({tf_c:.0f} TFLOP/s), "
+        f"KL backward {ms_b:.2f} ms ({tf_b:.0f} TFLOP/s), mean loss {loss:.4f}")
+    return {"workload": cfg.name, "selected_pairs": sel, "centroid_ms": round(ms_c, 3),
+            "centroid_tflops": round(tf_c, 1), "kl_backward_ms": round(ms_b, 3), "kl_backward_tflops": round(tf_b, 1),
+            "bf16_frac_centroid": round(tf_c / MFMA_PEAK_TFLOPS["bf16"], 4),
+            "bf16_frac_kl_backward": round(tf_b / MFMA_PEAK_TFLOPS["bf16"], 4)}
 
 
 def bench_decode_paged(dsa, torch, np, cfg, ind, layers, ws, stream, n, k, dev, page=64):

@@ -17,7 +17,8 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
     "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
-    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "Workspace",
+    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "attention_centroid",
+    "indexer_kl_backward", "Workspace",
 ]
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
@@ -81,11 +82,14 @@ def load_library():
     lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
     lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
     lib.dsa_linear_bf16.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, i64, vp]
+    lib.dsa_attn_probs.argtypes = [ctypes.POINTER(_AttnIn), vp, i32, i32, i32, vp, i64, i32, ctypes.c_float, vp, vp]
+    lib.dsa_indexer_kl_backward.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
                "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_sparse_attn_kv8", "dsa_layer_group",
-               "dsa_layer_schedule", "dsa_quantize_e4m3", "dsa_linear_bf16"):
+               "dsa_layer_schedule", "dsa_quantize_e4m3", "dsa_linear_bf16", "dsa_attn_probs",
+               "dsa_indexer_kl_backward"):
         getattr(lib, fn).restype = i32
     _lib = lib
     return lib
@@ -460,3 +464,50 @@ def indexer_projections(h, wq, wk, ww, H_I, stream=None):
     q, q_scale = quantize_e4m3(q32.view(T, H_I, d_I), stream=stream)
     k, k_scale = quantize_e4m3(k32, stream=stream)
     return {"q": q, "q_scale": q_scale, "k": k, "k_scale": k_scale, "w": w32}
+
+
+def attention_centroid(layers, idx, lses, idx_q_stride=None, out=None, stream=None):
+    """The centroid of the group's attention distributions on each query's index row
+    (dsa_attn_probs once per layer, weight 1/len(layers)): each layer's distribution is the
+    mean over its heads of the softmax over the row, rebuilt from the layer's q, latent kv,
+    sm_scale and the lse its sparse_attn returned for the same idx.  layers: MLA layer
+    dicts (bf16 q [B,Lq,H,576], kv [B,Lk,576]); lses: one [B,Lq,H] float32 per layer.
+    Returns pbar float32 [B, Lq, k] (0 at -1 entries)."""
+    q0 = layers[0]["q"]
+    B, Lq = q0.shape[0], q0.shape[1]
+    k = idx.shape[-1]
+    if idx_q_stride is None:
+        idx_q_stride = 0 if idx.shape[1] == 1 and Lq > 1 else k
+    if out is None:
+        out = torch.zeros((B, Lq, k), dtype=torch.float32, device=q0.device)
+    _require_cuda(idx, out)
+    alpha = 1.0 / len(layers)
+    for lay, lse in zip(layers, lses):
+        q, kv = lay["q"], lay["kv"]
+        _require_cuda(q, kv, lse)
+        s = _AttnIn(_ptr(q), _ptr(kv), kv.shape[-1], _ptr(kv), kv.shape[-1], None, _ptr(lse), q.shape[2], 1,
+                    q.shape[-1], lay.get("Dv", 512), float(lay["sm_scale"]), _dtype_code(q), _dtype_code(q))
+        _check("dsa_attn_probs", load_library().dsa_attn_probs(
+            ctypes.byref(s), _ptr(lse), B, Lq, kv.shape[1], _ptr(idx), idx_q_stride, k, alpha, _ptr(out),
+            _stream(stream)))
+    return out
+
+
+def indexer_kl_backward(q, k, w, idx, pbar, dk=None, stream=None):
+    """Loss and gradients of the group-centroid objective of the kept indexer
+    (dsa_indexer_kl_backward): q bf16 [B,Lq,H_I,128], k bf16 [B,Lk,128], w float32
+    [B,Lq,H_I], idx int32 [B,Lq,k], pbar float32 [B,Lq,k].  Returns dict(loss [B,Lq],
+    dq [B,Lq,H_I,128], dw [B,Lq,H_I], dk [B,Lk,128]); dk, if given, is added to."""
+    s, B, Lq, Lk = _indexer_struct(q, k, w, None, None)
+    kk = idx.shape[-1]
+    _require_cuda(idx, pbar)
+    loss = torch.empty((B, Lq), dtype=torch.float32, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dw = torch.empty(w.shape, dtype=torch.float32, device=q.device)
+    if dk is None:
+        dk = torch.zeros(k.shape, dtype=torch.float32, device=q.device)
+    _require_cuda(dk)
+    _check("dsa_indexer_kl_backward", load_library().dsa_indexer_kl_backward(
+        ctypes.byref(s), B, Lq, Lk, _ptr(idx), kk, _ptr(pbar), _ptr(loss), _ptr(dq), _ptr(dw), _ptr(dk),
+        _stream(stream)))
+    return {"loss": loss, "dq": dq, "dw": dw, "dk": dk}

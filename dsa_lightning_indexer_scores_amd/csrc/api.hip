@@ -368,6 +368,34 @@ int dsa_linear_bf16(const void* x, int64_t x_row_stride, const void* w, int64_t 
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 
+int dsa_attn_probs(const dsa_attn_in* in, const float* lse, int B, int Lq, int Lk, const int32_t* idx,
+                   int64_t idx_q_stride, int k, float alpha, float* P, void* stream) {
+  if (!in || !lse || !idx || !P || !in->q || !in->k) return DSA_ERR_ARG;
+  if (in->dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0) return DSA_ERR_SHAPE;
+  if (in->Hkv != 1 || in->Dqk != 576 || (in->H != 16 && in->H != 32)) return DSA_ERR_SHAPE;
+  if (in->k_row_stride < 576 || idx_q_stride < 0 || (idx_q_stride != 0 && idx_q_stride < k)) return DSA_ERR_SHAPE;
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || (in->k_row_stride % 8) != 0) return DSA_ERR_ALIGN;
+  if (!aligned(lse, 4) || !aligned(idx, 4) || !aligned(P, 4)) return DSA_ERR_ALIGN;
+  dsa::AttnProbsArgs a{in->q, in->k, in->k_row_stride, lse, idx, idx_q_stride, P, in->sm_scale, alpha,
+                       B, Lq, Lk, in->H, k};
+  return dsa::launch_attn_probs(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_indexer_kl_backward(const dsa_indexer_in* in, int B, int Lq, int Lk, const int32_t* idx, int k,
+                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* stream) {
+  if (!in || !in->q || !in->k || !in->w || !idx || !pbar || !loss || !dq || !dw || !dk) return DSA_ERR_ARG;
+  if (in->dtype != DSA_BF16) return DSA_ERR_DTYPE;
+  if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || k > dsa::kMaxKlK) return DSA_ERR_SHAPE;
+  if (in->d_I != 128 || in->H_I <= 0 || in->H_I > 64 || (in->H_I % 16) != 0) return DSA_ERR_SHAPE;
+  if (!aligned(in->q, 16) || !aligned(in->k, 16) || !aligned(in->w, 4)) return DSA_ERR_ALIGN;
+  if (!aligned(idx, 4) || !aligned(pbar, 4) || !aligned(loss, 4) || !aligned(dq, 4) || !aligned(dw, 4) ||
+      !aligned(dk, 4))
+    return DSA_ERR_ALIGN;
+  dsa::IndexerKlArgs a{in->q, in->k, in->w, idx, pbar, loss, dq, dw, dk, B, Lq, Lk, in->H_I, k};
+  return dsa::launch_indexer_kl(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
 int dsa_layer_schedule(int n_layers, int freq, int offset, const char* pattern, int32_t* anchor_out) {
   if (n_layers < 0 || !anchor_out) return DSA_ERR_ARG;
   int n_full = 0, last_full = -1;

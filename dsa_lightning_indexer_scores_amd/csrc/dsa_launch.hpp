@@ -92,6 +92,34 @@ hipError_t launch_quantize_e4m3(const void* x, int x_dtype, int rows, int row_el
 hipError_t launch_linear_bf16(const void* x, int64_t ldx, const void* w, int64_t ldw, int M, int N, int K, float* y,
                               int64_t ldy, hipStream_t s);
 
+// --- group-centroid objective of the indexer (training) ------------------------
+struct AttnProbsArgs {
+  const void* q;            // [B, Lq, H, 576] bf16
+  const void* kv;           // latent rows, [B, Lk] rows of k_row_stride bf16 (first 576 used)
+  int64_t k_row_stride;
+  const float* lse;         // [B, Lq, H] natural-log sum of exp(sm_scale q . K) over the row
+  const int32_t* idx;       // row r at idx + r * idx_q_stride, k entries
+  int64_t idx_q_stride;
+  float* P;                 // [B, Lq, k], accumulated
+  float sm_scale, alpha;
+  int B, Lq, Lk, H, k;
+};
+hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s);
+constexpr int kMaxKlK = 2048;   // index-row length limit of the backward (its scores stay in LDS)
+struct IndexerKlArgs {
+  const void* q;            // [B, Lq, H_I, 128] bf16
+  const void* kI;           // [B, Lk, 128] bf16
+  const float* w;           // [B, Lq, H_I]
+  const int32_t* idx;       // [B, Lq, k]
+  const float* pbar;        // [B, Lq, k]
+  float* loss;              // [B, Lq]
+  float* dq;                // [B, Lq, H_I, 128]
+  float* dw;                // [B, Lq, H_I]
+  float* dk;                // [B, Lk, 128], accumulated
+  int B, Lq, Lk, H_I, k;
+};
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t s);
+
 // --- sparse attention --------------------------------------------------------
 struct AttnArgs {
   const void* q;

@@ -1,0 +1,354 @@
+// The group-centroid objective of the kept indexer, backward (training; gfx950).
+//
+// GLM-5.2 技术报告速览, section "IndexShare": reusing one index set across a group of layers
+// loses accuracy when each indexer was trained for its own layer only, so the kept indexer
+// is fit, by KL, to the centroid pbar_t = (1 / (m + 1)) sum_j p_t^(l+j) of the head-averaged
+// attention distributions of the m + 1 layers it serves.  Read here in the sparse form:
+// both distributions live on the query's index row S_t, and the loss of row t is
+// KL(pbar_t || pi_t) with pi_t = softmax over S_t of the indexer scores
+//   I[t, s] = sum_j w[t, j] ReLU(q[t, j] . k[s]).
+// Its gradient with respect to I[t, s] is pi - pbar; with x = q[t, j] . k[s] and
+// c[j, s] = (pi - pbar)[s] w[t, j] [x > 0]:
+//   dw[t, j] = sum_s (pi - pbar)[s] ReLU(x),   dq[t, j] = sum_s c[j, s] k[s],
+//   dk[s]   += sum_t sum_j c[j, s] q[t, j]   (accumulated over the rows that selected s).
+//
+// attn_probs_kernel: one layer's head-averaged distribution on S_t, recomputed from the
+// layer's queries, latent rows and log-sum-exp (that of dsa_sparse_attn), accumulated
+// with a weight: P[t, i] += alpha / H sum_h exp(sm_scale q[t, h] . K[S_t[i]] - lse[t, h]).
+//
+// indexer_kl_kernel: one workgroup per query row, selected keys in tiles of 64 gathered to
+// LDS (row-major for the scores, transposed for dq).  Pass 1 scores every tile (wave w
+// owns heads 16w..16w+15; MFMA 16x16x32 bf16, fp32 accumulation) and keeps I in LDS; the
+// softmax, the loss and g = pi - pbar follow.  Pass 2 rescores each tile, forms c (rounded
+// to bf16 for the matrix cores), accumulates dw in fp32 and runs two more contractions:
+// dq (heads x dims over the tile's keys) in registers, and dk (keys x dims over the heads),
+// added to the global dk with fp32 atomics.
+#include "dsa_common.hpp"
+#include "dsa_launch.hpp"
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+namespace {
+constexpr int kLatent = 576;
+constexpr int kLatentPad = 584;   // LDS row of a query head: 16 rows of a read start in distinct banks
+constexpr int kDI = 128;          // indexer head dim
+constexpr int kTile = 64;         // selected keys per tile
+constexpr int kRowPadK = 136;     // LDS row (bf16) of a key in the row-major tile
+constexpr int kRowPad64 = 72;     // LDS row (bf16) of the 64-wide transposed / coefficient tiles
+}  // namespace
+
+template <int HB>
+__global__ __launch_bounds__(256) void attn_probs_kernel(AttnProbsArgs a) {
+  constexpr int H = 16 * HB;
+  __shared__ __attribute__((aligned(16))) __bf16 qs[H * kLatentPad];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = blockIdx.x;                       // query row (b, i)
+  const int b = r / a.Lq;
+  const __bf16* q = static_cast<const __bf16*>(a.q) + (size_t)r * H * kLatent;
+  for (int e = tid; e < H * (kLatent / 8); e += 256) {
+    const int h = e / (kLatent / 8), c = e - h * (kLatent / 8);
+    *reinterpret_cast<bf16x8*>(&qs[h * kLatentPad + 8 * c]) = *reinterpret_cast<const bf16x8*>(q + h * kLatent + 8 * c);
+  }
+  float lse[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) lse[hb] = a.lse[(size_t)r * H + 16 * hb + (lane & 15)];
+  __syncthreads();
+  const int32_t* irow = a.idx + (size_t)r * a.idx_q_stride;
+  const __bf16* kv = static_cast<const __bf16*>(a.kv) + (size_t)b * a.Lk * a.k_row_stride;
+  float* prow = a.P + (size_t)r * a.k;
+  const float wscale = a.alpha / (float)H;
+  for (int base = 16 * wv; base < a.k; base += 64) {
+    // A: the key rows (lane: key base + l % 16), B: the query heads (lane: head l % 16)
+    const int slot = base + (lane & 15);
+    const int s = slot < a.k ? irow[slot] : -1;
+    const __bf16* krow = kv + (size_t)(s >= 0 && s < a.Lk ? s : 0) * a.k_row_stride;
+    f32x4 acc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 6
+    for (int ks = 0; ks < kLatent / 32; ++ks) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * (lane >> 4));
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&qs[(16 * hb + (lane & 15)) * kLatentPad + 32 * ks + 8 * (lane >> 4)]);
+        acc[hb] = mfma_bf16_16x16x32(av, bv, acc[hb]);
+      }
+    }
+    // acc[hb] lane l: head 16 hb + l % 16, keys base + 4 (l / 16) + i
+    float ps[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) v += expf(a.sm_scale * acc[hb][i] - lse[hb]);
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off);   // the 16 heads of the lane's row
+      ps[i] = v;
+    }
+    if ((lane & 15) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sl = base + 4 * (lane >> 4) + i;
+        if (sl < a.k) {
+          const int si = irow[sl];
+          if (si >= 0 && si < a.Lk) prow[sl] += wscale * ps[i];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int HB>
+__global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
+  constexpr int H = 16 * HB;
+  __shared__ __attribute__((aligned(16))) __bf16 kt[kTile * kRowPadK];      // [key][dim]
+  __shared__ __attribute__((aligned(16))) __bf16 ktT[kDI * kRowPad64];      // [dim][key]
+  __shared__ __attribute__((aligned(16))) __bf16 qT[kDI * kRowPad64];       // [dim][head]
+  __shared__ __attribute__((aligned(16))) __bf16 cm[64 * kRowPad64];        // c [head][key]
+  __shared__ __attribute__((aligned(16))) __bf16 cmT[kTile * kRowPad64];    // c [key][head]
+  __shared__ float sc[kMaxKlK];                                              // I, then pi - pbar
+  __shared__ float part[4][kTile];
+  __shared__ float red[8];
+  __shared__ int sel[kTile];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int r = blockIdx.x;
+  const int b = r / a.Lq;
+  const bool active = wv < HB;                    // waves past the heads only help with loads
+  const __bf16* qrow = static_cast<const __bf16*>(a.q) + (size_t)r * H * kDI;
+  const __bf16* kbase = static_cast<const __bf16*>(a.kI) + (size_t)b * a.Lk * kDI;
+  const float* wrow = a.w + (size_t)r * H;
+  const int32_t* irow = a.idx + (size_t)r * a.k;
+  const float* pbar = a.pbar + (size_t)r * a.k;
+
+  // q^T in LDS (B operand of dk) and this wave's heads as A operands of the scores
+  for (int e = tid; e < 64 * kDI; e += 256) {   // head slots past H hold zeros
+    const int h = e / kDI, d = e - h * kDI;
+    __bf16 v = (__bf16)0.f;
+    if (h < H) v = qrow[e];
+    qT[d * kRowPad64 + h] = v;
+  }
+  bf16x8 aq[4];
+  float wh[4];
+  const int hw = active ? wv : 0;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    aq[ks] = *reinterpret_cast<const bf16x8*>(qrow + (16 * hw + l16) * kDI + 32 * ks + 8 * g4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wh[i] = wrow[16 * hw + 4 * g4 + i];
+
+  // gather tile t: the selected rows, row-major into kt and transposed into ktT (-1 and
+  // out-of-range entries read row 0 and are masked by sel = -1)
+  auto gather = [&](int t) {
+    __syncthreads();   // the previous tile's LDS reads are done
+    if (tid < kTile) {
+      const int slot = t * kTile + tid;
+      const int s = slot < a.k ? irow[slot] : -1;
+      sel[tid] = (s >= 0 && s < a.Lk) ? s : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + 256 * u, key = c >> 4, ch = c & 15;
+      const int s = sel[key];
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(kbase + (size_t)(s >= 0 ? s : 0) * kDI + 8 * ch);
+      *reinterpret_cast<bf16x8*>(&kt[key * kRowPadK + 8 * ch]) = v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ktT[(8 * ch + e) * kRowPad64 + key] = v[e];
+    }
+    __syncthreads();
+  };
+  // x[kb] lane l: key 16 kb + l % 16 of the tile, heads 16 hw + 4 (l / 16) + i
+  auto scores = [&](f32x4 (&x)[4]) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&kt[(16 * kb + l16) * kRowPadK + 32 * ks + 8 * g4]);
+        acc = mfma_bf16_16x16x32(aq[ks], bv, acc);
+      }
+      x[kb] = acc;
+    }
+  };
+
+  const int n_tiles = (a.k + kTile - 1) / kTile;
+  // pass 1: I on every selected key
+  for (int t = 0; t < n_tiles; ++t) {
+    gather(t);
+    if (active) {
+      f32x4 x[4];
+      scores(x);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wh[i], fmaxf(x[kb][i], 0.f), v);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g4 == 0) part[wv][16 * kb + l16] = v;
+      }
+    }
+    __syncthreads();
+    if (tid < kTile) {
+      const int slot = t * kTile + tid;
+      if (slot < a.k) {
+        float v = 0.f;
+        for (int w = 0; w < HB; ++w) v += part[w][tid];
+        sc[slot] = sel[tid] >= 0 ? v : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
+
+  // softmax over the selected keys, the loss, and g = pi - pbar
+  auto block_sum = [&](float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+    __syncthreads();
+    if (lane == 0) red[wv] = v;
+    __syncthreads();
+    return red[0] + red[1] + red[2] + red[3];
+  };
+  float m = -INFINITY;
+  for (int i = tid; i < a.k; i += 256) m = fmaxf(m, sc[i]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) red[4 + wv] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7]));
+  float z = 0.f;
+  if (m > -INFINITY)
+    for (int i = tid; i < a.k; i += 256) z += expf(sc[i] - m);
+  z = block_sum(z);
+  const float log_z = logf(z);
+  float kl = 0.f;
+  for (int i = tid; i < a.k; i += 256) {
+    const float I = sc[i];
+    const float p = pbar[i];
+    float gi = 0.f;
+    if (I > -INFINITY) {
+      const float log_pi = I - m - log_z;
+      gi = expf(log_pi) - p;
+      if (p > 0.f) kl += p * (logf(p) - log_pi);
+    }
+    sc[i] = gi;
+  }
+  kl = block_sum(kl);
+  if (tid == 0) a.loss[r] = kl;
+
+  // pass 2: gradients
+  f32x4 dq[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dwp[4] = {0.f, 0.f, 0.f, 0.f};
+  float* dk = a.dk + (size_t)b * a.Lk * kDI;
+  for (int t = 0; t < n_tiles; ++t) {
+    gather(t);
+    if (active) {
+      f32x4 x[4];
+      scores(x);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = 16 * kb + l16, slot = t * kTile + key;
+        const float gk = (slot < a.k && sel[key] >= 0) ? sc[slot] : 0.f;
+        __bf16 cv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dwp[i] = fmaf(gk, fmaxf(x[kb][i], 0.f), dwp[i]);
+          const float c = x[kb][i] > 0.f ? gk * wh[i] : 0.f;
+          cv[i] = (__bf16)c;
+          cm[(16 * wv + 4 * g4 + i) * kRowPad64 + key] = cv[i];
+        }
+        *reinterpret_cast<bf16x4*>(&cmT[key * kRowPad64 + 16 * wv + 4 * g4]) = bf16x4{cv[0], cv[1], cv[2], cv[3]};
+      }
+    } else {
+      // waves past the heads: zero coefficients so that the dk contraction over 64 head
+      // slots reads zeros there
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int key = 16 * kb + l16;
+        *reinterpret_cast<bf16x4*>(&cmT[key * kRowPad64 + 16 * wv + 4 * g4]) = bf16x4{0, 0, 0, 0};
+      }
+    }
+    __syncthreads();
+    // dq (wave w: heads 16w.., all 128 dims) over the tile's 64 keys
+    if (active) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cm[(16 * wv + l16) * kRowPad64 + 32 * ks + 8 * g4]);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ktT[(16 * db + l16) * kRowPad64 + 32 * ks + 8 * g4]);
+          dq[db] = mfma_bf16_16x16x32(av, bv, dq[db]);
+        }
+      }
+    }
+    // dk (wave w: keys 16w.. of the tile, all 128 dims) over the 64 head slots
+    {
+      f32x4 acc[8];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        if (32 * hs >= H) break;
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cmT[(16 * wv + l16) * kRowPad64 + 32 * hs + 8 * g4]);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&qT[(16 * db + l16) * kRowPad64 + 32 * hs + 8 * g4]);
+          acc[db] = mfma_bf16_16x16x32(av, bv, acc[db]);
+        }
+      }
+      // acc[db] lane l: dim 16 db + l % 16, keys 16 wv + 4 (l / 16) + i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * wv + 4 * g4 + i;
+        const int s = sel[key];
+        if (s >= 0 && t * kTile + key < a.k) {
+#pragma unroll
+          for (int db = 0; db < 8; ++db) atomicAdd(&dk[(size_t)s * kDI + 16 * db + l16], acc[db][i]);
+        }
+      }
+    }
+  }
+
+  if (active) {
+    // dq[db] lane l: dim 16 db + l % 16, heads 16 wv + 4 (l / 16) + i
+    float* dqr = a.dq + (size_t)r * H * kDI;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dqr[(16 * wv + 4 * g4 + i) * kDI + 16 * db + l16] = dq[db][i];
+    // dw: the lane's 4 heads summed over its key columns, then over the 16 lanes of the row
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = dwp[i];
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off);
+      if (l16 == 0) a.dw[(size_t)r * H + 16 * wv + 4 * g4 + i] = v;
+    }
+  }
+}
+
+hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s) {
+  const int rows = a.B * a.Lq;
+  if (a.H == 16) attn_probs_kernel<1><<<rows, 256, 0, s>>>(a);
+  else attn_probs_kernel<2><<<rows, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t s) {
+  const int rows = a.B * a.Lq;
+  switch (a.H_I / 16) {
+    case 1: indexer_kl_kernel<1><<<rows, 256, 0, s>>>(a); break;
+    case 2: indexer_kl_kernel<2><<<rows, 256, 0, s>>>(a); break;
+    case 3: indexer_kl_kernel<3><<<rows, 256, 0, s>>>(a); break;
+    default: indexer_kl_kernel<4><<<rows, 256, 0, s>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -321,6 +321,46 @@ int dsa_linear_bf16(const void* x, int64_t x_row_stride, const void* w, int64_t 
                     float* y, int64_t y_row_stride, void* stream);
 
 /*
+ * Training of the kept indexer ([A] "IndexShare": reusing one index set across a group
+ * of layers loses accuracy when each indexer was trained for its own layer only, so the
+ * kept indexer is fit by KL to the centroid pbar_t = 1/(m+1) sum_j p_t^(l+j) of the
+ * head-averaged attention distributions of the m + 1 layers it serves).  Read in the
+ * sparse form: both distributions live on the query's index row S_t.
+ *
+ * dsa_attn_probs: one layer's head-averaged distribution on S_t, accumulated with weight
+ * alpha (1/(m+1) to build the centroid over a group):
+ *   P[r, i] += alpha / H * sum_h exp(sm_scale * q[r, h] . K[S_r[i]] - lse[r, h])
+ * for idx entries S_r[i] in [0, Lk) (other entries are left unchanged).  in is the
+ * layer's dsa_attn_in as given to dsa_sparse_attn (MLA: Hkv = 1, Dqk = 576, bf16, H = 16
+ * or 32; K is the whole latent row); lse [B, Lq, H] is what dsa_sparse_attn wrote for the
+ * same idx (natural-log sum of exp(sm_scale q . K) over the row); idx row r at idx + r *
+ * idx_q_stride (k, or 0 to share row 0), k entries; P [B, Lq, k] fp32, caller-owned.
+ * Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE, DSA_ERR_SHAPE, DSA_ERR_ALIGN or DSA_ERR_HIP.
+ */
+int dsa_attn_probs(const dsa_attn_in* in, const float* lse, int B, int Lq, int Lk, const int32_t* idx,
+                   int64_t idx_q_stride, int k, float alpha, float* P, void* stream);
+
+/*
+ * dsa_indexer_kl_backward: loss and gradients of sum_r KL(pbar_r || pi_r), pi_r the
+ * softmax over S_r of the indexer scores I[r, s] = sum_j w[r, j] ReLU(q[r, j] . k[s])
+ * (the indexer-score equation of [A]), with g = pi - pbar:
+ *   loss[r] = sum_{s in S_r, pbar > 0} pbar (log pbar - log pi)
+ *   dw[r, j] = sum_s g[s] ReLU(x),  dq[r, j, :] = sum_s g[s] w[r, j] [x > 0] k[s]
+ *   dk[s, :] += sum_r sum_j g[s] w[r, j] [x > 0] q[r, j]      (x = q[r, j] . k[s])
+ * in: bf16 q^I [B, Lq, H_I, 128] and k^I [B, Lk, 128], fp32 w [B, Lq, H_I] (H_I a multiple
+ * of 16, at most 64; d_I = 128); idx [B, Lq, k] (entries outside [0, Lk) are not in S_r;
+ * positions within a row must be distinct), k <= 2048; pbar [B, Lq, k] aligned with idx
+ * (mass only on entries in S_r).  Outputs fp32, caller-owned: loss [B, Lq], dq, dw, and
+ * dk [B, Lk, 128], which is ADDED to (zero it first); its additions are fp32 atomics, so
+ * their order, and the last bits of dk, may vary from run to run.  The contractions run
+ * on the bf16 matrix cores with fp32 accumulation; the coefficients g w [x > 0] enter them
+ * rounded to bf16.  Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE, DSA_ERR_SHAPE,
+ * DSA_ERR_ALIGN or DSA_ERR_HIP.
+ */
+int dsa_indexer_kl_backward(const dsa_indexer_in* in, int B, int Lq, int Lk, const int32_t* idx, int k,
+                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* stream);
+
+/*
  * Layer schedule of an IndexShare stack ([B] section 5.2: the released configuration
  * sets index_topk_freq = 4, index_skip_topk_offset = 3 and no explicit pattern, and
  * after the offset the indexer types repeat full, shared, shared, shared; [A] section

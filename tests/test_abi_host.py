@@ -239,3 +239,27 @@ def test_quantize_argument_errors(args, st):
 def test_linear_argument_errors(args, st):
     lib = dsa.load_library()
     assert lib.dsa_linear_bf16(*args, None) == st
+
+
+@host_only
+def test_objective_argument_errors():
+    lib = dsa.load_library()
+    s = _attn_struct()
+    call = lambda st=s, lse=0x7000, idx=0x5000, P=0x6000, Lk=64, k=16, stride=16: lib.dsa_attn_probs(
+        ctypes.byref(st), lse, 1, 4, Lk, idx, stride, k, ctypes.c_float(0.5), P, None)
+    assert call(lse=0) == -1
+    assert call(P=0) == -1
+    assert call(st=_attn_struct(dtype=dsa.DSA_F32, H=4, Hkv=4, Dqk=64, Dv=64, ks=256, vs=256)) == -2
+    assert call(st=_attn_struct(H=48)) == -3                    # 16 or 32 heads
+    assert call(stride=8) == -3                                 # idx row stride below k
+    assert call(P=0x6002) == -4
+    ind = _indexer_struct()
+    kl = lambda st=ind, k=64, idx=0x5000, dk=0x9000: lib.dsa_indexer_kl_backward(
+        ctypes.byref(st), 1, 8, 64, idx, k, 0x6000, 0x7000, 0x8000, 0x8800, dk, None)
+    assert kl(idx=0) == -1
+    assert kl(dk=0) == -1
+    assert kl(st=_indexer_struct(dtype=dsa.DSA_FP8_E4M3, qs=0x100, ks=0x200)) == -2
+    assert kl(k=4096) == -3                                     # index rows of at most 2048
+    assert kl(st=_indexer_struct(H_I=8)) == -3                  # H_I a multiple of 16
+    assert kl(st=_indexer_struct(d_I=64)) == -3                 # d_I = 128
+    assert kl(dk=0x9002) == -4

@@ -721,3 +721,84 @@ def test_indexer_projections_bit_exact_on_integer_data():
     ok, _, msg = index_sets_agree(idx, oracle.topk_rows(sc, [r + 1 for r in rows], k), sc, [r + 1 for r in rows], k,
                                   TAU["fp8"])
     assert ok, msg
+
+
+# ---------------------------------------------------------------------------
+# Training of the kept indexer: the group centroid and the KL backward
+# ---------------------------------------------------------------------------
+def _objective_case(B=2, L=320, k=128, H=32, n_layers=2, B_seed=0):
+    cfg = synth.get_config("prefill16k", L=L, Lq=L, B=B, topk=k, H=H)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k)
+    layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(n_layers)]
+    lses = [dsa.sparse_attn(lay, idx, return_lse=True)[1] for lay in layers]
+    return cfg, ind, idx, layers, lses
+
+
+@pytest.mark.parametrize("H", [32, 16])
+def test_attention_centroid_parity(H):
+    """Each row's centroid of the group's head-averaged distributions on its index row,
+    against the oracle's (fp32 exp and MFMA sums of exact bf16 products: relative 1e-4)."""
+    cfg, ind, idx, layers, lses = _objective_case(H=H, n_layers=3)
+    pbar = dsa.attention_centroid(layers, idx, lses).cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    for b in range(cfg.B):
+        ora_layers = [{"q": attn_to_oracle({**lay, "q": lay["q"][b:b + 1], "kv": lay["kv"][b:b + 1]})["q"][0],
+                       "k": attn_to_oracle({**lay, "q": lay["q"][b:b + 1], "kv": lay["kv"][b:b + 1]})["k"][0],
+                       "sm_scale": lay["sm_scale"]} for lay in layers]
+        ref = oracle.attention_centroid_rows(ora_layers, idx_h[b], list(range(cfg.Lq)))
+        np.testing.assert_allclose(pbar[b], ref, rtol=1e-4, atol=1e-7)
+        np.testing.assert_allclose(pbar[b].sum(axis=1), 1.0, rtol=1e-4)
+        assert np.all(pbar[b][idx_h[b] < 0] == 0)
+
+
+def test_indexer_kl_backward_parity():
+    """Loss, dq, dw and dk against the oracle on the GPU's centroid.  Bounds: the
+    coefficients c = g w [x > 0] enter the contractions rounded to bf16 (relative 2^-9,
+    taken as 2^-8 over the sum of |terms|); g = pi - pbar carries the fp32 error of the
+    scores and the softmax (1e-4 pi); pre-activations x within the fp32 accumulation error
+    of 0 may take either ReLU branch, and their whole term is allowed."""
+    cfg, ind, idx, layers, lses = _objective_case(B=2, L=320, k=128)
+    pbar = dsa.attention_centroid(layers, idx, lses)
+    out = dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar)
+    got = {n: out[n].cpu().numpy().astype(np.float64) for n in out}
+    ora = indexer_to_oracle(ind)
+    idx_h, pb = idx.cpu().numpy(), pbar.cpu().numpy().astype(np.float64)
+    for b in range(cfg.B):
+        rows = list(range(cfg.Lq))
+        q, kk, w = ora["q"][b], ora["k"][b], ora["w"][b]
+        loss, dq, dw, dk = oracle.indexer_kl_rows(q, kk, w, idx_h[b], pb[b], rows)
+        bq = np.zeros_like(dq)
+        bw = np.zeros_like(dw)
+        bk = np.zeros_like(dk)
+        for t in rows:
+            sel = idx_h[b, t][idx_h[b, t] >= 0]
+            x = q[t] @ kk[sel].T
+            score = w[t] @ np.maximum(x, 0)
+            pi = np.exp(score - score.max()); pi /= pi.sum()
+            g = pi - pb[b, t][idx_h[b, t] >= 0]
+            dg = 1e-4 * pi + 1e-9
+            tau = 2.0 ** -18 * (np.abs(q[t]) @ np.abs(kk[sel]).T)           # x's fp32 error
+            near = np.abs(x) <= tau
+            c_abs = np.abs(w[t])[:, None] * ((x > 0) | near) * (np.abs(g) + dg)[None, :]
+            c_err = 2.0 ** -8 * c_abs + np.abs(w[t])[:, None] * ((x > 0) | near) * dg[None, :] \
+                + np.abs(w[t])[:, None] * near * np.abs(g)[None, :]
+            bq[t] = c_err @ np.abs(kk[sel])
+            np.add.at(bk, sel, c_err.T @ np.abs(q[t]))
+            bw[t] = (np.abs(x) * (dg[None, :] + 2.0 ** -16 * np.abs(g)[None, :])).sum(axis=1) \
+                + (near * tau * np.abs(g)[None, :]).sum(axis=1)
+        np.testing.assert_allclose(got["loss"][b], loss, rtol=1e-4, atol=1e-6)
+        for name, g_, r_, bd in (("dq", got["dq"][b], dq, bq), ("dw", got["dw"][b], dw, bw), ("dk", got["dk"][b], dk, bk)):
+            err = np.abs(g_ - r_)
+            lim = bd + 1e-6 * np.abs(r_).max()
+            assert np.all(err <= lim), f"{name}: worst excess {np.max(err - lim)} (max |ref| {np.abs(r_).max()})"
+    # the objective is zero with zero gradient when the target is the indexer's own distribution
+    own = torch.zeros_like(pbar)
+    sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"])
+    for b in range(cfg.B):
+        for t in range(cfg.Lq):
+            sel = idx[b, t][idx[b, t] >= 0].long()
+            own[b, t, : sel.numel()] = torch.softmax(sc[b, t, sel].double(), 0).float()
+    z = dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, own)
+    assert float(z["loss"].abs().max()) < 1e-5
+    assert float(z["dw"].abs().max()) < 1e-4 * float(out["dw"].abs().max())
