@@ -209,7 +209,7 @@ def main():
         print(summarize_counters(*args.summarize_counters, args.kernel, args.template, args.workload))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1"}))
         sys.exit(2)
 
     import numpy as np
