@@ -210,3 +210,85 @@ def test_chunked_prefill_equals_unchunked():
         part = dsa.indexer_topk(ind["q"][:, lo:hi], ind["k"][:, :hi], ind["w"][:, lo:hi], k,
                                 q_scale=ind["q_scale"][:, lo:hi], k_scale=ind["k_scale"][:, :hi])
         assert torch.equal(part, full[:, lo:hi]), f"chunk {c}"
+
+
+def test_projections_full_size_sampled_rows():
+    """The q^I map the bench times (4096 tokens, D = 6144, N = 64 x 128): sampled rows
+    against the oracle's float64 dot products within the bound of K fp32 roundings."""
+    T, D, N = 4096, 6144, 64 * 128
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    h = torch.randn((T, D), generator=g, device=DEV, dtype=torch.float32).to(torch.bfloat16)
+    wq = (torch.randn((N, D), generator=g, device=DEV, dtype=torch.float32) * D ** -0.5).to(torch.bfloat16)
+    y = dsa.linear_bf16(h, wq)
+    rows = [0, 1, 127, 128, 2047, 4095] + np.random.default_rng(3).integers(0, T, 4).tolist()
+    xo, wo = to_f64(h[rows]), to_f64(wq)
+    ref = oracle.linear(xo, wo)
+    bound = D * 2.0 ** -24 * (np.abs(xo) @ np.abs(wo).T) * 1.01
+    err = np.abs(y[rows].cpu().numpy().astype(np.float64) - ref)
+    assert np.all(err <= bound), f"worst excess {np.max(err - bound)}"
+
+
+def test_indexer_training_16k_sampled():
+    """The training step the bench times (16K bf16, k = 2048, 4 MLA layers): the centroid,
+    the loss, dq and dw on sampled rows, and dk on sampled keys (summed over every row that
+    selected them), against the oracle with the bounds of the small-size parity test."""
+    cfg = synth.get_config("prefill16k")
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(cfg.n_layers)]
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], cfg.topk)
+    lses = [dsa.sparse_attn(lay, idx, return_lse=True)[1] for lay in layers]
+    pbar = dsa.attention_centroid(layers, idx, lses)
+    out = dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar)
+    idx_h = idx[0].cpu().numpy()
+    pb = pbar[0].cpu().numpy().astype(np.float64)
+    rows = [0, 1, 2047, 2048, 9000, cfg.Lq - 1] + np.random.default_rng(4).integers(0, cfg.Lq, 3).tolist()
+    # centroid on the sampled rows
+    ora_layers = [{"q": to_f64(lay["q"][0, rows]), "k": to_f64(lay["kv"][0])[:, None, :], "sm_scale": lay["sm_scale"]}
+                  for lay in layers]
+    ref_p = oracle.attention_centroid_rows(ora_layers, idx_h[rows], list(range(len(rows))))
+    np.testing.assert_allclose(pb[rows], ref_p, rtol=1e-4, atol=1e-7)
+    # loss, dq, dw on the sampled rows (the GPU's centroid is the target of both sides)
+    q = to_f64(ind["q"][0])
+    kk = to_f64(ind["k"][0])
+    w = to_f64(ind["w"][0])
+    loss, dq, dw, _ = oracle.indexer_kl_rows(q, kk, w, idx_h[rows], pb[rows], rows)
+    np.testing.assert_allclose(out["loss"][0, rows].cpu().numpy(), loss, rtol=1e-4, atol=1e-6)
+
+    def bounds(t, r):
+        sel = idx_h[t][idx_h[t] >= 0]
+        x = q[t] @ kk[sel].T
+        score = w[t] @ np.maximum(x, 0)
+        pi = np.exp(score - score.max()); pi /= pi.sum()
+        gg = pi - pb[t][idx_h[t] >= 0]
+        dg = 1e-4 * pi + 1e-9
+        tau = 2.0 ** -18 * (np.abs(q[t]) @ np.abs(kk[sel]).T)
+        near = np.abs(x) <= tau
+        c_err = 2.0 ** -8 * np.abs(w[t])[:, None] * ((x > 0) | near) * (np.abs(gg) + dg)[None, :] \
+            + np.abs(w[t])[:, None] * ((x > 0) | near) * dg[None, :] + np.abs(w[t])[:, None] * near * np.abs(gg)[None, :]
+        bw = (np.abs(x) * (dg[None, :] + 2.0 ** -16 * np.abs(gg)[None, :])).sum(axis=1) + (near * tau * np.abs(gg)[None, :]).sum(axis=1)
+        return sel, c_err, bw
+
+    got_dq = out["dq"][0, rows].cpu().numpy()
+    got_dw = out["dw"][0, rows].cpu().numpy()
+    for r, t in enumerate(rows):
+        sel, c_err, bw = bounds(t, r)
+        assert np.all(np.abs(got_dq[r] - dq[r]) <= c_err @ np.abs(kk[sel]) + 1e-6 * np.abs(dq).max()), f"dq row {t}"
+        assert np.all(np.abs(got_dw[r] - dw[r]) <= bw + 1e-6 * np.abs(dw).max()), f"dw row {t}"
+    # dk on sampled keys: every row that selected them contributes
+    counts = np.bincount(idx_h[idx_h >= 0], minlength=cfg.L)
+    used = np.nonzero(counts)[0]
+    order = used[np.argsort(counts[used], kind="stable")]
+    keys = [int(order[0]), int(order[len(order) // 2]), int(order[(3 * len(order)) // 4])]   # light to typical
+    got_dk = out["dk"][0].cpu().numpy()
+    for s in keys:
+        src = np.nonzero((idx_h == s).any(axis=1))[0].tolist()
+        if not src:
+            continue
+        _, _, _, dk = oracle.indexer_kl_rows(q, kk, w, idx_h[src], pb[src], src)
+        lim = np.zeros(kk.shape[1])
+        for t in src:
+            sel, c_err, _ = bounds(t, 0)
+            j = int(np.nonzero(sel == s)[0][0])
+            lim += c_err[:, j] @ np.abs(q[t])
+        assert np.all(np.abs(got_dk[s] - dk[s]) <= lim + 1e-6 * np.abs(dk[s]).max()), f"dk key {s} ({len(src)} rows)"
