@@ -726,8 +726,8 @@ def test_indexer_projections_bit_exact_on_integer_data():
 # ---------------------------------------------------------------------------
 # Training of the kept indexer: the group centroid and the KL backward
 # ---------------------------------------------------------------------------
-def _objective_case(B=2, L=320, k=128, H=32, n_layers=2, B_seed=0):
-    cfg = synth.get_config("prefill16k", L=L, Lq=L, B=B, topk=k, H=H)
+def _objective_case(B=2, L=320, k=128, H=32, n_layers=2, H_I=64):
+    cfg = synth.get_config("prefill16k", L=L, Lq=L, B=B, topk=k, H=H, H_I=H_I)
     ind = synth.indexer_inputs(cfg, device=DEV)
     idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k)
     layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(n_layers)]
@@ -752,13 +752,14 @@ def test_attention_centroid_parity(H):
         assert np.all(pbar[b][idx_h[b] < 0] == 0)
 
 
-def test_indexer_kl_backward_parity():
+@pytest.mark.parametrize("L,k,H_I", [(320, 128, 64), (200, 100, 32), (150, 64, 16), (130, 50, 48)])
+def test_indexer_kl_backward_parity(L, k, H_I):
     """Loss, dq, dw and dk against the oracle on the GPU's centroid.  Bounds: the
     coefficients c = g w [x > 0] enter the contractions rounded to bf16 (relative 2^-9,
     taken as 2^-8 over the sum of |terms|); g = pi - pbar carries the fp32 error of the
     scores and the softmax (1e-4 pi); pre-activations x within the fp32 accumulation error
     of 0 may take either ReLU branch, and their whole term is allowed."""
-    cfg, ind, idx, layers, lses = _objective_case(B=2, L=320, k=128)
+    cfg, ind, idx, layers, lses = _objective_case(B=2, L=L, k=k, H_I=H_I)
     pbar = dsa.attention_centroid(layers, idx, lses)
     out = dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar)
     got = {n: out[n].cpu().numpy().astype(np.float64) for n in out}
