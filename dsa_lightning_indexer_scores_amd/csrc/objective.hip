@@ -16,8 +16,8 @@
 // layer's queries, latent rows and log-sum-exp (that of dsa_sparse_attn), accumulated
 // with a weight: P[t, i] += alpha / H sum_h exp(sm_scale q[t, h] . K[S_t[i]] - lse[t, h]).
 //
-// indexer_kl_kernel: one workgroup per query row, selected keys in tiles of 64 gathered to
-// LDS (row-major for the scores, transposed for dq).  Pass 1 scores every tile (wave w
+// indexer_kl_kernel: one workgroup per query row (75 KB of LDS: two per CU), selected keys
+// in tiles of 64 gathered to LDS (row-major for the scores, transposed for dq).  Pass 1 scores every tile (wave w
 // owns heads 16w..16w+15; MFMA 16x16x32 bf16, fp32 accumulation) and keeps I in LDS; the
 // softmax, the loss and g = pi - pbar follow.  Pass 2 rescores each tile, forms c (rounded
 // to bf16 for the matrix cores), accumulates dw in fp32 and runs two more contractions:
@@ -34,8 +34,15 @@ constexpr int kLatent = 576;
 constexpr int kLatentPad = 584;   // LDS row of a query head: 16 rows of a read start in distinct banks
 constexpr int kDI = 128;          // indexer head dim
 constexpr int kTile = 64;         // selected keys per tile
-constexpr int kRowPadK = 136;     // LDS row (bf16) of a key in the row-major tile
-constexpr int kRowPad64 = 72;     // LDS row (bf16) of the 64-wide transposed / coefficient tiles
+// LDS tiles are unpadded; their 16-byte chunks are XOR-swizzled by the row so that the 16
+// rows one operand read touches start in different banks.  sw128: [rows][128] bf16 (the
+// row-major key tile), sw64: [rows][64] bf16 (transposed and coefficient tiles).
+__device__ __forceinline__ int sw128(int row, int col) {
+  return row * 128 + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
+}
+__device__ __forceinline__ int sw64(int row, int col) {
+  return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
+}
 }  // namespace
 
 template <int HB>
@@ -103,11 +110,11 @@ __global__ __launch_bounds__(256) void attn_probs_kernel(AttnProbsArgs a) {
 template <int HB>
 __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
   constexpr int H = 16 * HB;
-  __shared__ __attribute__((aligned(16))) __bf16 kt[kTile * kRowPadK];      // [key][dim]
-  __shared__ __attribute__((aligned(16))) __bf16 ktT[kDI * kRowPad64];      // [dim][key]
-  __shared__ __attribute__((aligned(16))) __bf16 qT[kDI * kRowPad64];       // [dim][head]
-  __shared__ __attribute__((aligned(16))) __bf16 cm[64 * kRowPad64];        // c [head][key]
-  __shared__ __attribute__((aligned(16))) __bf16 cmT[kTile * kRowPad64];    // c [key][head]
+  __shared__ __attribute__((aligned(16))) __bf16 kt[kTile * kDI];     // [key][dim], sw128
+  __shared__ __attribute__((aligned(16))) __bf16 ktT[kDI * kTile];    // [dim][key], sw64
+  __shared__ __attribute__((aligned(16))) __bf16 qT[kDI * 64];        // [dim][head], sw64
+  __shared__ __attribute__((aligned(16))) __bf16 cm[64 * kTile];      // c [head][key], sw64
+  __shared__ __attribute__((aligned(16))) __bf16 cmT[kTile * 64];     // c [key][head], sw64
   __shared__ float sc[kMaxKlK];                                              // I, then pi - pbar
   __shared__ float part[4][kTile];
   __shared__ float red[8];
@@ -129,7 +136,7 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
     const int h = e / kDI, d = e - h * kDI;
     __bf16 v = (__bf16)0.f;
     if (h < H) v = qrow[e];
-    qT[d * kRowPad64 + h] = v;
+    qT[sw64(d, h)] = v;
   }
   bf16x8 aq[4];
   float wh[4];
@@ -155,9 +162,9 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
       const int c = tid + 256 * u, key = c >> 4, ch = c & 15;
       const int s = sel[key];
       const bf16x8 v = *reinterpret_cast<const bf16x8*>(kbase + (size_t)(s >= 0 ? s : 0) * kDI + 8 * ch);
-      *reinterpret_cast<bf16x8*>(&kt[key * kRowPadK + 8 * ch]) = v;
+      *reinterpret_cast<bf16x8*>(&kt[sw128(key, 8 * ch)]) = v;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ktT[(8 * ch + e) * kRowPad64 + key] = v[e];
+      for (int e = 0; e < 8; ++e) ktT[sw64(8 * ch + e, key)] = v[e];
     }
     __syncthreads();
   };
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&kt[(16 * kb + l16) * kRowPadK + 32 * ks + 8 * g4]);
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&kt[sw128(16 * kb + l16, 32 * ks + 8 * g4)]);
         acc = mfma_bf16_16x16x32(aq[ks], bv, acc);
       }
       x[kb] = acc;
@@ -261,9 +268,9 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
           dwp[i] = fmaf(gk, fmaxf(x[kb][i], 0.f), dwp[i]);
           const float c = x[kb][i] > 0.f ? gk * wh[i] : 0.f;
           cv[i] = (__bf16)c;
-          cm[(16 * wv + 4 * g4 + i) * kRowPad64 + key] = cv[i];
+          cm[sw64(16 * wv + 4 * g4 + i, key)] = cv[i];
         }
-        *reinterpret_cast<bf16x4*>(&cmT[key * kRowPad64 + 16 * wv + 4 * g4]) = bf16x4{cv[0], cv[1], cv[2], cv[3]};
+        *reinterpret_cast<bf16x4*>(&cmT[sw64(key, 16 * wv + 4 * g4)]) = bf16x4{cv[0], cv[1], cv[2], cv[3]};
       }
     } else {
       // waves past the heads: zero coefficients so that the dk contraction over 64 head
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int key = 16 * kb + l16;
-        *reinterpret_cast<bf16x4*>(&cmT[key * kRowPad64 + 16 * wv + 4 * g4]) = bf16x4{0, 0, 0, 0};
+        *reinterpret_cast<bf16x4*>(&cmT[sw64(key, 16 * wv + 4 * g4)]) = bf16x4{0, 0, 0, 0};
       }
     }
     __syncthreads();
@@ -279,10 +286,10 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
     if (active) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cm[(16 * wv + l16) * kRowPad64 + 32 * ks + 8 * g4]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cm[sw64(16 * wv + l16, 32 * ks + 8 * g4)]);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ktT[(16 * db + l16) * kRowPad64 + 32 * ks + 8 * g4]);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&ktT[sw64(16 * db + l16, 32 * ks + 8 * g4)]);
           dq[db] = mfma_bf16_16x16x32(av, bv, dq[db]);
         }
       }
@@ -295,10 +302,10 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
 #pragma unroll
       for (int hs = 0; hs < 2; ++hs) {
         if (32 * hs >= H) break;
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cmT[(16 * wv + l16) * kRowPad64 + 32 * hs + 8 * g4]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cmT[sw64(16 * wv + l16, 32 * hs + 8 * g4)]);
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&qT[(16 * db + l16) * kRowPad64 + 32 * hs + 8 * g4]);
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&qT[sw64(16 * db + l16, 32 * hs + 8 * g4)]);
           acc[db] = mfma_bf16_16x16x32(av, bv, acc[db]);
         }
       }
