@@ -7,9 +7,9 @@
 // linear layer's weight).  The fp32 result feeds the per-token E4M3 quantization.
 //
 // One workgroup of 256 threads computes a 128 x 128 block of y.  K advances in 64-column
-// steps: the x and w tiles of the next step are loaded into registers while the current
-// step's tiles are read from LDS, then written to the other LDS buffer (last read in the
-// step before, which a barrier closed), so each step costs one workgroup barrier.  Each wave
+// steps: the x and w tiles of the next step are loaded straight into the other LDS buffer
+// (last read in the step before, which the step's barrier closed) while the current
+// step's tiles are read, so each step costs one wait and one workgroup barrier.  Each wave
 // owns a 64 x 64 quarter of the block: 4 x 4 MFMA 16x16x32 bf16 accumulators, two K
 // sub-steps of 32 per tile.  LDS rows are 64 bf16 = eight 16-byte chunks, stored with the
 // chunk index XOR-ed with (row & 7) so that the 16 rows one operand read touches start in
@@ -32,28 +32,22 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(const uint16_t* __rest
                                                           int N, int K, float* __restrict__ y, int64_t ldy) {
   __shared__ __attribute__((aligned(16))) bf16x8 lx[2][kLinTile * 8];
   __shared__ __attribute__((aligned(16))) bf16x8 lw[2][kLinTile * 8];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (LDS bases go to M0)
   const int m0 = blockIdx.y * kLinTile, n0 = blockIdx.x * kLinTile;
   const int wm = (wv >> 1) * 64, wn = (wv & 1) * 64;
 
-  // 128 rows x 8 chunks per operand: thread tid moves chunks tid + 256 u, u = 0..3.
-  // Rows past M or N re-read the last row; their results are never stored.
-  bf16x8 rx[4], rw[4];
-  auto load_regs = [&](int k0) {
+  // 128 rows x 8 chunks per operand, moved by direct-to-LDS loads: wave wv's load u fills
+  // LDS slots 64 (4u + wv) .. + 63 (eight rows), lane l the slot's row r and physical chunk
+  // pc, reading the row's logical chunk pc ^ (r & 7) (the swizzle above).  Rows past M or N
+  // re-read the last row; their results are never stored.
+  auto issue = [&](int k0, int buf) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u, r = c >> 3, ch = c & 7;
+      const int slot = 64 * (4 * u + wv) + lane, r = slot >> 3, pc = slot & 7, ch = pc ^ (r & 7);
       const int gm = min(m0 + r, M - 1), gn = min(n0 + r, N - 1);
-      rx[u] = *reinterpret_cast<const bf16x8*>(x + (size_t)gm * ldx + k0 + ch * 8);
-      rw[u] = *reinterpret_cast<const bf16x8*>(w + (size_t)gn * ldw + k0 + ch * 8);
-    }
-  };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + 256 * u, r = c >> 3, ch = c & 7;
-      lx[buf][lin_slot(r, ch)] = rx[u];
-      lw[buf][lin_slot(r, ch)] = rw[u];
+      dma_16(x + (size_t)gm * ldx + k0 + ch * 8, lds_offset(&lx[buf][64 * (4 * u + wv)]));
+      dma_16(w + (size_t)gn * ldw + k0 + ch * 8, lds_offset(&lw[buf][64 * (4 * u + wv)]));
     }
   };
 
@@ -64,12 +58,12 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(const uint16_t* __rest
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int n_steps = K / kLinK;
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
+  issue(0, 0);
   for (int kt = 0; kt < n_steps; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < n_steps) load_regs((kt + 1) * kLinK);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this step's tiles have landed
+    __syncthreads();                                     // ... for every wave; the other buffer is free
+    if (kt + 1 < n_steps) issue((kt + 1) * kLinK, cur ^ 1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       // lane l: row l % 16 of each 16-row block, K chunk 4 ks + l / 16 (8 bf16)
@@ -83,10 +77,6 @@ __global__ __launch_bounds__(256) void linear_bf16_kernel(const uint16_t* __rest
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma_bf16_16x16x32(a[i], b[j], acc[i][j]);
-    }
-    if (kt + 1 < n_steps) {
-      store_lds(cur ^ 1);   // the other buffer was last read in step kt - 1
-      __syncthreads();
     }
   }
 
