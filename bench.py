@@ -161,7 +161,9 @@ def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
         f"calibration_write_kib: {write[cid][1]:.2f}",
         f"read_scale: {f_scale:.4f}",
         f"write_scale: {w_scale:.4f}",
-        f"launches: {len(sel)} (of {n_all} dispatches; those reading under 1% of the largest are left out)",
+        "# launches: the dispatches that do the work (those reading under 1% of the largest are left out)",
+        f"dispatches: {n_all}",
+        f"launches: {len(sel)}",
         f"fetch_kib_per_launch: {f_kib:.1f}",
         f"write_kib_per_launch: {w_kib:.1f}",
         f"read_bytes_per_launch: {int(read_b)}",

@@ -40,3 +40,18 @@ def test_counter_summary_scales_by_the_calibration_copy(tmp_path):
     assert int(fields["launches"]) == 2
     # mean fetch 2000 KiB read twice over, mean write 20 KiB
     assert int(fields["traffic_bytes_per_launch"]) == 2000 * 1024 * 2 + 20 * 1024
+
+
+def test_counter_summary_leaves_out_dispatches_that_do_no_work(tmp_path):
+    """A dispatch reading under 1% of the largest (the fused indexer's recompute pass when
+    no item failed) does not dilute the per-launch figures."""
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    k = "void dsa::indexer_topk_kernel<2, 4>(dsa::FusedParams)"
+    _csv(fetch, [(3, k, "FETCH_SIZE", 4000.0), (4, k, "FETCH_SIZE", 2.0),
+                 (9, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 524288.0)])
+    _csv(write, [(3, k, "WRITE_SIZE", 100.0), (4, k, "WRITE_SIZE", 1.0),
+                 (9, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1048576.0)])
+    text = bench.summarize_counters(str(fetch), str(write), "indexer_topk_kernel", "<2, 4>", "w")
+    fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
+    assert int(fields["dispatches"]) == 2 and int(fields["launches"]) == 1
+    assert int(fields["traffic_bytes_per_launch"]) == 4000 * 1024 * 2 + 100 * 1024
