@@ -150,6 +150,8 @@ FUSED_CASES = [
     ("fp8", 1, 20000, 20000, 256),
     ("bf16", 1, 12000, 12000, 512),
     ("fp8", 1, 2048, 65536, 256),      # 8 key segments, 2048 items: checked by the merge
+    ("fp8", 1, 9000, 9000, 1),         # k = 1: the sampled threshold sits near the sample's top
+    ("bf16", 1, 12000, 12000, 4096),   # the largest k: the threshold deep in the sample
 ]
 
 
