@@ -391,6 +391,17 @@ def main():
     if not args.no_quant:
         result["quantize"] = bench_quantize(dsa, torch, np, dev, stream)
         result["projections"] = bench_projections(dsa, torch, np, dev, stream)
+    att = bench_attainable(torch, dev, stream)
+    result["attainable"] = att
+    kk = result.get("kernels", {})
+    if att.get("fp8_gemm_tflops") and "indexer_topk" in kk and cfg.idx_dtype == "fp8":
+        kk["indexer_topk"]["frac_of_attainable_fp8_gemm"] = round(kk["indexer_topk"]["tflops"] / att["fp8_gemm_tflops"], 4)
+    if "sparse_attn" in kk:
+        kk["sparse_attn"]["frac_of_attainable_bf16_gemm"] = round(kk["sparse_attn"]["tflops"] / att["bf16_gemm_tflops"], 4)
+    if "decode" in result:
+        dc = result["decode"]
+        dc["indexer_frac_of_copy"] = round(dc["indexer_hbm_gbs"] / att["copy_gbs"], 4)
+        dc["attn_gather_frac_of_copy"] = round(dc["attn_gather_gbs"] / att["copy_gbs"], 4)
     if not args.no_train:
         result["indexer_training"] = bench_objective(dsa, synth, torch, dev, stream)
 
@@ -533,6 +544,53 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
            "varlen": varlen, "fp8_latent": fp8_kv, "paged": paged}
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
+    return out
+
+
+def bench_attainable(torch, dev, stream):
+    """Measured ceilings on this GPU, for context beside the datasheet peaks: a large bf16
+    GEMM and, where torch provides it, an fp8 one (hipBLASLt through torch; measurement only,
+    never on the library's path), and a 2 GiB device copy (read + write bytes)."""
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = 8192
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    a = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    b = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    out = {"gemm_shape": [n, n, n]}
+    ms = timed(lambda: torch.matmul(a, b))
+    out["bf16_gemm_tflops"] = round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.to(torch.float8_e4m3fn).t().contiguous().t()      # column-major right operand
+        one = torch.ones((), device=dev, dtype=torch.float32)
+        ms8 = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+        out["fp8_gemm_tflops"] = round(2.0 * n ** 3 / (ms8 * 1e-3) / 1e12, 1)
+        del a8, b8
+    except Exception as e:                                     # not provided by this torch build
+        out["fp8_gemm_tflops"] = None
+        out["fp8_gemm_note"] = f"unavailable: {type(e).__name__}"
+    del a, b
+    x = torch.empty(1 << 29, device=dev, dtype=torch.float32)
+    y = torch.empty_like(x)
+    x.fill_(1.0)
+    msc = timed(lambda: y.copy_(x))
+    out["copy_gbs"] = round(2.0 * x.numel() * 4 / (msc * 1e-3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    log(f"[bench] attainable: bf16 GEMM {out['bf16_gemm_tflops']} TFLOP/s, fp8 GEMM {out['fp8_gemm_tflops']} "
+        f"TFLOP/s, device copy {out['copy_gbs']} GB/s")
     return out
 
 
