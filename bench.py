@@ -21,6 +21,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -43,6 +44,18 @@ PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuff
                '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
                '--no-chunk1m --no-quant --no-train --copy-calibration')
 COPY_BYTES = 1 << 30
+# Counter passes for the execution profile of a kernel (each within one rocprofv3 pass's
+# limits on gfx950: at most 8 SQ, 4 TCC, 4 TCP, 2 TA and 2 GRBM counters).
+PMC_PASSES = {
+    "sq_issue": "SQ_VALU_MFMA_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+                "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_BUSY_CU_CYCLES GRBM_GUI_ACTIVE",
+    "sq_wait": "SQ_WAVE_CYCLES SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_ACTIVE_INST_ANY SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+               "SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_VALU_MFMA_COEXEC_CYCLES SQ_INST_CYCLES_VMEM_RD GRBM_GUI_ACTIVE",
+    "l2": "TCC_HIT_sum TCC_MISS_sum TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_WRITE_DRAM_32B_sum GRBM_GUI_ACTIVE",
+    "l1": "TCP_TCC_READ_REQ_sum TCP_TCC_READ_REQ_LATENCY_sum TCP_PENDING_STALL_CYCLES_sum "
+          "TCP_TCP_TA_DATA_STALL_CYCLES_sum TA_TA_BUSY_sum TA_ADDR_STALLED_BY_TC_CYCLES_sum GRBM_GUI_ACTIVE",
+}
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
 
 
 class Work:
@@ -72,9 +85,21 @@ class Work:
         return 2 * H * (Dqk + Dv) * pairs
 
 
+def kernel_sources(kernel):
+    """The library sources a kernel is built from: the csrc file that defines it, plus the
+    shared headers and build flags."""
+    if kernel in KERNEL_SOURCES:
+        return KERNEL_SOURCES[kernel]
+    found = []
+    for f in sorted(os.listdir(os.path.join(PKG, "csrc"))):
+        if f.endswith(".hip") and re.search(r"\b" + re.escape(kernel) + r"\s*\(", open(os.path.join(PKG, "csrc", f)).read()):
+            found.append("csrc/" + f)
+    return found
+
+
 def source_digest(kernel):
     h = hashlib.sha256()
-    for rel in sorted(KERNEL_SOURCES[kernel] + COMMON_SOURCES):
+    for rel in sorted(kernel_sources(kernel) + COMMON_SOURCES):
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(rel.encode())
             h.update(f.read())
@@ -174,6 +199,94 @@ def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
     return "\n".join(lines)
 
 
+def summarize_pmc(csvs, kernel, template, workload, command):
+    """Execution profile of one kernel from rocprofv3 counter runs (PMC_PASSES): the mean per
+    launch of every counter, then the fractions derived from them.  Launches are matched by
+    their order among the kernel's dispatches in each run; dispatches with a duration under
+    1% of the longest (the fused indexer's recompute pass when nothing failed) are left out."""
+    per_run = []
+    for path in csvs:
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if kernel not in name or template not in name:
+                    continue
+                d = rows.setdefault(int(r["Dispatch_Id"]), {"name": name, "ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+        per_run.append([rows[d] for d in sorted(rows)])
+    if not per_run or not per_run[0]:
+        raise SystemExit(f"no dispatches of {kernel}{template}")
+    n = min(len(r) for r in per_run)
+    top = max(d["ns"] for r in per_run for d in r[:n])
+    keep = [i for i in range(n) if all(r[i]["ns"] >= 0.01 * top for r in per_run)]
+    vals, ns = {}, []
+    for i in keep:
+        for r in per_run:
+            ns.append(r[i]["ns"])
+            for c, v in r[i].items():
+                if c not in ("name", "ns"):
+                    vals.setdefault(c, []).append(v)
+    mean = {c: sum(v) / len(v) for c, v in vals.items()}
+    lines = [f"# rocprofv3 counters of dsa::{kernel}{template}, workload {workload}",
+             "# commands, from the repository root on one MI355X (cd /tmp && export TMPDIR=/tmp first), one per pass:"]
+    for pname, ctrs in PMC_PASSES.items():
+        lines.append("#   " + command.format(counters=ctrs, dir=f"<{pname}_dir>"))
+    lines.append(f"#   python3 bench.py --summarize-pmc <each pass dir>/run_counter_collection.csv ... "
+                 f"--kernel {kernel} --template '{template}' --workload {workload}")
+    lines.append(f"dispatches_per_run: {n}")
+    lines.append(f"launches: {len(keep)}")
+    lines.append(f"mean_duration_us_under_counters: {sum(ns) / len(ns) / 1e3:.1f}")
+    for c in sorted(mean):
+        lines.append(f"{c}: {mean[c]:.6g}")
+    # derived fractions; GRBM_GUI_ACTIVE is summed over the XCDs by the CSV, so the busy
+    # clock of the launch is that sum / XCDs; SQ_ACTIVE_* and SQ_WAVE_CYCLES count quad-cycles
+    gui = mean.get("GRBM_GUI_ACTIVE")
+    def put(name, v, note):
+        lines.append(f"{name}: {v:.4f}    # {note}")
+    if gui:
+        clk = gui / N_XCD
+        lines.append(f"busy_cycles_per_xcd: {clk:.6g}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            put("mfma_busy_frac", mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (clk * N_SIMD), "SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)")
+        if "SQ_ACTIVE_INST_VALU" in mean:
+            put("valu_busy_frac", 4 * mean["SQ_ACTIVE_INST_VALU"] / (clk * N_SIMD), "4 x SQ_ACTIVE_INST_VALU / (cycles x 1024 SIMDs)")
+        if "SQ_LDS_IDX_ACTIVE" in mean:
+            put("lds_active_frac", mean["SQ_LDS_IDX_ACTIVE"] / (clk * N_CU), "SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs)")
+        if "SQ_LDS_BANK_CONFLICT" in mean:
+            put("lds_bank_conflict_frac", mean["SQ_LDS_BANK_CONFLICT"] / (clk * N_CU), "SQ_LDS_BANK_CONFLICT / (cycles x 256 CUs)")
+        if "SQ_VALU_MFMA_COEXEC_CYCLES" in mean:
+            put("mfma_valu_coexec_frac", mean["SQ_VALU_MFMA_COEXEC_CYCLES"] / (clk * N_SIMD), "SQ_VALU_MFMA_COEXEC_CYCLES / (cycles x 1024 SIMDs)")
+        if "TA_TA_BUSY_sum" in mean:
+            put("ta_busy_frac", mean["TA_TA_BUSY_sum"] / (clk * N_CU), "TA_TA_BUSY_sum / (cycles x 256 CUs)")
+        if "TCP_PENDING_STALL_CYCLES_sum" in mean:
+            put("l1_pending_stall_frac", mean["TCP_PENDING_STALL_CYCLES_sum"] / (clk * N_CU), "TCP_PENDING_STALL_CYCLES_sum / (cycles x 256 CUs)")
+    if "SQ_WAVE_CYCLES" in mean and "SQ_WAIT_INST_ANY" in mean:
+        put("wave_wait_inst_frac", mean["SQ_WAIT_INST_ANY"] / mean["SQ_WAVE_CYCLES"], "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES")
+    if "SQ_WAVE_CYCLES" in mean and "SQ_ACTIVE_INST_ANY" in mean:
+        put("wave_issue_frac", mean["SQ_ACTIVE_INST_ANY"] / mean["SQ_WAVE_CYCLES"], "SQ_ACTIVE_INST_ANY / SQ_WAVE_CYCLES")
+    if "TCC_HIT_sum" in mean and "TCC_MISS_sum" in mean:
+        put("l2_hit_frac", mean["TCC_HIT_sum"] / max(1.0, mean["TCC_HIT_sum"] + mean["TCC_MISS_sum"]), "TCC_HIT / (TCC_HIT + TCC_MISS)")
+    if "TCC_EA0_RDREQ_DRAM_32B_sum" in mean:
+        lines.append(f"l2_miss_read_bytes_per_launch: {int(32 * mean['TCC_EA0_RDREQ_DRAM_32B_sum'])}    "
+                     f"# 32 x TCC_EA0_RDREQ_DRAM_32B: L2 misses to the memory side (served by the Infinity Cache or HBM)")
+    if "TCC_EA0_WRREQ_WRITE_DRAM_32B_sum" in mean:
+        lines.append(f"l2_write_bytes_per_launch: {int(32 * mean['TCC_EA0_WRREQ_WRITE_DRAM_32B_sum'])}    "
+                     f"# 32 x TCC_EA0_WRREQ_WRITE_DRAM_32B")
+    if "TCP_TCC_READ_REQ_sum" in mean and "TCP_TCC_READ_REQ_LATENCY_sum" in mean:
+        put("l1_to_l2_read_latency_cycles", mean["TCP_TCC_READ_REQ_LATENCY_sum"] / max(1.0, mean["TCP_TCC_READ_REQ_sum"]),
+            "TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum")
+    if "SQ_INSTS_MFMA" in mean and "SQ_INSTS_VALU" in mean:
+        put("valu_insts_per_mfma", (mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]) / max(1.0, mean["SQ_INSTS_MFMA"]),
+            "(SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (SQ_INSTS_VALU includes the MFMAs)")
+    for dt in ("BF16", "F8"):
+        c = f"SQ_INSTS_VALU_MFMA_MOPS_{dt}"
+        if mean.get(c):
+            lines.append(f"mfma_flops_{dt.lower()}_per_launch: {mean[c] * 512:.6g}    # 512 x {c}")
+    lines.append(f"source_digest: {source_digest(kernel)}")
+    return "\n".join(lines)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -197,6 +310,12 @@ def parse():
                     help="print the HBM traffic summary of two rocprofv3 counter runs and exit")
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="print per (kernel, grid) launch statistics of a rocprofv3 kernel trace and exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="CSV",
+                    help="print the execution profile (PMC_PASSES counter runs) of --kernel and exit")
+    ap.add_argument("--pmc-command", default="",
+                    help="the benchmark command the counter runs profiled (recorded in the summary)")
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the library GEMM and device-copy reference measurements")
     ap.add_argument("--kernel", default="mla_attn32_kernel")
     ap.add_argument("--template", default="")
     return ap.parse_args()
@@ -209,6 +328,11 @@ def main():
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.kernel, args.template, args.workload))
+        return
+    if args.summarize_pmc:
+        cmd = ('rocprofv3 --pmc {counters} --kernel-include-regex "dsa::" --output-format csv -d {dir} -o run -- '
+               + (args.pmc_command or "python3 bench.py ..."))
+        print(summarize_pmc(args.summarize_pmc, args.kernel, args.template, args.workload, cmd))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "the library and this benchmark run on one GPU; --gpus must be 1"}))
@@ -391,17 +515,10 @@ def main():
     if not args.no_quant:
         result["quantize"] = bench_quantize(dsa, torch, np, dev, stream)
         result["projections"] = bench_projections(dsa, torch, np, dev, stream)
-    att = bench_attainable(torch, dev, stream)
-    result["attainable"] = att
-    kk = result.get("kernels", {})
-    if att.get("fp8_gemm_tflops") and "indexer_topk" in kk and cfg.idx_dtype == "fp8":
-        kk["indexer_topk"]["frac_of_attainable_fp8_gemm"] = round(kk["indexer_topk"]["tflops"] / att["fp8_gemm_tflops"], 4)
-    if "sparse_attn" in kk:
-        kk["sparse_attn"]["frac_of_attainable_bf16_gemm"] = round(kk["sparse_attn"]["tflops"] / att["bf16_gemm_tflops"], 4)
-    if "decode" in result:
-        dc = result["decode"]
-        dc["indexer_frac_of_copy"] = round(dc["indexer_hbm_gbs"] / att["copy_gbs"], 4)
-        dc["attn_gather_frac_of_copy"] = round(dc["attn_gather_gbs"] / att["copy_gbs"], 4)
+    if not args.no_attainable:
+        # context only: what torch's library GEMMs and a device copy reach on this GPU (the
+        # roofline fractions are taken against the datasheet peaks, never against these)
+        result["library_reference"] = bench_attainable(torch, dev, stream)
     if not args.no_train:
         result["indexer_training"] = bench_objective(dsa, synth, torch, dev, stream)
 

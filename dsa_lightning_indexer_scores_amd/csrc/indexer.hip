@@ -174,17 +174,12 @@ __device__ __forceinline__ float tile_score(const Op<DT> (&a)[HB], const Op<DT> 
 // every fourth 64-key tile of the chunk, reading k^I straight from HBM (no reuse).
 // ---------------------------------------------------------------------------
 // Keys per workgroup: chosen so that rows x chunks fills the resident workgroup slots
-// (4 per CU) about once, without a partial last wave of workgroups.
+// (4 per CU on the 256 CUs of gfx950) about once, without a partial last wave of
+// workgroups.  The plan depends only on the sizes, so the workspace it implies is pure host
+// arithmetic and every call with the same sizes makes the same launches.
+constexpr long long kResidentSlots = 4LL * 256;
 static int rowscan_chunk(int rows, int Lk) {
-  static int n_cu = 0;
-  if (n_cu == 0) {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess && hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      n_cu = v;
-    else
-      n_cu = 256;
-  }
-  const long long target = 4LL * n_cu;
+  const long long target = kResidentSlots;
   long long per_row = (target + rows - 1) / rows;
   const long long max_chunks = (Lk + 255) / 256;
   if (per_row > max_chunks) per_row = max_chunks;

@@ -1,7 +1,8 @@
 // Deterministic top-k over materialised score rows (gfx950).
 //
 // GLM-5.2 技术报告速览, section "IndexShare": keep the k highest indexer scores of each
-// query; GLM-5 technical report, section 3.2: the top-k operator must be deterministic.
+// query; GLM-5 technical report, section 3.2, paragraph "DSA RL 要点": the top-k operator must be
+// deterministic.
 //
 // One workgroup per row.  Scores are mapped to order-preserving uint32 keys.  From a
 // 2048-bin histogram of the top 11 key bits (built by the score kernel, or by one pass

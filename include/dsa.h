@@ -13,8 +13,8 @@
  *      the selected positions' K/V of its own layer and recomputes score, softmax and
  *      value aggregation; only top-k position IDs cross layers; MLA decode uses the
  *      576-d latent: 512-d compressed KV + 64-d RoPE key).
- *  [C] GLM-5 technical report, section 3.2 "DSA 强化学习洞察": the top-k operator must
- *      be deterministic.
+ *  [C] GLM-5 technical report (Chinese translation), section 3.2 "Reasoning RL",
+ *      paragraph "DSA RL 要点": the top-k operator must be deterministic.
  *
  * Conventions (all entry points):
  *  - Every pointer argument is DEVICE memory owned by the caller, except the struct

@@ -17,8 +17,8 @@ the pages:
   "DSA 与 IndexShare 的组合数据流" (sparse core attention recomputes score,
   softmax and value aggregation on the selected positions only; only the top-k
   position IDs flow across layers).
-* GLM-5 technical report, section 3.2 "DSA 强化学习洞察" (the top-k operator must
-  be deterministic).
+* GLM-5 technical report (Chinese translation), section 3.2 "Reasoning RL",
+  paragraph "DSA RL 要点" (the top-k operator must be deterministic).
 
 Pins: every function here is checked by the ``-m "not gpu"`` tests against
 hand-worked examples, closed forms, invariants and library routines (see

@@ -67,3 +67,17 @@ def index_sets_agree(gpu_idx, ora_idx, ora_scores, n_valid, k, tau):
                 return False, r, f"row {r}: position {s} score {sc[s]} outside band of theta {theta}"
         bad += 1
     return True, bad, msg
+
+
+def poisoned(shape, dtype, device="cuda"):
+    """An output buffer filled with a value no kernel writes (NaN for floats, 0x7F7F7F7F for
+    index rows), so that a test can check that every element was written."""
+    if dtype == torch.int32:
+        return torch.full(shape, 0x7F7F7F7F, dtype=torch.int32, device=device)
+    return torch.full(shape, float("nan"), dtype=dtype, device=device)
+
+
+def all_written(t):
+    if t.dtype == torch.int32:
+        return not bool((t == 0x7F7F7F7F).any())
+    return not bool(torch.isnan(t).any())

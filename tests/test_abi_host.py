@@ -263,3 +263,93 @@ def test_objective_argument_errors():
     assert kl(st=_indexer_struct(H_I=8)) == -3                  # H_I a multiple of 16
     assert kl(st=_indexer_struct(d_I=64)) == -3                 # d_I = 128
     assert kl(dk=0x9002) == -4
+
+
+# ---------------------------------------------------------------------------
+# The binding checks dtypes, shapes and batch sizes before a pointer reaches a kernel (a
+# kernel indexes every tensor by sizes taken from the others).  The checks run on host
+# tensors: a wrong dtype or shape is reported as such, and a correct one gets as far as the
+# device check.
+# ---------------------------------------------------------------------------
+
+def _raises(fn, *words):
+    with pytest.raises(ValueError) as e:
+        fn()
+    msg = str(e.value)
+    assert all(w in msg for w in words), msg
+
+
+def _fp8_indexer(B=2, Lq=8, Lk=16, H=16, d=128):
+    return dict(q=torch.zeros(B, Lq, H, d, dtype=torch.uint8), k=torch.zeros(B, Lk, d, dtype=torch.uint8),
+                w=torch.zeros(B, Lq, H), q_scale=torch.ones(B, Lq), k_scale=torch.ones(B, Lk))
+
+
+def test_binding_checks_indexer_operands():
+    good = _fp8_indexer()
+    f = lambda **kw: dsa._indexer_struct(**{**good, **kw})
+    _raises(lambda: f(), "q", "on the GPU")                                   # passes dtype/shape checks
+    _raises(lambda: f(k=torch.zeros(2, 16, 128, dtype=torch.bfloat16)), "k", "dtype")
+    _raises(lambda: f(k=torch.zeros(2, 16, 64, dtype=torch.uint8)), "k", "shape")
+    _raises(lambda: f(k=torch.zeros(1, 16, 128, dtype=torch.uint8)), "k", "shape")   # batch
+    _raises(lambda: f(w=torch.zeros(2, 8, 16, dtype=torch.bfloat16)), "w", "dtype")
+    _raises(lambda: f(w=torch.zeros(2, 8, 8)), "w", "shape")
+    _raises(lambda: f(q_scale=None), "q_scale", "required")
+    _raises(lambda: f(k_scale=torch.ones(2, 15)), "k_scale", "shape")
+    _raises(lambda: f(q_scale=torch.ones(2, 8, dtype=torch.float64)), "q_scale", "dtype")
+    bf = dict(q=torch.zeros(1, 4, 16, 128, dtype=torch.bfloat16), k=torch.zeros(1, 4, 128, dtype=torch.bfloat16),
+              w=torch.zeros(1, 4, 16), q_scale=None, k_scale=None)
+    _raises(lambda: dsa._indexer_struct(**bf), "q", "on the GPU")
+    _raises(lambda: dsa._indexer_struct(**{**bf, "q_scale": torch.ones(1, 4)}), "scales")
+    _raises(lambda: dsa._indexer_struct(**{**bf, "k": torch.zeros(1, 4, 128, dtype=torch.uint8)}), "k", "dtype")
+
+
+def _mla_layer(B=2, Lq=4, Lk=32, H=32):
+    return {"q": torch.zeros(B, Lq, H, 576, dtype=torch.bfloat16), "kv": torch.zeros(B, Lk, 576, dtype=torch.bfloat16),
+            "sm_scale": 576 ** -0.5, "Dv": 512}
+
+
+def test_binding_checks_attention_operands():
+    lay = _mla_layer()
+    out = torch.zeros(2, 4, 32, 512, dtype=torch.bfloat16)
+    _raises(lambda: dsa._attn_struct(lay, out, None), "q", "on the GPU")
+    _raises(lambda: dsa._attn_struct({**lay, "kv": torch.zeros(2, 32, 576)}, out, None), "kv", "dtype")
+    _raises(lambda: dsa._attn_struct({**lay, "kv": torch.zeros(1, 32, 576, dtype=torch.bfloat16)}, out, None),
+            "kv", "shape")
+    _raises(lambda: dsa._attn_struct({**lay, "kv": torch.zeros(2, 32, 512, dtype=torch.bfloat16)}, out, None),
+            "shorter")
+    _raises(lambda: dsa._attn_struct(lay, torch.zeros(2, 4, 32, 512, dtype=torch.float16), None), "out", "dtype")
+    _raises(lambda: dsa._attn_struct(lay, torch.zeros(2, 4, 16, 512, dtype=torch.bfloat16), None), "out", "shape")
+    _raises(lambda: dsa._attn_struct(lay, out, torch.zeros(2, 4, 16)), "lse", "shape")
+    _raises(lambda: dsa._attn_struct(lay, out, torch.zeros(2, 4, 32)), "q", "on the GPU")
+    kv8 = {**lay, "kv": torch.zeros(2, 32, 576, dtype=torch.uint8), "kv_scale": torch.ones(2, 31)}
+    _raises(lambda: dsa._attn_struct(kv8, out, None), "kv_scale", "shape")
+    kv8["kv_scale"] = torch.ones(2, 32)
+    _raises(lambda: dsa._attn_struct(kv8, out, None), "q", "on the GPU")
+    _raises(lambda: dsa._attn_struct({**kv8, "kv": torch.zeros(2, 32, 576, dtype=torch.bfloat16)}, out, None),
+            "kv", "dtype")
+    mha = {"q": torch.zeros(1, 4, 4, 64), "k": torch.zeros(1, 8, 2, 64), "v": torch.zeros(1, 8, 2, 32, dtype=torch.bfloat16),
+           "sm_scale": 0.125}
+    _raises(lambda: dsa._attn_struct(mha, torch.zeros(1, 4, 4, 32), None), "v", "dtype")
+    mha["v"] = torch.zeros(1, 8, 2, 32)
+    _raises(lambda: dsa._attn_struct(mha, torch.zeros(1, 4, 4, 32), None), "q", "on the GPU")
+
+
+def test_binding_checks_index_rows():
+    _raises(lambda: dsa._check_idx(torch.zeros(2, 4, 64, dtype=torch.int64), 2, 4, 64, 64, None), "idx", "dtype")
+    _raises(lambda: dsa._check_idx(torch.zeros(2, 3, 64, dtype=torch.int32), 2, 4, 64, 64, None), "idx", "shape")
+    _raises(lambda: dsa._check_idx(torch.zeros(2, 4, 64, dtype=torch.int32), 2, 4, 64, 0, None), "idx", "shape")
+    _raises(lambda: dsa._check_idx(torch.zeros(2, 4, 64, dtype=torch.int32), 2, 4, 64, 128, None), "idx_q_stride")
+    _raises(lambda: dsa._check_idx(torch.zeros(2, 1, 64, dtype=torch.int32), 2, 4, 64, 0, None), "on the GPU")
+    # the public calls check before allocating or launching
+    lay = _mla_layer()
+    _raises(lambda: dsa.sparse_attn(lay, torch.zeros(2, 4, 64, dtype=torch.int64)), "idx", "dtype")
+    _raises(lambda: dsa.topk(torch.zeros(4, 100, dtype=torch.float64), 8), "scores", "dtype")
+    _raises(lambda: dsa.topk(torch.zeros(4, 100), 8, n_valid=torch.zeros(4, dtype=torch.int64)), "n_valid", "dtype")
+    _raises(lambda: dsa.topk(torch.zeros(4, 100), 8, n_valid=torch.zeros(3, dtype=torch.int32)), "n_valid", "shape")
+    ind = _fp8_indexer()
+    _raises(lambda: dsa.indexer_topk(ind["q"], ind["k"], ind["w"].double(), 4, q_scale=ind["q_scale"],
+                                     k_scale=ind["k_scale"]), "w", "dtype")
+    _raises(lambda: dsa.indexer_kl_backward(torch.zeros(1, 4, 16, 128, dtype=torch.bfloat16),
+                                            torch.zeros(1, 8, 128, dtype=torch.bfloat16), torch.zeros(1, 4, 16),
+                                            torch.zeros(1, 4, 8, dtype=torch.int32), torch.zeros(1, 4, 7)),
+            "q", "on the GPU")

@@ -130,3 +130,46 @@ def test_integer_inputs_give_exact_integer_scores():
         dots = qi[0, t] @ ki[0, : t + 1].T
         exact = wi[0, t] @ np.maximum(dots, 0)
         assert np.array_equal(I[0, t, : t + 1], exact.astype(np.float64))
+
+
+def _triple_loop_scores(q, k, w, Lk):
+    """The indexer-score equation written out as plain Python loops over (query, key, head,
+    dim), with the causal rule s <= p_i, p_i = Lk - Lq + i; keys past p_i get -inf."""
+    Lq, H, d = len(q), len(q[0]), len(q[0][0])
+    out = []
+    for i in range(Lq):
+        p = Lk - Lq + i
+        row = []
+        for s in range(Lk):
+            if s > p:
+                row.append(float("-inf"))
+                continue
+            total = 0.0
+            for j in range(H):
+                dot = 0.0
+                for e in range(d):
+                    dot += q[i][j][e] * k[s][e]
+                total += w[i][j] * (dot if dot > 0.0 else 0.0)
+            row.append(total)
+        out.append(row)
+    return out
+
+
+def test_matches_triple_loop_on_tiny_inputs():
+    # Brute force on tiny shapes, signed weights, and queries that are the last Lq of Lk
+    # positions (so the causal offset is exercised); agreement to rtol 1e-12.
+    rng = np.random.default_rng(11)
+    for (Lq, Lk, H, d) in [(12, 12, 3, 4), (5, 9, 2, 3), (1, 7, 3, 4)]:
+        q = rng.standard_normal((Lq, H, d))
+        k = rng.standard_normal((Lk, d))
+        w = rng.standard_normal((Lq, H))
+        ref = np.array(_triple_loop_scores(q.tolist(), k.tolist(), w.tolist(), Lk))
+        got = indexer_scores_rows(q, k, w, range(Lq), Lk)
+        assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+        f = np.isfinite(ref)
+        np.testing.assert_allclose(got[f], ref[f], rtol=1e-12, atol=1e-14)
+        # the batched entry point agrees with the row form when Lq == Lk
+        if Lq == Lk:
+            full = indexer_scores(q[None], k[None], w[None])[0]
+            assert np.array_equal(np.isneginf(full), np.isneginf(ref))
+            np.testing.assert_allclose(full[f], ref[f], rtol=1e-12, atol=1e-14)
