@@ -18,7 +18,7 @@ __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
     "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
-    "sparse_attn", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "attention_centroid",
+    "sparse_attn", "sparse_attn_noalloc", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "attention_centroid",
     "indexer_kl_backward", "Workspace",
 ]
 
@@ -78,6 +78,7 @@ def load_library():
     lib.dsa_paged_rows.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, vp, vp]
     lib.dsa_sparse_attn.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp, sz, vp]
     lib.dsa_sparse_attn_kv8.argtypes = [ctypes.POINTER(_AttnIn), vp, i32, i32, i32, vp, i64, i32, vp, sz, vp]
+    lib.dsa_sparse_attn_noalloc.argtypes = [ctypes.POINTER(_AttnIn), i32, i32, i32, vp, i64, i32, vp]
     lib.dsa_layer_group.argtypes = [ctypes.POINTER(_IndexerIn), ctypes.POINTER(_AttnIn), i32, i32, i32,
                                     i32, i32, vp, vp, sz, vp]
     lib.dsa_layer_schedule.argtypes = [i32, i32, i32, ctypes.c_char_p, ctypes.POINTER(ctypes.c_int32)]
@@ -88,7 +89,8 @@ def load_library():
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
-               "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_sparse_attn_kv8", "dsa_layer_group",
+               "dsa_indexer_topk_paged", "dsa_paged_rows", "dsa_sparse_attn", "dsa_sparse_attn_kv8",
+               "dsa_sparse_attn_noalloc", "dsa_layer_group",
                "dsa_layer_schedule", "dsa_quantize_e4m3", "dsa_linear_bf16", "dsa_attn_probs",
                "dsa_indexer_kl_backward"):
         getattr(lib, fn).restype = i32
@@ -430,6 +432,27 @@ def sparse_attn(layer, idx, idx_q_stride=None, return_lse=False, ws=None, out=No
         _check("dsa_sparse_attn", load_library().dsa_sparse_attn(
             ctypes.byref(s), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _ptr(buf), nbytes, _stream(stream)))
     return (out, lse) if return_lse else out
+
+
+def sparse_attn_noalloc(layer, idx, out, lse=None, idx_q_stride=None, stream=None):
+    """sparse_attn through dsa_sparse_attn_noalloc: the split-key partials go to the library's
+    own device buffer, so the call allocates nothing.  out [B, Lq, H, Dv] (and lse
+    [B, Lq, H] float32, optional) are the caller's; bf16 latent caches only.  Calls that
+    overlap on one GPU race (they share the buffer)."""
+    q = layer["q"]
+    if q is None or q.dim() != 4 or idx is None or idx.dim() != 3:
+        raise ValueError("q must be [B, Lq, H, Dqk] and idx [B, Lq | 1, k]")
+    if layer.get("kv_scale") is not None:
+        raise ValueError("dsa_sparse_attn_noalloc takes bf16 latent caches")
+    B, Lq = q.shape[0], q.shape[1]
+    k = idx.shape[-1]
+    if idx_q_stride is None:
+        idx_q_stride = 0 if idx.shape[1] == 1 and Lq > 1 else k
+    _check_idx(idx, B, Lq, k, idx_q_stride, q.device)
+    s, Lk, _ = _attn_struct(layer, out, lse)
+    _check("dsa_sparse_attn_noalloc", load_library().dsa_sparse_attn_noalloc(
+        ctypes.byref(s), B, Lq, Lk, _ptr(idx), idx_q_stride, k, _stream(stream)))
+    return out
 
 
 def layer_group(full, layers, topk_k, ws=None, return_lse=False, outs=None, idx_out=None, out_dtype=None,

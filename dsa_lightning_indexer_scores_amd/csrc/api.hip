@@ -5,6 +5,13 @@
 
 #include <stdint.h>
 
+#include <mutex>
+
+// Device buffer of dsa_sparse_attn_noalloc (split-key partial results), one copy on each
+// GPU the library runs on.  Host code never uses this name as an address: the device
+// address of each GPU's copy is looked up once (noalloc_scratch below) and passed on.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 constexpr int kMaxFusedK = 4096;
@@ -153,6 +160,39 @@ int run_indexer_topk(const dsa_indexer_in* in, int B, int Lq, int Lk, int k, int
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // device address of `scratch` on each GPU
+
+// The device address of the scratch buffer on the device of `stream` (the current device
+// for the null stream), looked up with that device current on its first use.
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return DSA_ERR_HIP;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return DSA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return DSA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return DSA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return DSA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return DSA_ERR_HIP;
+    if (e != hipSuccess || !p) return DSA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t dsa_workspace_size(int op, int dtype, int B, int Lq, int Lk, int k, int heads) {
@@ -284,6 +324,23 @@ int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t*
   if (need > 0 && (!ws || ws_bytes < need)) return DSA_ERR_WORKSPACE;
   if (ws && !aligned(ws, 256)) return DSA_ERR_ALIGN;
   const hipError_t e = dsa::launch_sparse_attn(make_attn_args(in, B, Lq, Lk, idx, idx_q_stride, k), ws, ws_bytes,
+                                               static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
+}
+
+int dsa_sparse_attn_noalloc(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx, int64_t idx_q_stride,
+                            int k, void* stream) {
+  int st = check_attn(in, B, Lq, Lk, idx, idx_q_stride, k);
+  if (st != DSA_OK) return st;
+  const size_t need = dsa::sparse_attn_ws(B, Lq, k, in->H, idx_q_stride, in->dtype);
+  if (need > DSA_NOALLOC_SCRATCH_BYTES) return DSA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+    if (st != DSA_OK) return st;
+  }
+  const hipError_t e = dsa::launch_sparse_attn(make_attn_args(in, B, Lq, Lk, idx, idx_q_stride, k), ws,
+                                               need > 0 ? (size_t)DSA_NOALLOC_SCRATCH_BYTES : 0,
                                                static_cast<hipStream_t>(stream));
   return e == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }

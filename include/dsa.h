@@ -264,6 +264,30 @@ int dsa_sparse_attn(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t*
                     int64_t idx_q_stride, int k, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * dsa_sparse_attn for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  Same computation,
+ * same kernels and the same result as dsa_sparse_attn; the partial results of keys split
+ * over several workgroups (few query rows, i.e. decode) go to a buffer the library owns
+ * instead of a caller workspace: a static device array of DSA_NOALLOC_SCRATCH_BYTES, one
+ * copy on each GPU the library runs on, held until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine); the caller still provides q, the
+ * cache, idx, out and lse.
+ * Limit: DSA_NOALLOC_SCRATCH_BYTES (40 MiB) holds the split partials of every call with at
+ * most 32 heads and at most 256 query rows (B * Lq: the decode and MTP-draft shapes, which
+ * need at most 32 MiB), and calls with 1024 or more query rows need none.  A call whose
+ * dsa_workspace_size(DSA_OP_SPARSE_ATTN, ...) exceeds it returns DSA_ERR_WORKSPACE before
+ * anything is enqueued.
+ * Concurrency: every call on a GPU shares that GPU's buffer, which keeps the last call's
+ * contents; calls ordered on one stream are safe, calls that overlap on one GPU (other
+ * streams, other threads) race and give undefined results.  The first call on a device
+ * looks up the buffer's device address with that device current (the device of `stream`).
+ * Returns as dsa_sparse_attn, or DSA_ERR_HIP if that lookup fails.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES (40u << 20)
+int dsa_sparse_attn_noalloc(const dsa_attn_in* in, int B, int Lq, int Lk, const int32_t* idx,
+                            int64_t idx_q_stride, int k, void* stream);
+
+/*
  * One IndexShare group ([A] section "IndexShare"; [B] section 5.2): the Full layer's
  * indexer + top-k runs once (dsa_indexer_topk with `full`), writing idx_out [B, Lq, k];
  * then layers[0..n_layers) each run dsa_sparse_attn with that same idx (layer 0 is the

@@ -176,6 +176,34 @@ def test_fp8_latent_attention_argument_errors():
 
 
 @host_only
+def test_noalloc_attention_limits():
+    # the allocation-free entry point checks its arguments like dsa_sparse_attn and rejects
+    # calls whose split partials exceed its device buffer, before any device call
+    lib = dsa.load_library()
+    limit = 40 << 20
+
+    def call(s, idx=0x5000, B=1, Lq=4, Lk=64, k=16, qstride=16):
+        return lib.dsa_sparse_attn_noalloc(ctypes.byref(s), B, Lq, Lk, idx, qstride, k, None)
+    assert call(_attn_struct(), idx=0) == -1
+    assert call(_attn_struct(H=40)) == -3
+    assert call(_attn_struct(q=0x1008)) == -4
+    big = dict(B=300, Lq=1, Lk=10 ** 6, k=2048, qstride=2048)    # 300 rows x 32 heads split 4 ways
+    assert dsa.workspace_size(dsa.DSA_OP_SPARSE_ATTN, dsa.DSA_BF16, 300, 1, 10 ** 6, 2048, 32) > limit
+    assert call(_attn_struct(), **big) == -5
+    wide = dict(B=64, Lq=8, Lk=10 ** 5, k=2048, qstride=2048)    # 64 heads, 512 rows split twice
+    assert dsa.workspace_size(dsa.DSA_OP_SPARSE_ATTN, dsa.DSA_BF16, 64, 8, 10 ** 5, 2048, 64) > limit
+    assert call(_attn_struct(H=64), **wide) == -5
+
+
+def test_noalloc_buffer_holds_every_decode_shape():
+    # every call with at most 32 heads and at most 256 query rows fits the 40 MiB buffer
+    worst = max(dsa.workspace_size(dsa.DSA_OP_SPARSE_ATTN, dsa.DSA_BF16, B, Lq, 10 ** 6, k, H)
+                for H in (16, 32) for Lq in (1, 2, 4) for B in range(1, 257 // Lq)
+                for k in (1, 33, 64, 520, 2047, 2048, 4096))
+    assert 0 < worst <= 40 << 20
+
+
+@host_only
 def test_layer_group_argument_errors():
     lib = dsa.load_library()
     full = _indexer_struct()
