@@ -355,6 +355,35 @@ constexpr int kBlk2Bytes = 2 * kBlkBytes;        // 36864
 constexpr int kDmaPerBlk2 = kBlk2Bytes / 1024;   // 36 wave-wide 1 KB direct-to-LDS loads
 
 
+// LDS layout of a 36 KB block of 32 latent rows: key group w (keys 8 w .. 8 w + 7)
+// occupies 9 KB, whose 1 KB segment u holds bytes [128 u, 128 u + 128) of the 8 rows, row r
+// at 128 r with its 16-byte chunks XOR-swizzled by sw8(r) = ((r & 3) << 1) | (r >> 2).  One
+// direct-to-LDS load fills one segment of one group (lane l: row l / 8, slot l % 8), so a
+// lane needs one key per group, the nine segments of a row differ only by an immediate
+// offset, and each load covers eight whole 128-byte lines.  sw8 puts the eight rows of a K
+// operand read in distinct 16-byte bank groups and the four rows of a transposed V^T read
+// in distinct 32-byte bank groups.
+constexpr int kSegBytes = 1024;                   // one 128-byte segment of 8 rows
+constexpr int kGroupBytes = 9 * kSegBytes;        // 8 rows of 1152 bytes
+
+__device__ __forceinline__ int sw8(int r) { return ((r & 3) << 1) | (r >> 2); }
+
+// byte offset of 16-byte chunk c of row r of a block in that layout
+__device__ __forceinline__ int blk_chunk_off(int r, int c) {
+  return (r >> 3) * kGroupBytes + (c >> 3) * kSegBytes + (r & 7) * 128 + 16 * ((c & 7) ^ sw8(r & 7));
+}
+
+// segments U .. U1-1 of one key group: src is the lane's address in its row (slot included),
+// lds the group's LDS address
+template <int U, int U1>
+__device__ __forceinline__ void dma_group_segs(const uint8_t* src, uint32_t lds) {
+  if constexpr (U < U1) {
+    // the instruction offset moves the LDS destination as well as the global address
+    dma_16o<128 * U>(src, lds + (kSegBytes - 128) * U);
+    dma_group_segs<U + 1, U1>(src, lds);
+  }
+}
+
 // NB = latent row buffers: block j is computed from buffer j % NB while the rows of
 // blocks j+1 .. j+NB-1 are in flight.  NB = 2 leaves room for two workgroups per CU (the
 // prefill grids); NB = 4 takes most of the LDS for one workgroup per CU with three blocks
@@ -429,38 +458,52 @@ void mla_attn32_kernel(MlaParams P) {
       else slot[lane] = -1;
     }
   };
-  // the block's 32 latent rows: bf16 rows land at r * 1152 with 16-byte chunks swizzled
-  // as swz(r, c); E4M3 rows land unswizzled at r * 576 (36 chunks per row)
+  // the block's 32 latent rows.  bf16: this wave loads key group wv_id (rows 8 wv_id +
+  // lane / 8) in the layout above, nine segment loads per block.  E4M3: the code rows land
+  // unswizzled at r * 576 (36 chunks per row) in 1 KB pieces, for the conversion to bf16.
   constexpr int kRowChunks = KV8 ? kChunks / 2 : kChunks;
-  int dma_row[kSlots];
-  uint32_t dma_off[kSlots];
+  int dma_row[KV8 ? kSlots : 1];
+  uint32_t dma_off[KV8 ? kSlots : 1];
+  if constexpr (KV8) {
 #pragma unroll
-  for (int u = 0; u < kSlots; ++u) {
-    const int piece = (wv_id + u * NW) * 64 + lane;
-    const int r = min(piece / kRowChunks, kBlk2 - 1);   // loads past the block are skipped
-    dma_row[u] = r;
-    dma_off[u] = 16 * (KV8 ? piece - r * kRowChunks : swz(r, piece - r * kRowChunks));
+    for (int u = 0; u < kSlots; ++u) {
+      const int piece = (wv_id + u * NW) * 64 + lane;
+      const int r = min(piece / kRowChunks, kBlk2 - 1);   // loads past the block are skipped
+      dma_row[u] = r;
+      dma_off[u] = 16 * (piece - r * kRowChunks);
+    }
   }
+  const int dr = lane >> 3;
+  const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ sw8(dr));
+  const uint8_t* row_src = kvbase;                       // this wave's row, set by the first part
   // loads u0 .. u1-1 of this wave for the t-th block (KV8: the first part also gathers the
   // block's 32 scales, every wave the same)
   auto issue_rows = [&](int t, int buf, auto u0c, auto u1c) {
     constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
     const int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
-    if constexpr (KV8 && u0 == 0) {
-      if (lane < kBlk2) {
-        const uint32_t kk = (uint32_t)slot[lane] < (uint32_t)a.Lk ? (uint32_t)slot[lane] : 0u;
-        dma_4(sclbase + kk, lds_offset(&sclring[t & (kKeyBufs2 - 1)][0]));
+    if constexpr (KV8) {
+      if constexpr (u0 == 0) {
+        if (lane < kBlk2) {
+          const uint32_t kk = (uint32_t)slot[lane] < (uint32_t)a.Lk ? (uint32_t)slot[lane] : 0u;
+          dma_4(sclbase + kk, lds_offset(&sclring[t & (kKeyBufs2 - 1)][0]));
+        }
       }
-    }
-    int key[u1 - u0];
+      int key[u1 - u0];
 #pragma unroll
-    for (int u = u0; u < u1; ++u) key[u - u0] = slot[dma_row[u]];
+      for (int u = u0; u < u1; ++u) key[u - u0] = slot[dma_row[u]];
 #pragma unroll
-    for (int u = u0; u < u1; ++u) {
-      if (wv_id + u * NW < kDma) {                     // wave-uniform
-        const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
-        dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(dma_buf(buf) + (wv_id + u * NW) * 1024));
+      for (int u = u0; u < u1; ++u) {
+        if (wv_id + u * NW < kDma) {                     // wave-uniform
+          const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
+          dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(dma_buf(buf) + (wv_id + u * NW) * 1024));
+        }
       }
+    } else {
+      if constexpr (u0 == 0) {
+        const uint32_t key = (uint32_t)slot[8 * wv_id + dr];
+        row_src = kvbase + (uint64_t)(key < (uint32_t)a.Lk ? key : 0u) * row_bytes32 + dchunk;   // invalid: masked later
+      }
+      dma_group_segs<u0, u1>(row_src, lds_offset(dma_buf(buf) + wv_id * kGroupBytes));
     }
   };
   using C0 = Phase<0>;
@@ -483,17 +526,22 @@ void mla_attn32_kernel(MlaParams P) {
   for (int dt = 0; dt < kDt; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_use = -kMaxStart, l_lane = 0.f;
   const float sl2 = a.sm_scale * kLog2e;
-  // K operand of row r16 of sub-block ds: chunk 4ks+g sits at 128*(ks/2) + 16*swz
-  const int kbase_off = ds * kBlkBytes + r16 * kRowBytes;
-  const int k_off0 = kbase_off + 16 * swz(r16, g);
-  const int k_off1 = kbase_off + 16 * swz(r16, 4 + g);
-  // V^T operand of value dims 256 ds + 16 dt.. (sub-block 0; sub-block 1 is kBlkBytes on)
+  // K operand of row r16 of sub-block ds (group 2 ds + r16 / 8, row r16 % 8): chunk 4 ks + g
+  int k_off0, k_off1;
+  {
+    const int w = 2 * ds + (r16 >> 3), r = r16 & 7;
+    k_off0 = w * kGroupBytes + r * 128 + 16 * (g ^ sw8(r));
+    k_off1 = w * kGroupBytes + r * 128 + 16 * ((4 + g) ^ sw8(r));
+  }
+  // V^T operand of value dims 256 ds + 16 dt ..: key row 4 g + r16 / 4 of sub-block 0
+  // (sub-block 1 is two groups on), chunk 32 ds + 8 (dt / 4) + 2 (dt % 4) + (r16 % 4) / 2,
+  // half r16 % 2
   int v_off[4];
   {
-    const int vrow = 4 * g + (r16 >> 2);
-    const int c0 = 2 * kDt * ds + ((r16 & 3) >> 1);
+    const int w = g >> 1, r = 4 * (g & 1) + (r16 >> 2), bb = (r16 & 3) >> 1, hh = r16 & 1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v_off[u] = vrow * kRowBytes + 16 * swz(vrow, c0 + 2 * u) + 8 * (r16 & 1);
+    for (int m = 0; m < 4; ++m)
+      v_off[m] = w * kGroupBytes + 4 * ds * kSegBytes + r * 128 + 16 * ((2 * m + bb) ^ sw8(r)) + 8 * hh;
   }
   __builtin_amdgcn_s_waitcnt(0);                 // operands and the first idx entries
   if (nb > 0) {
@@ -546,8 +594,8 @@ void mla_attn32_kernel(MlaParams P) {
             if (e < 2) { lo[2 * e] = v0; lo[2 * e + 1] = v1; }
             else { hi[2 * e - 4] = v0; hi[2 * e - 3] = v1; }
           }
-          *reinterpret_cast<i32x4*>(dst + r * kRowBytes + 16 * swz(r, 2 * c)) = lo;
-          *reinterpret_cast<i32x4*>(dst + r * kRowBytes + 16 * swz(r, 2 * c + 1)) = hi;
+          *reinterpret_cast<i32x4*>(dst + blk_chunk_off(r, 2 * c)) = lo;
+          *reinterpret_cast<i32x4*>(dst + blk_chunk_off(r, 2 * c + 1)) = hi;
         }
       }
       __syncthreads();                                   // B1b: the bf16 block is complete
@@ -562,7 +610,7 @@ void mla_attn32_kernel(MlaParams P) {
       bf16x8 kop[kQSteps];
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ++ks)
-        kop[ks] = *reinterpret_cast<const bf16x8*>(kb + (ks & 1 ? k_off1 : k_off0) + 128 * (ks >> 1));
+        kop[ks] = *reinterpret_cast<const bf16x8*>(kb + (ks & 1 ? k_off1 : k_off0) + kSegBytes * (ks >> 1));
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kQSteps; ks += 2) {
@@ -639,8 +687,8 @@ void mla_attn32_kernel(MlaParams P) {
       bf16x4 vt0[kDt], vt1[kDt];
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        vt0[dt] = lds_read_tr16(kb + v_off[dt & 3] + 128 * (dt >> 2));
-        vt1[dt] = lds_read_tr16(kb + kBlkBytes + v_off[dt & 3] + 128 * (dt >> 2));
+        vt0[dt] = lds_read_tr16(kb + v_off[dt & 3] + kSegBytes * (dt >> 2));
+        vt1[dt] = lds_read_tr16(kb + 2 * kGroupBytes + v_off[dt & 3] + kSegBytes * (dt >> 2));
       }
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {

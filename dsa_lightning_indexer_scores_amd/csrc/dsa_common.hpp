@@ -109,6 +109,12 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
 __device__ __forceinline__ void dma_16(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds), "v"(gsrc) : "memory");
 }
+// the same with an immediate byte offset added to the global address
+template <int OFF>
+__device__ __forceinline__ void dma_16o(const void* gsrc, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off offset:%2" ::"s"(lds), "v"(gsrc), "n"(OFF)
+               : "memory");
+}
 __device__ __forceinline__ void dma_4(const void* gsrc, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off" ::"s"(lds), "v"(gsrc) : "memory");
 }
