@@ -298,6 +298,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="prefill128k")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill16k", action="store_true", help="skip the 16384-token bf16 prefill group line")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-allfull", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 80-layer stack at the prefill workload")
@@ -506,6 +507,9 @@ def main():
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
 
+    if not args.no_prefill16k and cfg.name != "prefill16k":
+        result["prefill16k"] = bench_prefill16k(dsa, synth, accounting, torch, np, dev, stream)
+
     if not args.no_decode:
         result["decode"] = bench_decode(args, dsa, synth, accounting, torch, np, dev, stream)
 
@@ -526,6 +530,49 @@ def main():
         result["cpu_baseline"] = cpu_baseline(cfg)
 
     print(json.dumps(result), flush=True)
+
+
+def bench_prefill16k(dsa, synth, accounting, torch, np, dev, stream, steps=3):
+    """The 16384-token prefill group with a bf16 indexer (H_I = 64, d_I = 128), k = 2048:
+    one fused indexer + top-k, then the 4 layers' sparse MLA attention, timed like the
+    headline step."""
+    cfg = synth.get_config("prefill16k")
+    L, k = cfg.L, cfg.topk
+    ind = synth.indexer_inputs(cfg, device=dev)
+    layers = [synth.attention_inputs(cfg, layer=l, device=dev) for l in range(cfg.n_layers)]
+    idx = torch.empty((1, L, k), dtype=torch.int32, device=dev)
+    outs = [torch.empty((1, L, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in range(cfg.n_layers)]
+    ws = dsa.Workspace()
+
+    def step(ev):
+        ev[0].record(stream)
+        dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, ws=ws, out=idx)
+        ev[1].record(stream)
+        for l in range(cfg.n_layers):
+            dsa.sparse_attn(layers[l], idx, ws=ws, out=outs[l])
+        ev[2].record(stream)
+
+    step([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    step_ms = float(np.mean([e[0].elapsed_time(e[2]) for e in evs]))
+    idx_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) / cfg.n_layers
+    idx_flop = accounting.indexer_flops(accounting.causal_pairs(L, L), cfg.H_I, cfg.d_I)
+    attn_flop = accounting.attention_flops(accounting.selected_pairs(L, k, L), cfg.H, cfg.Dqk, cfg.Dv)
+    out = {"workload": cfg.name, "L": L, "topk": k, "indexer_dtype": "bf16", "step_ms": round(step_ms, 3),
+           "tokens_per_s": round(L / (step_ms * 1e-3), 1),
+           "indexer_topk_ms": round(idx_ms, 4),
+           "indexer_frac": round(idx_flop / (idx_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+           "attn_ms_per_layer": round(attn_ms, 4),
+           "attn_frac": round(attn_flop / (attn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4)}
+    log(f"[bench] prefill16k group {step_ms:.2f} ms (indexer+topk {idx_ms:.3f} ms, attention {attn_ms:.3f} ms/layer)")
+    del ind, layers, outs, idx, ws
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_stack(dsa, torch, inds, layers, outs, ws, k, stream, n=80):
@@ -621,6 +668,34 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
               "indexer_hbm_frac": round(v_bytes / (v_idx * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"[bench] decode varlen (mean {lens_np.mean():.0f} keys) step {v_step * 1e3:.1f} us "
         f"(indexer+topk {v_idx * 1e3:.1f} us)")
+    # MTP draft step: 4 draft queries per sequence attend with the first step's index row
+    # (idx_q_stride = 0); the indexer does not run again, each layer gathers the shared rows
+    n_mtp = cfg.mtp
+    g4 = torch.Generator(device=dev)
+    g4.manual_seed(cfg.seed * 1000 + 77)
+    layers_mtp = [{**lay, "q": torch.randn((cfg.B, n_mtp, cfg.H, cfg.Dqk), generator=g4, device=dev,
+                                          dtype=torch.float32).to(torch.bfloat16)} for lay in layers]
+    outs_mtp = [torch.empty((cfg.B, n_mtp, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev) for _ in layers]
+
+    def step_mtp(ev):
+        ev[0].record(stream)
+        for l in range(cfg.n_layers):
+            dsa.sparse_attn(layers_mtp[l], idx, idx_q_stride=0, ws=ws, out=outs_mtp[l])
+        ev[1].record(stream)
+
+    step_mtp([torch.cuda.Event(enable_timing=True) for _ in range(2)])
+    torch.cuda.synchronize()
+    evm = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+    for s_ in range(n):
+        step_mtp(evm[s_])
+    torch.cuda.synchronize()
+    m_step = float(np.median([e[0].elapsed_time(e[1]) for e in evm]))
+    mtp = {"draft_queries": n_mtp, "reuses_index_row": True, "step_us": round(m_step * 1e3, 1),
+           "attn_us_per_layer": round(m_step * 1e3 / cfg.n_layers, 1),
+           "us_per_draft_token": round(m_step * 1e3 / (cfg.B * n_mtp), 3)}
+    log(f"[bench] decode MTP ({n_mtp} draft queries sharing the index row) step {m_step * 1e3:.1f} us "
+        f"(attention {m_step * 1e3 / cfg.n_layers:.1f} us/layer)")
+    del layers_mtp, outs_mtp
     # FP8 latent caches (E4M3 codes + one fp32 scale per row): the same step with every
     # layer's attention reading 580 bytes per selected row instead of 1152
     layers8 = [synth.fp8_latent(lay) for lay in layers]
@@ -658,7 +733,7 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
            "attn_us_per_layer": round(attn_ms * 1e3, 1),
            "attn_gather_gbs": round(gather_bytes / (attn_ms * 1e-3) / 1e9, 1),
            "attn_gather_frac": round(gather_bytes / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-           "varlen": varlen, "fp8_latent": fp8_kv, "paged": paged}
+           "varlen": varlen, "mtp": mtp, "fp8_latent": fp8_kv, "paged": paged}
     del ind, layers, outs, idx
     torch.cuda.empty_cache()
     return out
