@@ -879,6 +879,7 @@ def bench_objective(dsa, synth, torch, dev, stream):
     lses = [dsa.sparse_attn(lay, idx, return_lse=True)[1] for lay in layers]
     pbar = torch.zeros(idx.shape, dtype=torch.float32, device=dev)
     dk = torch.zeros(ind["k"].shape, dtype=torch.float32, device=dev)
+    ws = dsa.Workspace()
 
     def centroid():
         pbar.zero_()
@@ -886,7 +887,7 @@ def bench_objective(dsa, synth, torch, dev, stream):
 
     def backward():
         dk.zero_()
-        return dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar, dk=dk)
+        return dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar, dk=dk, ws=ws)
 
     def timed(fn, n=3):
         fn()

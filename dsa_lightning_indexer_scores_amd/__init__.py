@@ -16,14 +16,14 @@ import torch
 
 __all__ = [
     "DSA_F32", "DSA_BF16", "DSA_FP8_E4M3", "DSA_OP_TOPK", "DSA_OP_INDEXER_TOPK",
-    "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DsaError", "library_path", "load_library",
+    "DSA_OP_SPARSE_ATTN", "DSA_OP_LAYER_GROUP", "DSA_OP_INDEXER_KL", "DsaError", "library_path", "load_library",
     "workspace_size", "status_string", "indexer_scores", "topk", "indexer_topk",
     "sparse_attn", "sparse_attn_noalloc", "layer_group", "layer_schedule", "LayerStack", "quantize_e4m3", "linear_bf16", "indexer_projections", "attention_centroid",
     "indexer_kl_backward", "Workspace",
 ]
 
 DSA_F32, DSA_BF16, DSA_FP8_E4M3 = 0, 1, 2
-DSA_OP_TOPK, DSA_OP_INDEXER_TOPK, DSA_OP_SPARSE_ATTN, DSA_OP_LAYER_GROUP = 0, 1, 2, 3
+DSA_OP_TOPK, DSA_OP_INDEXER_TOPK, DSA_OP_SPARSE_ATTN, DSA_OP_LAYER_GROUP, DSA_OP_INDEXER_KL = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -85,7 +85,8 @@ def load_library():
     lib.dsa_quantize_e4m3.argtypes = [vp, i32, i32, i32, i64, vp, i64, vp, i64, vp]
     lib.dsa_linear_bf16.argtypes = [vp, i64, vp, i64, i32, i32, i32, vp, i64, vp]
     lib.dsa_attn_probs.argtypes = [ctypes.POINTER(_AttnIn), vp, i32, i32, i32, vp, i64, i32, ctypes.c_float, vp, vp]
-    lib.dsa_indexer_kl_backward.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp]
+    lib.dsa_indexer_kl_backward.argtypes = [ctypes.POINTER(_IndexerIn), i32, i32, i32, vp, i32, vp, vp, vp, vp, vp, vp,
+                                            sz, vp]
     lib.dsa_status_string.argtypes = [i32]
     lib.dsa_status_string.restype = ctypes.c_char_p
     for fn in ("dsa_indexer_scores", "dsa_topk", "dsa_indexer_topk", "dsa_indexer_topk_varlen",
@@ -664,11 +665,12 @@ def attention_centroid(layers, idx, lses, idx_q_stride=None, out=None, stream=No
     return out
 
 
-def indexer_kl_backward(q, k, w, idx, pbar, dk=None, stream=None):
+def indexer_kl_backward(q, k, w, idx, pbar, dk=None, ws=None, stream=None):
     """Loss and gradients of the group-centroid objective of the kept indexer
     (dsa_indexer_kl_backward): q bf16 [B,Lq,H_I,128], k bf16 [B,Lk,128], w float32
     [B,Lq,H_I], idx int32 [B,Lq,k], pbar float32 [B,Lq,k].  Returns dict(loss [B,Lq],
-    dq [B,Lq,H_I,128], dw [B,Lq,H_I], dk [B,Lk,128]); dk, if given, is added to."""
+    dq [B,Lq,H_I,128], dw [B,Lq,H_I], dk [B,Lk,128]); dk, if given, is added to.  dk does
+    not depend on the order of the rows' additions (fixed-point sums in the workspace)."""
     s, B, Lq, Lk = _indexer_struct(q, k, w, None, None)
     dev = q.device
     if idx is None or idx.dim() != 3:
@@ -684,7 +686,9 @@ def indexer_kl_backward(q, k, w, idx, pbar, dk=None, stream=None):
         if dk is None:
             dk = torch.zeros(k.shape, dtype=torch.float32, device=dev)
     _expect(dk, "dk", (torch.float32,), tuple(k.shape), dev)
+    ws = ws or Workspace()
+    buf, nbytes = ws.get(workspace_size(DSA_OP_INDEXER_KL, DSA_BF16, B, Lq, Lk, kk), dev, stream)
     _check("dsa_indexer_kl_backward", load_library().dsa_indexer_kl_backward(
         ctypes.byref(s), B, Lq, Lk, _ptr(idx), kk, _ptr(pbar), _ptr(loss), _ptr(dq), _ptr(dw), _ptr(dk),
-        _stream(stream)))
+        _ptr(buf), nbytes, _stream(stream)))
     return {"loss": loss, "dq": dq, "dw": dw, "dk": dk}

@@ -214,6 +214,9 @@ size_t dsa_workspace_size(int op, int dtype, int B, int Lq, int Lk, int k, int h
       const size_t b = attn_ws(DSA_BF16, B, Lq, k, heads);
       return a > b ? a : b;
     }
+    case DSA_OP_INDEXER_KL:
+      if (dtype != DSA_BF16 || k > dsa::kMaxKlK) return 0;
+      return dsa::indexer_kl_ws(B, Lk);
     default:
       return 0;
   }
@@ -440,7 +443,8 @@ int dsa_attn_probs(const dsa_attn_in* in, const float* lse, int B, int Lq, int L
 }
 
 int dsa_indexer_kl_backward(const dsa_indexer_in* in, int B, int Lq, int Lk, const int32_t* idx, int k,
-                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* stream) {
+                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* ws,
+                            size_t ws_bytes, void* stream) {
   if (!in || !in->q || !in->k || !in->w || !idx || !pbar || !loss || !dq || !dw || !dk) return DSA_ERR_ARG;
   if (in->dtype != DSA_BF16) return DSA_ERR_DTYPE;
   if (B <= 0 || Lq <= 0 || Lk <= 0 || k <= 0 || k > dsa::kMaxKlK) return DSA_ERR_SHAPE;
@@ -449,7 +453,10 @@ int dsa_indexer_kl_backward(const dsa_indexer_in* in, int B, int Lq, int Lk, con
   if (!aligned(idx, 4) || !aligned(pbar, 4) || !aligned(loss, 4) || !aligned(dq, 4) || !aligned(dw, 4) ||
       !aligned(dk, 4))
     return DSA_ERR_ALIGN;
-  dsa::IndexerKlArgs a{in->q, in->k, in->w, idx, pbar, loss, dq, dw, dk, B, Lq, Lk, in->H_I, k};
+  if (!ws || ws_bytes < dsa::indexer_kl_ws(B, Lk)) return DSA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return DSA_ERR_ALIGN;
+  dsa::IndexerKlArgs a{in->q, in->k, in->w, idx, pbar, loss, dq, dw, dk,
+                       static_cast<unsigned long long*>(ws), B, Lq, Lk, in->H_I, k};
   return dsa::launch_indexer_kl(a, static_cast<hipStream_t>(stream)) == hipSuccess ? DSA_OK : DSA_ERR_HIP;
 }
 

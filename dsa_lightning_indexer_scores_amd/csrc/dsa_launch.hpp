@@ -115,9 +115,14 @@ struct IndexerKlArgs {
   float* loss;              // [B, Lq]
   float* dq;                // [B, Lq, H_I, 128]
   float* dw;                // [B, Lq, H_I]
-  float* dk;                // [B, Lk, 128], accumulated
+  float* dk;                // [B, Lk, 128], added to
+  unsigned long long* dk_fix;  // [B, Lk, 128] 64-bit fixed-point sums (workspace)
   int B, Lq, Lk, H_I, k;
 };
+// dk contributions are rounded to multiples of 2^-kDkFixBits and summed as 64-bit integers,
+// so the result does not depend on the order in which rows add them
+constexpr int kDkFixBits = 30;
+inline size_t indexer_kl_ws(int B, int Lk) { return ((size_t)B * Lk * 128 * 8 + 255) / 256 * 256; }
 hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t s);
 
 // --- sparse attention --------------------------------------------------------

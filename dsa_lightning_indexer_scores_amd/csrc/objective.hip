@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
 #pragma unroll
   for (int db = 0; db < 8; ++db) dq[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dwp[4] = {0.f, 0.f, 0.f, 0.f};
-  float* dk = a.dk + (size_t)b * a.Lk * kDI;
+  unsigned long long* dkf = a.dk_fix + (size_t)b * a.Lk * kDI;
   for (int t = 0; t < n_tiles; ++t) {
     gather(t);
     if (active) {
@@ -316,7 +316,9 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
         const int s = sel[key];
         if (s >= 0 && t * kTile + key < a.k) {
 #pragma unroll
-          for (int db = 0; db < 8; ++db) atomicAdd(&dk[(size_t)s * kDI + 16 * db + l16], acc[db][i]);
+          for (int db = 0; db < 8; ++db)
+            atomicAdd(&dkf[(size_t)s * kDI + 16 * db + l16],
+                      (unsigned long long)__float2ll_rn(acc[db][i] * (float)(1 << kDkFixBits)));
         }
       }
     }
@@ -347,14 +349,27 @@ hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// dk[e] += the fixed-point sum of element e (two's complement in 64 bits)
+__global__ __launch_bounds__(256) void dk_fix_add_kernel(const unsigned long long* __restrict__ fix,
+                                                         float* __restrict__ dk, size_t n) {
+  const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (e < n) dk[e] += (float)((double)(long long)fix[e] * (1.0 / (double)(1ll << kDkFixBits)));
+}
+
 hipError_t launch_indexer_kl(const IndexerKlArgs& a, hipStream_t s) {
   const int rows = a.B * a.Lq;
+  const size_t n_dk = (size_t)a.B * a.Lk * 128;
+  hipError_t e = launch_zero(a.dk_fix, n_dk * sizeof(unsigned long long), s);
+  if (e != hipSuccess) return e;
   switch (a.H_I / 16) {
     case 1: indexer_kl_kernel<1><<<rows, 256, 0, s>>>(a); break;
     case 2: indexer_kl_kernel<2><<<rows, 256, 0, s>>>(a); break;
     case 3: indexer_kl_kernel<3><<<rows, 256, 0, s>>>(a); break;
     default: indexer_kl_kernel<4><<<rows, 256, 0, s>>>(a); break;
   }
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dk_fix_add_kernel<<<(unsigned)((n_dk + 255) / 256), 256, 0, s>>>(a.dk_fix, a.dk, n_dk);
   return hipGetLastError();
 }
 

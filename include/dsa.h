@@ -65,7 +65,8 @@ typedef enum {
   DSA_OP_TOPK = 0,
   DSA_OP_INDEXER_TOPK = 1,
   DSA_OP_SPARSE_ATTN = 2,
-  DSA_OP_LAYER_GROUP = 3
+  DSA_OP_LAYER_GROUP = 3,
+  DSA_OP_INDEXER_KL = 4
 } dsa_op;
 
 /*
@@ -129,7 +130,8 @@ typedef struct {
 /*
  * Bytes of device workspace needed by `op` (a dsa_op) for these sizes; 0 if none.
  * dtype is the indexer dtype for DSA_OP_INDEXER_TOPK / DSA_OP_LAYER_GROUP and the
- * attention dtype for DSA_OP_SPARSE_ATTN; `heads` is the attention head count H for
+ * attention dtype for DSA_OP_SPARSE_ATTN and DSA_BF16 for DSA_OP_INDEXER_KL (B and Lk are
+ * the indexer's, Lq and k its query rows and index-row length); `heads` is the attention head count H for
  * DSA_OP_SPARSE_ATTN and DSA_OP_LAYER_GROUP (0 elsewhere).  For DSA_OP_TOPK the rows
  * are B * Lq rows of Lk scores (the optional workspace of dsa_topk).  The value covers both
  * idx_q_stride conventions of dsa_sparse_attn.  Pure host arithmetic, no device call;
@@ -375,14 +377,19 @@ int dsa_attn_probs(const dsa_attn_in* in, const float* lse, int B, int Lq, int L
  * of 16, at most 64; d_I = 128); idx [B, Lq, k] (entries outside [0, Lk) are not in S_r;
  * positions within a row must be distinct), k <= 2048; pbar [B, Lq, k] aligned with idx
  * (mass only on entries in S_r).  Outputs fp32, caller-owned: loss [B, Lq], dq, dw, and
- * dk [B, Lk, 128], which is ADDED to (zero it first); its additions are fp32 atomics, so
- * their order, and the last bits of dk, may vary from run to run.  The contractions run
- * on the bf16 matrix cores with fp32 accumulation; the coefficients g w [x > 0] enter them
- * rounded to bf16.  Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE, DSA_ERR_SHAPE,
- * DSA_ERR_ALIGN or DSA_ERR_HIP.
+ * dk [B, Lk, 128], to which this call's dk is ADDED (zero it for a fresh result).  dk is deterministic:
+ * each contribution is rounded to a multiple of 2^-30 and the contributions of a key are
+ * summed as 64-bit integers in the workspace, so the sum does not depend on the order in
+ * which the rows add them (each key's partial sums must stay below 2^33 in magnitude);
+ * the sum is then converted and added to dk.  The contractions run on the bf16 matrix
+ * cores with fp32 accumulation; the coefficients g w [x > 0] enter them rounded to bf16.
+ * ws: dsa_workspace_size(DSA_OP_INDEXER_KL, DSA_BF16, B, Lq, Lk, k, 0) bytes (256-byte
+ * aligned).  Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE, DSA_ERR_SHAPE, DSA_ERR_ALIGN,
+ * DSA_ERR_WORKSPACE or DSA_ERR_HIP.
  */
 int dsa_indexer_kl_backward(const dsa_indexer_in* in, int B, int Lq, int Lk, const int32_t* idx, int k,
-                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* stream);
+                            const float* pbar, float* loss, float* dq, float* dw, float* dk, void* ws,
+                            size_t ws_bytes, void* stream);
 
 /*
  * Layer schedule of an IndexShare stack ([B] section 5.2: the released configuration

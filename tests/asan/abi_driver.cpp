@@ -152,8 +152,11 @@ int main() {
   float* pp = static_cast<float*>(P(0x6000));
   EXPECT(dsa_attn_probs(&a, nullptr, 1, 4, 64, idx, 16, 16, 0.5f, pp, nullptr), DSA_ERR_ARG);
   EXPECT(dsa_attn_probs(&h48, lse, 1, 4, 64, idx, 16, 16, 0.5f, pp, nullptr), DSA_ERR_SHAPE);
-  EXPECT(dsa_indexer_kl_backward(&b, 1, 8, 64, idx, 4096, pp, pp, pp, pp, pp, nullptr), DSA_ERR_SHAPE);
-  EXPECT(dsa_indexer_kl_backward(&f8, 1, 8, 64, idx, 64, pp, pp, pp, pp, pp, nullptr), DSA_ERR_DTYPE);
+  EXPECT(dsa_indexer_kl_backward(&b, 1, 8, 64, idx, 4096, pp, pp, pp, pp, pp, ws, big, nullptr), DSA_ERR_SHAPE);
+  EXPECT(dsa_indexer_kl_backward(&f8, 1, 8, 64, idx, 64, pp, pp, pp, pp, pp, ws, big, nullptr), DSA_ERR_DTYPE);
+  EXPECT(dsa_indexer_kl_backward(&b, 1, 8, 64, idx, 64, pp, pp, pp, pp, pp, nullptr, big, nullptr), DSA_ERR_WORKSPACE);
+  EXPECT(dsa_workspace_size(DSA_OP_INDEXER_KL, DSA_BF16, 1, 8, 64, 64, 0), (size_t)64 * 128 * 8);
+  EXPECT(dsa_workspace_size(DSA_OP_INDEXER_KL, DSA_FP8_E4M3, 1, 8, 64, 64, 0), 0);
 
   // layer schedule (host only, runs in full): patterns in exactly sized buffers
   int32_t anchors[80];

@@ -282,8 +282,8 @@ def test_objective_argument_errors():
     assert call(stride=8) == -3                                 # idx row stride below k
     assert call(P=0x6002) == -4
     ind = _indexer_struct()
-    kl = lambda st=ind, k=64, idx=0x5000, dk=0x9000: lib.dsa_indexer_kl_backward(
-        ctypes.byref(st), 1, 8, 64, idx, k, 0x6000, 0x7000, 0x8000, 0x8800, dk, None)
+    kl = lambda st=ind, k=64, idx=0x5000, dk=0x9000, ws=0x100000, nbytes=1 << 40: lib.dsa_indexer_kl_backward(
+        ctypes.byref(st), 1, 8, 64, idx, k, 0x6000, 0x7000, 0x8000, 0x8800, dk, ws, nbytes, None)
     assert kl(idx=0) == -1
     assert kl(dk=0) == -1
     assert kl(st=_indexer_struct(dtype=dsa.DSA_FP8_E4M3, qs=0x100, ks=0x200)) == -2
@@ -291,6 +291,9 @@ def test_objective_argument_errors():
     assert kl(st=_indexer_struct(H_I=8)) == -3                  # H_I a multiple of 16
     assert kl(st=_indexer_struct(d_I=64)) == -3                 # d_I = 128
     assert kl(dk=0x9002) == -4
+    assert kl(ws=0) == -5
+    assert kl(nbytes=64 * 128 * 8 - 1) == -5                   # one int64 per dk element
+    assert kl(ws=0x100010) == -4
 
 
 # ---------------------------------------------------------------------------

@@ -855,6 +855,21 @@ def test_attention_centroid_parity(H):
         assert np.all(pbar[b][idx_h[b] < 0] == 0)
 
 
+def test_indexer_kl_backward_dk_is_deterministic():
+    """dk sums each key's contributions in 64-bit fixed point, so repeated calls give the
+    same bits whatever order the rows arrive in, and a given dk is added to exactly once
+    (one fp32 rounding of the sum)."""
+    cfg, ind, idx, layers, lses = _objective_case(B=2, L=700, k=256, H_I=64)
+    pbar = dsa.attention_centroid(layers, idx, lses)
+    runs = [dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar) for _ in range(3)]
+    for r in runs[1:]:
+        for name in ("loss", "dq", "dw", "dk"):
+            assert torch.equal(r[name], runs[0][name]), name
+    base = torch.randn(ind["k"].shape, device=DEV, dtype=torch.float32)
+    added = dsa.indexer_kl_backward(ind["q"], ind["k"], ind["w"], idx, pbar, dk=base.clone())["dk"]
+    assert torch.equal(added, base + runs[0]["dk"])
+
+
 @pytest.mark.parametrize("L,k,H_I", [(320, 128, 64), (200, 100, 32), (150, 64, 16), (130, 50, 48)])
 def test_indexer_kl_backward_parity(L, k, H_I):
     """Loss, dq, dw and dk against the oracle on the GPU's centroid.  Bounds: the
