@@ -119,42 +119,76 @@ __device__ __forceinline__ float relu_bits(float x) {
 // 16hb..16hb+15; b[kb]: keys 16kb..16kb+15 of the tile; wv[tt][hb][i] = w'[16hb + 4g + i].
 // Returns, in lane l of out[tt], sum_j w'_j ReLU(q_j . k_{s0+l}) (before the fp8 key
 // scale).  Shared by the materialising and the fused kernels so both produce identical
-// bits (each token's arithmetic does not depend on TW).  The (key block, token) groups of
-// MFMAs are issued one group ahead of their epilogues, so the matrix core and the VALU
-// work on different groups at the same time.
+// bits (each token's arithmetic does not depend on TW, nor on the issue order below).
+//
+// FP8: one 16x16x128 MFMA per (key block, token, head block), and its epilogue (four
+// ReLUs and four FMAs, 32 VALU cycles against the MFMA's 32) is issued kLag MFMAs later,
+// when its result has long landed, between two MFMAs: MFMA m, epilogue m - kLag,
+// MFMA m + 1, ...  The order is held by empty asm statements: the B operand of MFMA m
+// passes through one that also takes the accumulator of epilogue m - 1 - kLag, so that
+// epilogue cannot sink below the MFMA.  BF16 (four dependent MFMAs per dot product):
+// groups of MFMAs are issued one group ahead of their epilogues.
 template <int DT, int HB, int TW>
 __device__ __forceinline__ void tile_scores(const Op<DT> (&a)[TW][HB], const Op<DT> (&b)[4],
                                             const f32x4 (&wv)[TW][HB], float (&out)[TW]) {
-  constexpr int kMfmaPerDot = (DT == DSA_FP8_E4M3) ? 1 : 4;
-  f32x4 d[4][TW][HB];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int tt = 0; tt < TW; ++tt)
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) d[kb][tt][hb] = dot16<DT>(a[tt][hb], b[kb]);
   float p[TW][4];
+  if constexpr (DT == DSA_FP8_E4M3) {
+    constexpr int N = 4 * TW * HB;   // MFMAs, in (key block, token, head block) order
+    constexpr int kLag = 3;
+    f32x4 d[N];
+    Op<DT> bl[4] = {b[0], b[1], b[2], b[3]};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int tt = 0; tt < TW; ++tt) {
-      float acc = 0.f;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        acc = fmaf(wv[tt][hb][0], relu_bits(d[kb][tt][hb][0]), acc);
-        acc = fmaf(wv[tt][hb][1], relu_bits(d[kb][tt][hb][1]), acc);
-        acc = fmaf(wv[tt][hb][2], relu_bits(d[kb][tt][hb][2]), acc);
-        acc = fmaf(wv[tt][hb][3], relu_bits(d[kb][tt][hb][3]), acc);
+    for (int m = 0; m < N + kLag; ++m) {
+      if (m < N) {
+        const int kb = m / (TW * HB), tt = (m / HB) % TW, hb = m % HB;
+        if (m > kLag) {
+          const int e = m - 1 - kLag;
+          asm volatile("" : "+v"(bl[kb].v) : "v"(p[(e / HB) % TW][e / (TW * HB)]));
+        }
+        d[m] = dot16<DT>(a[tt][hb], bl[kb]);
+        asm volatile("" : "+v"(d[m]));
       }
-      p[tt][kb] = acc;
+      if (m >= kLag) {
+        const int e = m - kLag;
+        const int kb = e / (TW * HB), tt = (e / HB) % TW, hb = e % HB;
+        float acc = hb == 0 ? 0.f : p[tt][kb];
+        acc = fmaf(wv[tt][hb][0], relu_bits(d[e][0]), acc);
+        acc = fmaf(wv[tt][hb][1], relu_bits(d[e][1]), acc);
+        acc = fmaf(wv[tt][hb][2], relu_bits(d[e][2]), acc);
+        acc = fmaf(wv[tt][hb][3], relu_bits(d[e][3]), acc);
+        p[tt][kb] = acc;
+      }
     }
-  __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDot * HB, 0);
+  } else {
+    f32x4 d[4][TW][HB];
 #pragma unroll
-  for (int grp = 1; grp < 4 * TW; ++grp) {
-    __builtin_amdgcn_sched_group_barrier(0x008, kMfmaPerDot * HB, 0);
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) d[kb][tt][hb] = dot16<DT>(a[tt][hb], b[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int tt = 0; tt < TW; ++tt) {
+        float acc = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+          acc = fmaf(wv[tt][hb][0], relu_bits(d[kb][tt][hb][0]), acc);
+          acc = fmaf(wv[tt][hb][1], relu_bits(d[kb][tt][hb][1]), acc);
+          acc = fmaf(wv[tt][hb][2], relu_bits(d[kb][tt][hb][2]), acc);
+          acc = fmaf(wv[tt][hb][3], relu_bits(d[kb][tt][hb][3]), acc);
+        }
+        p[tt][kb] = acc;
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * HB, 0);
+#pragma unroll
+    for (int grp = 1; grp < 4 * TW; ++grp) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * HB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 8 * HB, 0);
+    }
     __builtin_amdgcn_sched_group_barrier(0x002, 8 * HB, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x002, 8 * HB, 0);
 #pragma unroll
   for (int tt = 0; tt < TW; ++tt) out[tt] = reduce_scatter4(p[tt][0], p[tt][1], p[tt][2], p[tt][3]);
 }
