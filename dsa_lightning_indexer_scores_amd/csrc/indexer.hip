@@ -40,9 +40,11 @@ template <> struct IdxTraits<DSA_FP8_E4M3> {
 
 
 
-// Per-lane operand slice of one 16-row block of a d_I = 128 row: lane group g = lane/16
-// takes bytes [g * kRowBytes/4, (g+1) * kRowBytes/4).  A (queries) and B (keys) use the
-// same slice, so the MFMA pairs equal feature indices.
+// Per-lane operand slice of one 16-row block of a d_I = 128 row, for lane group g = lane/16.
+// FP8 (one 16x16x128 MFMA): bytes [16g, 16g + 16) and [64 + 16g, 80 + 16g).  BF16 (four
+// 16x16x32 MFMAs, i = 0..3): bytes [64i + 16g, 64i + 16g + 16).  Either way the four lane
+// groups of one load instruction read one whole 64-byte half of each of the 16 rows.  A
+// (queries) and B (keys) use the same slices, so the MFMA pairs equal feature indices.
 template <int DT> struct Op;
 template <> struct Op<DSA_FP8_E4M3> { i32x8 v; };
 template <> struct Op<DSA_BF16> { bf16x8 v[4]; };
@@ -51,18 +53,17 @@ template <int DT>
 __device__ __forceinline__ Op<DT> load_op(const uint8_t* row, int g);
 template <>
 __device__ __forceinline__ Op<DSA_FP8_E4M3> load_op<DSA_FP8_E4M3>(const uint8_t* row, int g) {
-  const i32x4* p = reinterpret_cast<const i32x4*>(row + 32 * g);
-  i32x4 lo = p[0], hi = p[1];
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(row + 16 * g);
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(row + 64 + 16 * g);
   Op<DSA_FP8_E4M3> o;
   o.v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return o;
 }
 template <>
 __device__ __forceinline__ Op<DSA_BF16> load_op<DSA_BF16>(const uint8_t* row, int g) {
-  const bf16x8* p = reinterpret_cast<const bf16x8*>(row + 64 * g);
   Op<DSA_BF16> o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o.v[i] = p[i];
+  for (int i = 0; i < 4; ++i) o.v[i] = *reinterpret_cast<const bf16x8*>(row + 64 * i + 16 * g);
   return o;
 }
 
@@ -78,8 +79,8 @@ __device__ __forceinline__ Op<DT> load_op_tile(const uint8_t* tile, int row, int
 template <>
 __device__ __forceinline__ Op<DSA_FP8_E4M3> load_op_tile<DSA_FP8_E4M3>(const uint8_t* tile, int row, int g) {
   const uint8_t* r = tile + row * 128;
-  const i32x4 lo = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, 2 * g));
-  const i32x4 hi = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, 2 * g + 1));
+  const i32x4 lo = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, g));
+  const i32x4 hi = *reinterpret_cast<const i32x4*>(r + 16 * tile_chunk<DSA_FP8_E4M3>(row, g + 4));
   Op<DSA_FP8_E4M3> o;
   o.v = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   return o;
@@ -89,7 +90,7 @@ __device__ __forceinline__ Op<DSA_BF16> load_op_tile<DSA_BF16>(const uint8_t* ti
   const uint8_t* r = tile + row * 256;
   Op<DSA_BF16> o;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o.v[i] = *reinterpret_cast<const bf16x8*>(r + 16 * tile_chunk<DSA_BF16>(row, 4 * g + i));
+  for (int i = 0; i < 4; ++i) o.v[i] = *reinterpret_cast<const bf16x8*>(r + 16 * tile_chunk<DSA_BF16>(row, 4 * i + g));
   return o;
 }
 
@@ -451,46 +452,72 @@ __global__ __launch_bounds__(256) void indexer_chunksel_kernel(IndexerArgs a, in
   const int n_c = max(0, s_causal_end - s_begin);
   const uint32_t dc = n_c > k ? block_digit256(lhist, (uint32_t)k, sh) : 0u;
 
-  // ordered compaction of the entries with digit >= dc: 1024 entries per round, one
-  // ballot per 256 (entry e0 + 256 u + tid), prefix over (u, wave) in LDS
+  // Ordered compaction of the entries with digit >= dc.  Wave w takes the contiguous
+  // range [w q, min(n_c, (w + 1) q)) of the chunk (q = n_c / 4 rounded up to 64, at most
+  // 64 entries per lane), holds its keys in registers and counts its entries; after a
+  // barrier it writes them behind those of the lower waves, in position order (ballot
+  // rank), into the score buffer itself (keys at [0, n), chunk offsets at [8192, 8192 + n));
+  // the workgroup then copies both arrays out in full 16-byte pieces.  More than 8192
+  // entries (heavy ties) go straight to global memory instead.
   const size_t slot = (size_t)qrow * L.row_stride + (size_t)chunk * L.chunk;
   uint32_t* ok = L.keys + slot;
   uint32_t* op = L.pos + slot;
-  uint32_t base = 0;
-  for (int e0 = 0; e0 < n_c; e0 += 1024) {
-    uint32_t key[4];
-    uint64_t m[4];
+  constexpr int kHalf = kSelMaxChunk / 2;
+  const int q = (n_c + 255) / 256 * 64;
+  const int lo = min(n_c, wv_id * q), hi = min(n_c, lo + q);
+  uint32_t kr[kSelMaxChunk / 256];
+  uint32_t n_w = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = e0 + 256 * u + tid;
-      key[u] = e < n_c ? order_key(lsc[e]) : 0u;
-      m[u] = ballot(e < n_c && (key[u] >> 21) >= dc);
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) sh[4 * u + wv_id] = (uint32_t)popc64(m[u]);
-    }
-    __syncthreads();
-    uint32_t before[4], run = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int ww = 0; ww < 4; ++ww) {
-        if (ww == wv_id) before[u] = run;
-        run += sh[4 * u + ww];
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if ((m[u] >> lane) & 1ull) {
-        const uint32_t o = base + before[u] + rank_below(m[u]);
-        ok[o] = key[u];
-        op[o] = (uint32_t)(s_begin + e0 + 256 * u + tid);
-      }
-    }
-    base += run;
-    __syncthreads();
+  for (int i = 0; i < kSelMaxChunk / 256; ++i) {
+    const int e = lo + 64 * i + lane;
+    kr[i] = e < hi ? order_key(lsc[e]) : 0u;
+    n_w += (uint32_t)popc64(ballot(e < hi && (kr[i] >> 21) >= dc));
   }
-  if (tid == 0) L.cnt[(size_t)qrow * L.n_chunks + chunk] = base;
+  if (lane == 0) sh[8 + wv_id] = n_w;   // block_digit256 uses sh[0..4]
+  __syncthreads();                      // every wave holds its keys: lsc may be overwritten
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t c = sh[8 + w];
+    base += w < wv_id ? c : 0u;
+    total += c;
+  }
+  const bool staged = total <= (uint32_t)kHalf;   // workgroup-uniform
+  uint32_t* lk = reinterpret_cast<uint32_t*>(lsc);
+#pragma unroll
+  for (int i = 0; i < kSelMaxChunk / 256; ++i) {
+    const int e = lo + 64 * i + lane;
+    const bool take = e < hi && (kr[i] >> 21) >= dc;
+    const uint64_t m = ballot(take);
+    if (take) {
+      const uint32_t o = base + rank_below(m);
+      if (staged) {
+        lk[o] = kr[i];
+        lk[kHalf + o] = (uint32_t)e;
+      } else {
+        ok[o] = kr[i];
+        op[o] = (uint32_t)(s_begin + e);
+      }
+    }
+    base += (uint32_t)popc64(m);
+  }
+  if (staged) {
+    __syncthreads();
+    for (uint32_t j = 4 * tid; j < total; j += 1024) {
+      if (j + 4 <= total) {
+        *reinterpret_cast<i32x4*>(ok + j) = *reinterpret_cast<const i32x4*>(lk + j);
+        i32x4 p4 = *reinterpret_cast<const i32x4*>(lk + kHalf + j);
+        p4 += s_begin;
+        *reinterpret_cast<i32x4*>(op + j) = p4;
+      } else {
+        for (uint32_t jj = j; jj < total; ++jj) {
+          ok[jj] = lk[jj];
+          op[jj] = (uint32_t)s_begin + lk[kHalf + jj];
+        }
+      }
+    }
+  }
+  if (tid == 0) L.cnt[(size_t)qrow * L.n_chunks + chunk] = total;
 }
 
 // After every chunk of a row is scored: one workgroup per (chunk, row) finds the row's
