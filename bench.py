@@ -32,17 +32,20 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 
-# HBM traffic per launch comes from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
-# summarised under profiles/.  A summary is used only while the kernel's sources still
-# hash to the digest it records; otherwise the traffic is reported as null.
+# Memory traffic per launch comes from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
+# summarised under profiles/.  Both count the L2's requests to the memory side (its misses
+# and write-backs), which the Infinity Cache or HBM serves: an upper bound of the DRAM bytes.
+# A summary is used only while the kernel's sources still hash to the digest it records;
+# otherwise the traffic is reported as null.
 PKG = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd")
 KERNEL_SOURCES = {"mla_attn32_kernel": ["csrc/attn.hip"], "indexer_topk_kernel": ["csrc/indexer.hip"]}
 COMMON_SOURCES = ["csrc/dsa_common.hpp", "csrc/dsa_launch.hpp", "build_lib.py"]
-TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_kernel_prefill128k_hbm.txt"),
-                   "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_hbm.txt")}
+TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_kernel_prefill128k_memtraffic.txt"),
+                   "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_memtraffic.txt")}
 PMC_COMMAND = ('rocprofv3 --pmc {counter} --kernel-include-regex "dsa::|copyBuffer" --output-format csv '
-               '-d {dir} -o run -- python3 bench.py --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode '
-               '--no-chunk1m --no-quant --no-train --copy-calibration')
+               '-d {dir} -o run -- {bench}')
+BENCH_ONE_STEP = ("python3 bench.py --workload {workload} --steps 1 --warmup 0 --no-cpu --no-allfull --no-decode "
+                  "--no-prefill16k --no-stack --no-chunk1m --no-quant --no-train --no-attainable")
 COPY_BYTES = 1 << 30
 # Counter passes for the execution profile of a kernel (each within one rocprofv3 pass's
 # limits on gfx950: at most 8 SQ, 4 TCC, 4 TCP, 2 TA and 2 GRBM counters).
@@ -144,8 +147,8 @@ def summarize_trace(trace_csv):
 
 def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
     """Summary text of the two counter runs for one kernel.  FETCH_SIZE and WRITE_SIZE are
-    KiB per dispatch; each is scaled by what it reads for the 1 GiB device copy that the
-    same run makes (the copy whose WRITE_SIZE is 1 GiB)."""
+    KiB per dispatch of L2-to-memory-side traffic; each is scaled by what it reads for the
+    1 GiB device copy that the same run makes (the copy whose WRITE_SIZE is 1 GiB)."""
     def load(path):
         out = {}
         with open(path) as f:
@@ -174,11 +177,13 @@ def summarize_counters(fetch_csv, write_csv, kernel, template, workload):
     w_kib = sum(write[d][1] for d in sel) / len(sel)
     read_b = f_kib * 1024 * f_scale
     write_b = w_kib * 1024 * w_scale
+    bench_cmd = BENCH_ONE_STEP.format(workload=workload) + " --copy-calibration"
     lines = [
-        f"# HBM traffic of dsa::{kernel}{template}, workload {workload}",
+        f"# memory-side traffic (L2 misses and write-backs: FETCH_SIZE, WRITE_SIZE; served by the",
+        f"# Infinity Cache or HBM) of dsa::{kernel}{template}, workload {workload}",
         "# commands, from the repository root on one MI355X (cd /tmp && export TMPDIR=/tmp first):",
-        "#   " + PMC_COMMAND.format(counter="FETCH_SIZE", dir="<fetch_dir>"),
-        "#   " + PMC_COMMAND.format(counter="WRITE_SIZE", dir="<write_dir>"),
+        "#   " + PMC_COMMAND.format(counter="FETCH_SIZE", dir="<fetch_dir>", bench=bench_cmd),
+        "#   " + PMC_COMMAND.format(counter="WRITE_SIZE", dir="<write_dir>", bench=bench_cmd),
         f"#   python3 bench.py --summarize-counters <fetch_dir>/run_counter_collection.csv "
         f"<write_dir>/run_counter_collection.csv --kernel {kernel} --template '{template}' --workload {workload}",
         f"calibration_copy_bytes: {COPY_BYTES}",
@@ -203,7 +208,7 @@ def summarize_pmc(csvs, kernel, template, workload, command):
     """Execution profile of one kernel from rocprofv3 counter runs (PMC_PASSES): the mean per
     launch of every counter, then the fractions derived from them.  Launches are matched by
     their order among the kernel's dispatches in each run; dispatches with a duration under
-    1% of the longest (the fused indexer's recompute pass when nothing failed) are left out."""
+    5% of the longest (the fused indexer's recompute pass when nothing failed) are left out."""
     per_run = []
     for path in csvs:
         rows = {}
@@ -219,7 +224,7 @@ def summarize_pmc(csvs, kernel, template, workload, command):
         raise SystemExit(f"no dispatches of {kernel}{template}")
     n = min(len(r) for r in per_run)
     top = max(d["ns"] for r in per_run for d in r[:n])
-    keep = [i for i in range(n) if all(r[i]["ns"] >= 0.01 * top for r in per_run)]
+    keep = [i for i in range(n) if all(r[i]["ns"] >= 0.05 * top for r in per_run)]
     vals, ns = {}, []
     for i in keep:
         for r in per_run:
@@ -332,7 +337,7 @@ def main():
         return
     if args.summarize_pmc:
         cmd = ('rocprofv3 --pmc {counters} --kernel-include-regex "dsa::" --output-format csv -d {dir} -o run -- '
-               + (args.pmc_command or "python3 bench.py ..."))
+               + (args.pmc_command or BENCH_ONE_STEP.format(workload=args.workload)))
         print(summarize_pmc(args.summarize_pmc, args.kernel, args.template, args.workload, cmd))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -742,7 +747,8 @@ def bench_decode(args, dsa, synth, accounting, torch, np, dev, stream):
 def bench_attainable(torch, dev, stream):
     """Measured ceilings on this GPU, for context beside the datasheet peaks: a large bf16
     GEMM and, where torch provides it, an fp8 one (hipBLASLt through torch; measurement only,
-    never on the library's path), and a 2 GiB device copy (read + write bytes)."""
+    never on the library's path), a 2 GiB device copy (read + write bytes) and a 2 GiB
+    reduction (read bytes)."""
     def timed(fn, n=5):
         fn()
         torch.cuda.synchronize()
@@ -779,10 +785,15 @@ def bench_attainable(torch, dev, stream):
     x.fill_(1.0)
     msc = timed(lambda: y.copy_(x))
     out["copy_gbs"] = round(2.0 * x.numel() * 4 / (msc * 1e-3) / 1e9, 1)
-    del x, y
+    # a read-only stream (a library reduction over 2 GiB, as int64 words): the reference for
+    # read-bound kernels
+    x64 = x.view(torch.int64)
+    msr = timed(lambda: torch.sum(x64))
+    out["read_gbs"] = round(x.numel() * 4 / (msr * 1e-3) / 1e9, 1)
+    del x, y, x64
     torch.cuda.empty_cache()
     log(f"[bench] attainable: bf16 GEMM {out['bf16_gemm_tflops']} TFLOP/s, fp8 GEMM {out['fp8_gemm_tflops']} "
-        f"TFLOP/s, device copy {out['copy_gbs']} GB/s")
+        f"TFLOP/s, device copy {out['copy_gbs']} GB/s, read {out['read_gbs']} GB/s")
     return out
 
 
