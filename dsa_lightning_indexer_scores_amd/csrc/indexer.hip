@@ -704,11 +704,13 @@ __device__ __forceinline__ uint32_t lane_prefix(uint32_t c, uint32_t& total) {
   return rank_below(b0) + 2u * rank_below(b1) + 4u * rank_below(b2);
 }
 
-// In-place stable compaction keeping the entries with take(key, eq_rank) true, where
-// eq_rank is the number of keys == theta that precede the entry.  Destinations never
-// pass the entries still to be read (out <= index), so the list can be compacted in place.
-template <typename Take>
-__device__ uint32_t compact_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, Take take) {
+// Stable compaction of the entries with take(key, eq, eq_rank) true, where eq_rank is the
+// number of keys == theta that precede the entry: put(dst, key, pos) receives the kept
+// entries at dst = 0, 1, ... in list order.  Destinations never pass the entries still to
+// be read (dst <= index), so put may write the list itself (in-place compaction).
+template <typename Take, typename Put>
+__device__ uint32_t compact_list(const uint32_t* keys, const uint32_t* pos, uint32_t n, uint32_t theta, Take take,
+                                 Put put) {
   const int lane = lane_id();
   uint32_t out = 0, eq_seen = 0;
   uint32_t ck[16], cp[16], nk[16], np[16];
@@ -738,8 +740,7 @@ __device__ uint32_t compact_list(uint32_t* keys, uint32_t* pos, uint32_t n, uint
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         if (tk[i]) {
-          keys[dst] = ck[4 * j + i];
-          pos[dst] = cp[4 * j + i];
+          put(dst, ck[4 * j + i], cp[4 * j + i]);
           ++dst;
         }
       out += t_tot;
@@ -768,16 +769,29 @@ __device__ void select_exact(const uint32_t* keys, uint32_t n, uint32_t k, uint3
   need_eq = krem - above;
 }
 
-// In-place stable compaction keeping keys > theta and the first need_eq keys == theta.
-__device__ uint32_t compact_exact(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, uint32_t need_eq) {
+// Stable compaction keeping keys > theta and the first need_eq keys == theta, in place or
+// into separate arrays (put).
+template <typename Put>
+__device__ uint32_t compact_exact_to(const uint32_t* keys, const uint32_t* pos, uint32_t n, uint32_t theta,
+                                     uint32_t need_eq, Put put) {
   return compact_list(keys, pos, n, theta, [=](uint32_t key, bool eq, uint32_t eq_rank) {
     return key > theta || (eq && eq_rank < need_eq);
+  }, put);
+}
+__device__ uint32_t compact_exact(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t theta, uint32_t need_eq) {
+  return compact_exact_to(keys, pos, n, theta, need_eq, [=](uint32_t d, uint32_t key, uint32_t p) {
+    keys[d] = key;
+    pos[d] = p;
   });
 }
 
 // In-place stable compaction keeping every key >= th.
 __device__ uint32_t compact_ge(uint32_t* keys, uint32_t* pos, uint32_t n, uint32_t th) {
-  return compact_list(keys, pos, n, th, [=](uint32_t key, bool, uint32_t) { return key >= th; });
+  return compact_list(keys, pos, n, th, [=](uint32_t key, bool, uint32_t) { return key >= th; },
+                      [=](uint32_t d, uint32_t key, uint32_t p) {
+                        keys[d] = key;
+                        pos[d] = p;
+                      });
 }
 
 // Exact top-k of a candidate list: afterwards keys/pos[0..min(n,k)) hold the k largest
@@ -794,6 +808,22 @@ __device__ uint32_t reduce_to_k(uint32_t* keys, uint32_t* pos, uint32_t n, uint3
   const uint32_t r = compact_exact(keys, pos, n, th, ne);
   __threadfence_block();
   return r;
+}
+
+// Exact top-k of a candidate list, written straight to its destination: put(j, key, pos)
+// receives the kept entries j = 0 .. min(n, k) - 1 in list order (the k largest keys, ties
+// to the earlier entry); the list itself is not modified.  Returns min(n, k).
+template <typename Put>
+__device__ uint32_t select_to(const uint32_t* keys, const uint32_t* pos, uint32_t n, uint32_t k, uint32_t* hist,
+                              Put put) {
+  __threadfence_block();   // the wave's own list stores are visible to its loads
+  if (n <= k) {
+    for (uint32_t j = (uint32_t)lane_id(); j < n; j += 64) put(j, keys[j], pos[j]);
+    return n;
+  }
+  uint32_t th, ne;
+  select_exact(keys, n, k, hist, th, ne);
+  return compact_exact_to(keys, pos, n, th, ne, put);
 }
 
 // Make room in a streaming candidate list that holds n > k entries: drop every key below
@@ -1171,34 +1201,43 @@ void indexer_topk_kernel(FusedParams P) {
     for (int tt = 0; tt < TW; ++tt)
       cnt[tt] = flush_stage(stg[wv_id * TW + tt], scnt[tt], rk[tt], rp[tt], cnt[tt]);
     __threadfence_block();
-#pragma unroll
-    for (int tt = 0; tt < TW; ++tt) {
+    // one call per token of the wave (unrolled by hand: the selection is large)
+    auto finish_row = [&](const int tt) {
       const int t = t0 + wv_id * TW + tt;
-      if (t >= a.Lq) continue;
+      if (t >= a.Lq) return;
       const int n_causal = max(0, min(p_t[tt] + 1, s_hi) - s_lo);
       if (P.S == 1 && spec[tt] && cnt[tt] < (uint32_t)min(P.k, n_causal)) {
         // too few keys passed the speculative threshold: the item is recomputed exactly
         if (lane == 0) P.fail_items[atomicAdd(P.fail_count, 1)] = item;
       }
-      uint32_t kth;
-      cnt[tt] = reduce_to_k(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id], kth);
       const size_t row = (size_t)b * a.Lq + t;
-      if (P.S == 1) {
-        int32_t* out = P.idx + row * P.k;
-        for (int j = lane; j < P.k; j += 64) out[j] = j < (int)cnt[tt] ? (int32_t)rp[tt][j] : -1;
+      // the top k go straight to the row's index row (one key segment: positions, -1 past
+      // a short list) or to the segment's list (keys and positions)
+      const bool one = P.S == 1;
+      int32_t* out = P.idx + row * P.k;
+      uint32_t* ok = P.seg_keys + row * P.seg_stride + (size_t)seg * P.k;
+      uint32_t* op = P.seg_pos + row * P.seg_stride + (size_t)seg * P.k;
+      cnt[tt] = select_to(rk[tt], rp[tt], cnt[tt], (uint32_t)P.k, hist[wv_id],
+                          [=](uint32_t d, uint32_t key, uint32_t p) {
+                            if (one) {
+                              out[d] = (int32_t)p;
+                            } else {
+                              ok[d] = key;
+                              op[d] = p;
+                            }
+                          });
+      if (one) {
+        for (int j = (int)cnt[tt] + lane; j < P.k; j += 64) out[j] = -1;
       } else {
-        uint32_t* ok = P.seg_keys + row * P.seg_stride + (size_t)seg * P.k;
-        uint32_t* op = P.seg_pos + row * P.seg_stride + (size_t)seg * P.k;
-        for (int j = lane; j < (int)cnt[tt]; j += 64) {
-          ok[j] = rk[tt][j];
-          op[j] = rp[tt][j];
-        }
         if (lane == 0) {
           P.seg_cnt[row * P.S + seg] = (int32_t)cnt[tt];
           P.seg_spec[row * P.S + seg] = spec[tt] ? theta0[tt] : 0u;
         }
       }
-    }
+    };
+    finish_row(0);
+    if constexpr (TW > 1) finish_row(1);
+    static_assert(TW <= 2, "finish_row calls");
   }
 }
 
