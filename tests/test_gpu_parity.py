@@ -26,7 +26,6 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
 TAU = {"bf16": 1e-3, "fp8": 2e-2, "f32": 1e-5}
-SCORE_RTOL = {"f32": 1e-5, "bf16": 1e-4, "fp8": 3e-3}
 
 
 def _cfg(dtype, L, k, **kw):
@@ -378,6 +377,40 @@ def test_paged_decode_equals_contiguous_caches(dtype, Lq, page):
     lay_pool["kv"] = _to_pool(lay["kv"], table, page, pool_pages)[None]
     got = dsa.sparse_attn(lay_pool, rows.reshape(1, B * Lq, k), out_dtype=torch.float32)
     assert torch.equal(got.reshape(ref.shape), ref)
+
+
+@pytest.mark.parametrize("dtype,L,k", [("fp8", 12000, 512), ("bf16", 6000, 256)])
+def test_future_keys_do_not_change_earlier_rows(dtype, L, k):
+    """Causality: overwriting every k^I row, key scale and latent KV row at positions past m
+    changes nothing in the index rows and attention outputs of the queries at positions < m
+    (bit for bit), through the fused indexer and the MLA kernel at sizes with several work
+    items per row and a ragged tail."""
+    cfg = _cfg(dtype, L, k)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    lay = synth.attention_inputs(cfg, layer=1, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    out = dsa.sparse_attn(lay, idx, out_dtype=torch.float32)
+    m = L // 2 + 37
+    ind2 = dict(ind)
+    kk = ind["k"].clone()
+    if kk.dtype == torch.uint8:
+        kk[:, m:] = 0x5A                                  # a finite E4M3 code (72)
+    else:
+        kk[:, m:] = 3.0
+    ind2["k"] = kk
+    if ind["k_scale"] is not None:
+        ks = ind["k_scale"].clone()
+        ks[:, m:] = 7.0
+        ind2["k_scale"] = ks
+    lay2 = dict(lay)
+    kv = lay["kv"].clone()
+    kv[:, m:] = -2.0
+    lay2["kv"] = kv
+    idx2 = dsa.indexer_topk(ind2["q"], ind2["k"], ind2["w"], k, **_ind_args(ind2))
+    out2 = dsa.sparse_attn(lay2, idx2, out_dtype=torch.float32)
+    assert torch.equal(idx[:, :m], idx2[:, :m])
+    assert torch.equal(out[:, :m], out2[:, :m])
+    assert not torch.equal(idx[:, m:], idx2[:, m:])       # the later rows did see the change
 
 
 def test_rows_shorter_than_k_select_every_causal_key():
