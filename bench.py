@@ -138,9 +138,19 @@ def summarize_trace(trace_csv):
             grid = (r.get("Grid_Size_X") or r.get("Grid_Size") or "?", r.get("Grid_Size_Y", "1"))
             dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
             groups.setdefault((name, grid), []).append(dur)
-    lines = ["kernel,grid_x,grid_y,calls,avg_us,min_us,max_us"]
-    for (name, grid), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        lines.append(f'"{name}",{grid[0]},{grid[1]},{len(d)},{sum(d) / len(d) / 1e3:.2f},'
+    # launches under 5% of the longest of their group (the fused indexer's near-empty
+    # recompute pass, for one) get a row of their own, marked "short"
+    rows = []
+    for (name, grid), d in groups.items():
+        top = max(d)
+        long_d = [x for x in d if x >= 0.05 * top]
+        short_d = [x for x in d if x < 0.05 * top]
+        rows.append((name, grid, "", long_d))
+        if short_d:
+            rows.append((name, grid, "short", short_d))
+    lines = ["kernel,grid_x,grid_y,launches,calls,avg_us,min_us,max_us"]
+    for name, grid, tag, d in sorted(rows, key=lambda r: -sum(r[3])):
+        lines.append(f'"{name}",{grid[0]},{grid[1]},{tag or "work"},{len(d)},{sum(d) / len(d) / 1e3:.2f},'
                      f'{min(d) / 1e3:.2f},{max(d) / 1e3:.2f}')
     return "\n".join(lines)
 
