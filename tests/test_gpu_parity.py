@@ -699,6 +699,8 @@ def _quant_inputs(dtype, T=37, H=64, D=128, seed=8):
     x[5] *= 1e-6                                  # subnormal codes
     x[7] *= 3e4
     x[9, 0, :4] = torch.tensor([-0.0, 1.0, -1.0, 0.0])
+    x[11] *= 1e-35                                # scale below 2^-100: quotients by division
+    x[13] *= 1e-40                                # subnormal inputs and scale
     return x.to(torch.bfloat16) if dtype == "bf16" else x
 
 
@@ -717,11 +719,13 @@ def test_quantize_e4m3_bit_exact(dtype, H, D):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_quantize_e4m3_rounding_boundaries(dtype):
+@pytest.mark.parametrize("width", [760, 1024])
+def test_quantize_e4m3_rounding_boundaries(dtype, width):
     """Quotients on and next to E4M3 rounding boundaries, with scales that are not powers
     of two (amax = 448 * 3 and 448 * 5 / 4): every midpoint between neighbouring codes
     (normal and subnormal), and the neighbouring representable inputs, must round exactly as
-    the single-precision quotient does (ties to even)."""
+    the single-precision quotient does (ties to even).  Rows of 760 values take the
+    two-pass kernel, rows of 1024 the register-resident one (reciprocal and correction)."""
     grid = decode_e4m3(np.arange(0x7F, dtype=np.uint8))          # 0 .. 448
     mids = (grid[:-1] + grid[1:]) / 2
     rows = []
@@ -733,8 +737,8 @@ def test_quantize_e4m3_rounding_boundaries(dtype):
         row = np.concatenate([[448.0 * c], x, near]).astype(np.float32)
         rows.append(row)
     n = max(len(r) for r in rows)
-    n = (n + 7) // 8 * 8
-    x = np.zeros((len(rows), n), np.float32)
+    assert n <= width
+    x = np.zeros((len(rows), width), np.float32)
     for i, r in enumerate(rows):
         x[i, :len(r)] = r
     xt = torch.from_numpy(x)
