@@ -10,10 +10,10 @@
 // token) and code = round-to-nearest-even of x / scale, both divisions in IEEE single
 // precision.
 //
-// Rows that fit in registers (up to 64 lanes x 16 pieces of 16 bytes) are read from memory
-// once: every lane loads its pieces, the row's lanes agree on the largest magnitude, and
-// the codes come from the values still held.  Other rows take one wave each and two
-// passes over the row.
+// Rows that fit in registers (up to 8192 values: 64 lanes x 16 or 32 pieces of 16 bytes)
+// are read from memory once: every lane loads its pieces, the row's lanes agree on the
+// largest magnitude, and the codes come from the values still held.  Other rows take one
+// wave each and two passes over the row.
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
 #include "../../include/dsa.h"
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void quantize_e4m3_rows_kernel(const void* __r
                                                                  uint8_t* __restrict__ codes, int64_t c_stride,
                                                                  float* __restrict__ scales, int64_t s_stride) {
   constexpr int kPer = kBf16 ? 8 : 4;          // values per 16-byte piece
-  constexpr int kMaxPieces = 16;
+  constexpr int kMaxPieces = kBf16 ? 16 : 32;   // 8192 values either way
   constexpr int kEsize = kBf16 ? 2 : 4;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -181,7 +181,7 @@ hipError_t launch_quantize_e4m3(const void* x, int x_dtype, int rows, int row_el
     if (pieces <= 64 && (pieces & (pieces - 1)) == 0) {
       lpr_log2 = __builtin_ctz((unsigned)pieces);
       n_pieces = 1;
-    } else if (pieces % 64 == 0 && pieces / 64 <= 16) {
+    } else if (pieces % 64 == 0 && pieces / 64 <= (bf ? 16 : 32)) {
       lpr_log2 = 6;
       n_pieces = pieces / 64;
     }
