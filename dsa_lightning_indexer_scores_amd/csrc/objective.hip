@@ -12,9 +12,9 @@
 //   dw[t, j] = sum_s (pi - pbar)[s] ReLU(x),   dq[t, j] = sum_s c[j, s] k[s],
 //   dk[s]   += sum_t sum_j c[j, s] q[t, j]   (accumulated over the rows that selected s).
 //
-// attn_probs_kernel: one layer's head-averaged distribution on S_t, recomputed from the
-// layer's queries, latent rows and log-sum-exp (that of dsa_sparse_attn), accumulated
-// with a weight: P[t, i] += alpha / H sum_h exp(sm_scale q[t, h] . K[S_t[i]] - lse[t, h]).
+// dsa_attn_probs (one layer's head-averaged distribution on S_t, recomputed from the
+// layer's queries, latent rows and log-sum-exp) runs attn_probs32_kernel, which shares
+// the gathered 32-key blocks of the sparse attention kernels (attn.hip).
 //
 // indexer_kl_kernel: one workgroup per query row (75 KB of LDS: two per CU), selected keys
 // in tiles of 64 gathered to LDS (row-major for the scores, transposed for dq).  Pass 1 scores every tile (wave w
@@ -30,8 +30,6 @@
 namespace dsa {
 
 namespace {
-constexpr int kLatent = 576;
-constexpr int kLatentPad = 584;   // LDS row of a query head: 16 rows of a read start in distinct banks
 constexpr int kDI = 128;          // indexer head dim
 constexpr int kTile = 64;         // selected keys per tile
 // LDS tiles are unpadded; their 16-byte chunks are XOR-swizzled by the row so that the 16
@@ -44,67 +42,6 @@ __device__ __forceinline__ int sw64(int row, int col) {
   return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
 }
 }  // namespace
-
-template <int HB>
-__global__ __launch_bounds__(256) void attn_probs_kernel(AttnProbsArgs a) {
-  constexpr int H = 16 * HB;
-  __shared__ __attribute__((aligned(16))) __bf16 qs[H * kLatentPad];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = blockIdx.x;                       // query row (b, i)
-  const int b = r / a.Lq;
-  const __bf16* q = static_cast<const __bf16*>(a.q) + (size_t)r * H * kLatent;
-  for (int e = tid; e < H * (kLatent / 8); e += 256) {
-    const int h = e / (kLatent / 8), c = e - h * (kLatent / 8);
-    *reinterpret_cast<bf16x8*>(&qs[h * kLatentPad + 8 * c]) = *reinterpret_cast<const bf16x8*>(q + h * kLatent + 8 * c);
-  }
-  float lse[HB];
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) lse[hb] = a.lse[(size_t)r * H + 16 * hb + (lane & 15)];
-  __syncthreads();
-  const int32_t* irow = a.idx + (size_t)r * a.idx_q_stride;
-  const __bf16* kv = static_cast<const __bf16*>(a.kv) + (size_t)b * a.Lk * a.k_row_stride;
-  float* prow = a.P + (size_t)r * a.k;
-  const float wscale = a.alpha / (float)H;
-  for (int base = 16 * wv; base < a.k; base += 64) {
-    // A: the key rows (lane: key base + l % 16), B: the query heads (lane: head l % 16)
-    const int slot = base + (lane & 15);
-    const int s = slot < a.k ? irow[slot] : -1;
-    const __bf16* krow = kv + (size_t)(s >= 0 && s < a.Lk ? s : 0) * a.k_row_stride;
-    f32x4 acc[HB];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 6
-    for (int ks = 0; ks < kLatent / 32; ++ks) {
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(krow + 32 * ks + 8 * (lane >> 4));
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) {
-        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&qs[(16 * hb + (lane & 15)) * kLatentPad + 32 * ks + 8 * (lane >> 4)]);
-        acc[hb] = mfma_bf16_16x16x32(av, bv, acc[hb]);
-      }
-    }
-    // acc[hb] lane l: head 16 hb + l % 16, keys base + 4 (l / 16) + i
-    float ps[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float v = 0.f;
-#pragma unroll
-      for (int hb = 0; hb < HB; ++hb) v += expf(a.sm_scale * acc[hb][i] - lse[hb]);
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off);   // the 16 heads of the lane's row
-      ps[i] = v;
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sl = base + 4 * (lane >> 4) + i;
-        if (sl < a.k) {
-          const int si = irow[sl];
-          if (si >= 0 && si < a.Lk) prow[sl] += wscale * ps[i];
-        }
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 template <int HB>
@@ -342,12 +279,6 @@ __global__ __launch_bounds__(256) void indexer_kl_kernel(IndexerKlArgs a) {
   }
 }
 
-hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s) {
-  const int rows = a.B * a.Lq;
-  if (a.H == 16) attn_probs_kernel<1><<<rows, 256, 0, s>>>(a);
-  else attn_probs_kernel<2><<<rows, 256, 0, s>>>(a);
-  return hipGetLastError();
-}
 
 // dk[e] += the fixed-point sum of element e (two's complement in 64 bits)
 __global__ __launch_bounds__(256) void dk_fix_add_kernel(const unsigned long long* __restrict__ fix,
