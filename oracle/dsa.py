@@ -1,8 +1,7 @@
 """fp64 definitions of the indexer score, the top-k selection, sparse attention and the
 IndexShare layer group (test infrastructure only; see the package docstring).
 
-Conventions shared by every function (the readings of the pages are listed in the
-design notes of the repository):
+Conventions shared by every function:
 
 * Batched rows: query i of a call with Lq queries and Lk keys sits at position
   p_i = Lk - Lq + i and may see keys s <= p_i (causality, GLM-5.2 技术报告速览,
