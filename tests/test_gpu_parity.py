@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
 
-Bars (see the design notes for their derivation):
+Bars (each derived where it is used, from the arithmetic of the kernel it checks):
 * dsa_topk fed the oracle's fp32 scores: bit-exact (same idx array, order, padding).
 * materialised scores: an element bound from the arithmetic (exact operand products,
   accumulation error of each dot product and of the head-weighted sum; see EPS_DOT).
