@@ -38,7 +38,9 @@ MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 # A summary is used only while the kernel's sources still hash to the digest it records;
 # otherwise the traffic is reported as null.
 PKG = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd")
-KERNEL_SOURCES = {"mla_attn32_kernel": ["csrc/attn.hip"], "indexer_topk_kernel": ["csrc/indexer.hip"]}
+KERNEL_SOURCES = {"mla_attn32_kernel": ["csrc/attn.hip", "csrc/mla_blocks.hpp"],
+                  "mla_combine_kernel": ["csrc/attn.hip", "csrc/mla_blocks.hpp"],
+                  "indexer_topk_kernel": ["csrc/indexer.hip"]}
 COMMON_SOURCES = ["csrc/dsa_common.hpp", "csrc/dsa_launch.hpp", "build_lib.py"]
 TRAFFIC_SUMMARY = {"sparse_attn": ("mla_attn32_kernel", "profiles/mla_attn32_kernel_prefill128k_memtraffic.txt"),
                    "indexer_topk": ("indexer_topk_kernel", "profiles/indexer_topk_kernel_prefill128k_memtraffic.txt")}

@@ -24,18 +24,12 @@
 // (row/2) % 8, so the 16 rows read by one MFMA operand fall in distinct banks.
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
+#include "mla_blocks.hpp"
 #include "../../include/dsa.h"
 
 namespace dsa {
 
-constexpr int kMlaD = 576;
-constexpr int kMlaDv = 512;
-constexpr int kBlk = 16;                        // keys per block
-constexpr int kRowBytes = kMlaD * 2;            // 1152
-constexpr int kChunks = kRowBytes / 16;         // 72 chunks of 16 B per row
-constexpr int kBlkBytes = kBlk * kRowBytes;     // 18432
 constexpr int kDmaPerBlk = kBlkBytes / 1024;    // 18 wave-wide 1 KB direct-to-LDS loads
-constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleGap = 8.0f;             // log2 headroom before the max is raised
 constexpr float kMaxStart = 1e30f;              // initial running maximum is -kMaxStart
 constexpr int kKeyBufs = 4;                     // idx ring slots (j .. j+2 in use)
@@ -44,11 +38,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const uint8_t* p) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p));
 }
-
-template <int N>
-struct Phase {
-  static constexpr int value = N;
-};
 
 __device__ __forceinline__ f32x4 sp_plus(f32x4 lo_half, f32x4 hi_half) { return lo_half + hi_half; }
 
@@ -350,42 +339,6 @@ void mla_attn_kernel(MlaParams P) {
 // hi and lo parts of p are two MFMAs on the same operand, and each 32 keys take three
 // barriers and one max reduction instead of four and two.
 // ---------------------------------------------------------------------------
-constexpr int kBlk2 = 32;                        // keys per block
-constexpr int kBlk2Bytes = 2 * kBlkBytes;        // 36864
-constexpr int kDmaPerBlk2 = kBlk2Bytes / 1024;   // 36 wave-wide 1 KB direct-to-LDS loads
-
-
-// LDS layout of a 36 KB block of 32 latent rows: key group w (keys 8 w .. 8 w + 7)
-// occupies 9 KB, whose 1 KB segment u holds bytes [128 u, 128 u + 128) of the 8 rows, row r
-// at 128 r with its 16-byte chunks XOR-swizzled by the row: chunk c sits in slot c ^ r.  One
-// direct-to-LDS load fills one segment of one group (lane l: row l / 8, slot l % 8), so a
-// lane needs one key per group, the nine segments of a row differ only by an immediate
-// offset, and each load covers eight whole 128-byte lines.  Measured on gfx950 (an LDS
-// access probe): with this swizzle the K operand reads (ds_read_b128) run conflict-free at
-// about 246 bytes per clock and CU, and the transposed V^T reads (ds_read_b64_tr_b16) at
-// about 206; the row-major layout reached 128 on the V^T reads, and a swizzle by
-// ((r & 3) << 1) | (r >> 2) about 130 on both.
-constexpr int kSegBytes = 1024;                   // one 128-byte segment of 8 rows
-constexpr int kGroupBytes = 9 * kSegBytes;        // 8 rows of 1152 bytes
-
-__device__ __forceinline__ int sw8(int r) { return r; }
-
-// byte offset of 16-byte chunk c of row r of a block in that layout
-__device__ __forceinline__ int blk_chunk_off(int r, int c) {
-  return (r >> 3) * kGroupBytes + (c >> 3) * kSegBytes + (r & 7) * 128 + 16 * ((c & 7) ^ sw8(r & 7));
-}
-
-// segments U .. U1-1 of one key group: src is the lane's address in its row (slot included),
-// lds the group's LDS address
-template <int U, int U1>
-__device__ __forceinline__ void dma_group_segs(const uint8_t* src, uint32_t lds) {
-  if constexpr (U < U1) {
-    // the instruction offset moves the LDS destination as well as the global address
-    dma_16o<128 * U>(src, lds + (kSegBytes - 128) * U);
-    dma_group_segs<U + 1, U1>(src, lds);
-  }
-}
-
 // NB = latent row buffers: block j is computed from buffer j % NB while the rows of
 // blocks j+1 .. j+NB-1 are in flight.  NB = 2 leaves room for two workgroups per CU (the
 // prefill grids); NB = 4 takes most of the LDS for one workgroup per CU with three blocks
@@ -846,139 +799,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   if (a.lse && tid == 0) a.lse[qh] = L > 0.f ? M + logf(L) : -INFINITY;
 }
 
-// ---------------------------------------------------------------------------
-// One layer's head-averaged attention distribution on each query's index row, for the
-// group centroid of the kept indexer's training (dsa_attn_probs):
-//   P[r, i] += alpha / H sum_h exp(sm_scale q[r, h] . K[S_r[i]] - lse[r, h]).
-// The gather and the score MFMAs are those of mla_attn32_kernel (two row buffers of 32
-// latent rows, idx ring two blocks ahead, wave (ht, ds) scores sub-block ds against head
-// tile ht with Q^T in registers; here Q^T is the A operand, so a lane holds four heads of
-// one key).  The log-sum-exp is known, so there is no running maximum and no exchange
-// inside a block: a lane adds its four heads and two lane swaps add the four lane groups,
-// and with 32 heads the second head tile's sums reach the first through LDS.
-// A block's P entries are written one block later (after the next block barrier), from
-// values of P loaded when the block started, so every block takes one barrier and the
-// read-modify-write of P waits on no load.  Each P entry is written once per call, by
-// one lane, so results do not depend on timing.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_probs32_kernel(AttnProbsArgs a) {
-  constexpr int NB = 2;
-  constexpr int kQSteps = 18;
-  constexpr int kKeyAhead = 2 * NB - 2;
-  constexpr int kKeyBufs2 = 4;
-  __shared__ __attribute__((aligned(16))) uint8_t lrows[NB * kBlk2Bytes];
-  __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs2][kBlk2];
-  __shared__ float xsum[2][2][16];                 // [block parity][sub-block][key]: head tile 1
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
-  const int wv_id = uniform(tid >> 6);
-  const int hpq = a.H / 16;                        // head tiles (1 or 2)
-  const int ht = wv_id % hpq;
-  const int ds = wv_id / hpq;
-  const bool wave_active = wv_id < 2 * hpq;
-  const int r = blockIdx.x;                        // query row b * Lq + i
-  const int b = r / a.Lq;
-  const int32_t* idx_row = a.idx + (size_t)r * a.idx_q_stride;
-  const int nb = (a.k + kBlk2 - 1) / kBlk2;
-  const uint8_t* kvbase = static_cast<const uint8_t*>(a.kv) + (size_t)b * a.Lk * a.k_row_stride * 2;
-  const uint32_t row_bytes32 = (uint32_t)(a.k_row_stride * 2);
-  float* prow = a.P + (size_t)r * a.k;
-  const float wscale = a.alpha / (float)a.H;
-
-  // idx entries of block t into ring slot t % 4 (lanes 0..31; every wave issues the same
-  // load, so its own vmcnt covers them); entries past k are -1
-  auto issue_keys = [&](int t) {
-    int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
-    const int pos = t * kBlk2 + lane;
-    if (lane < kBlk2) {
-      if (pos < a.k) dma_4(idx_row + pos, lds_offset(slot));
-      else slot[lane] = -1;
-    }
-  };
-  // the 32 rows of block t: wave w loads key group w (rows 8 w + lane / 8), nine segments
-  const int dr = lane >> 3;
-  const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ sw8(dr));
-  auto issue_rows = [&](int t, int buf) {
-    const uint32_t key = (uint32_t)keyring[t & (kKeyBufs2 - 1)][8 * wv_id + dr];
-    const uint8_t* src = kvbase + (uint64_t)(key < (uint32_t)a.Lk ? key : 0u) * row_bytes32 + dchunk;
-    dma_group_segs<0, 9>(src, lds_offset(lrows + buf * kBlk2Bytes + wv_id * kGroupBytes));
-  };
-
-  for (int t = 0; t < kKeyAhead && t < nb; ++t) issue_keys(t);
-  const int h = ht * 16 + r16;
-  bf16x8 qop[kQSteps];
-  {
-    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
-        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)r * a.H + (wave_active ? h : 0)) * kMlaD);
-#pragma unroll
-    for (int ks = 0; ks < kQSteps; ++ks) qop[ks] = qrow[4 * ks + g];
-  }
-  const float sl2 = a.sm_scale * kLog2e;
-  float lse2[4];                                   // heads 16 ht + 4 g + i
-#pragma unroll
-  for (int i = 0; i < 4; ++i) lse2[i] = a.lse[(size_t)r * a.H + (wave_active ? ht * 16 + 4 * g + i : 0)] * kLog2e;
-  int k_off0, k_off1;
-  {
-    const int w = 2 * ds + (r16 >> 3), rr = r16 & 7;
-    k_off0 = w * kGroupBytes + rr * 128 + 16 * (g ^ sw8(rr));
-    k_off1 = w * kGroupBytes + rr * 128 + 16 * ((4 + g) ^ sw8(rr));
-  }
-  // lanes 0..15 of head tile 0 own slot 16 ds + r16 of every block: its P entry is the
-  // loaded old value plus the wave's head sum and, with 32 heads, head tile 1's from LDS
-  const bool owner = wave_active && ht == 0 && g == 0;
-  const int sl = 16 * ds + r16;
-  auto put = [&](int t, float own, float old) {
-    float v = own;
-    if (hpq == 2) v += xsum[t & 1][ds][r16];
-    const int key = keyring[t & (kKeyBufs2 - 1)][sl];
-    const int pos = t * kBlk2 + sl;
-    if (pos < a.k && (uint32_t)key < (uint32_t)a.Lk) prow[pos] = old + wscale * v;
-  };
-  __builtin_amdgcn_s_waitcnt(0);                   // operands and the first idx entries
-  if (nb > 0) {
-    __syncthreads();
-    issue_rows(0, 0);
-  }
-  float held = 0.f, pold = 0.f;                     // owners: the previous block's sum and old P
-  for (int j = 0; j < nb; ++j) {
-    const int buf = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of j, idx of j+1, P of j-1
-    __syncthreads();                                     // landed for all; buffer of j-1 free
-    if (owner && j > 0) put(j - 1, held, pold);
-    if (owner) pold = j * kBlk2 + sl < a.k ? prow[j * kBlk2 + sl] : 0.f;
-    if (j + kKeyAhead < nb) issue_keys(j + kKeyAhead);
-    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1);
-    if (wave_active) {
-      const uint8_t* kb = lrows + buf * kBlk2Bytes;
-      bf16x8 kop[kQSteps];
-#pragma unroll
-      for (int ks = 0; ks < kQSteps; ++ks)
-        kop[ks] = *reinterpret_cast<const bf16x8*>(kb + (ks & 1 ? k_off1 : k_off0) + kSegBytes * (ks >> 1));
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < kQSteps; ks += 2) {
-        s0 = mfma_bf16_16x16x32(qop[ks], kop[ks], s0);
-        s1 = mfma_bf16_16x16x32(qop[ks + 1], kop[ks + 1], s1);
-      }
-      const f32x4 s = s0 + s1;
-      // lane: key 16 ds + r16, heads 16 ht + 4 g + i
-      float e = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(s[i] * sl2 - lse2[i]);
-      const float mine = wave_sum16x4(e);              // the 16 heads of the tile
-      if (g == 0) {
-        if (ht == 1) xsum[j & 1][ds][r16] = mine;
-        else held = mine;
-      }
-    }
-  }
-  __syncthreads();                                       // head tile 1's sums of the last block
-  if (owner && nb > 0) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // P of the last block
-    put(nb - 1, held, pold);
-  }
-}
-
 struct MlaPlan {
   int nq, dvs, nw, n_groups, n_split, bps;
   bool k32;           // mla_attn32_kernel (32-key blocks, one query per workgroup)
@@ -1026,11 +846,6 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
 size_t sparse_attn_ws(int B, int Lq, int k, int H, int64_t idx_q_stride, int dtype) {
   if (dtype != DSA_BF16) return 0;
   return plan_mla(B, Lq, k, H, idx_q_stride).total;
-}
-
-hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s) {
-  attn_probs32_kernel<<<a.B * a.Lq, 256, 0, s>>>(a);
-  return hipGetLastError();
 }
 
 hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipStream_t s) {

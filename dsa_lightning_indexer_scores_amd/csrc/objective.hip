@@ -12,9 +12,9 @@
 //   dw[t, j] = sum_s (pi - pbar)[s] ReLU(x),   dq[t, j] = sum_s c[j, s] k[s],
 //   dk[s]   += sum_t sum_j c[j, s] q[t, j]   (accumulated over the rows that selected s).
 //
-// dsa_attn_probs (one layer's head-averaged distribution on S_t, recomputed from the
-// layer's queries, latent rows and log-sum-exp) runs attn_probs32_kernel, which shares
-// the gathered 32-key blocks of the sparse attention kernels (attn.hip).
+// attn_probs32_kernel: one layer's head-averaged distribution on S_t, recomputed from the
+// layer's queries, latent rows and log-sum-exp (that of dsa_sparse_attn), accumulated
+// with a weight, in the gathered 32-key blocks of the sparse attention (mla_blocks.hpp).
 //
 // indexer_kl_kernel: one workgroup per query row (75 KB of LDS: two per CU), selected keys
 // in tiles of 64 gathered to LDS (row-major for the scores, transposed for dq).  Pass 1 scores every tile (wave w
@@ -25,6 +25,7 @@
 // added to the global dk with fp32 atomics.
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
+#include "mla_blocks.hpp"
 #include "../../include/dsa.h"
 
 namespace dsa {
@@ -42,6 +43,146 @@ __device__ __forceinline__ int sw64(int row, int col) {
   return row * 64 + ((((col >> 3) ^ (row & 7)) << 3) | (col & 7));
 }
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// One layer's head-averaged attention distribution on each query's index row, for the
+// group centroid of the kept indexer's training (dsa_attn_probs):
+//   P[r, i] += alpha / H sum_h exp(sm_scale q[r, h] . K[S_r[i]] - lse[r, h]).
+// The gather and the score MFMAs are those of the sparse attention's mla_attn32_kernel
+// (attn.hip; the block layout is in mla_blocks.hpp): two row buffers of 32 latent rows,
+// the idx ring two blocks ahead, wave (ht, ds) scoring sub-block ds against head tile ht
+// with Q^T in registers (here Q^T is the A operand, so a lane holds four heads of one
+// key).  The log-sum-exp is known, so there is no running maximum and no exchange
+// inside a block: a lane adds its four heads and two lane swaps add the four lane groups,
+// and with 32 heads the second head tile's sums reach the first through LDS.
+// A block's P entries are written one block later (after the next block barrier), from
+// values of P loaded when the block started, so every block takes one barrier and the
+// read-modify-write of P waits on no load.  Each P entry is written once per call, by
+// one lane, so results do not depend on timing.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_probs32_kernel(AttnProbsArgs a) {
+  constexpr int NB = 2;
+  constexpr int kQSteps = 18;
+  constexpr int kKeyAhead = 2 * NB - 2;
+  constexpr int kKeyBufs2 = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lrows[NB * kBlk2Bytes];
+  __shared__ __attribute__((aligned(16))) int keyring[kKeyBufs2][kBlk2];
+  __shared__ float xsum[2][2][16];                 // [block parity][sub-block][key]: head tile 1
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wv_id = uniform(tid >> 6);
+  const int hpq = a.H / 16;                        // head tiles (1 or 2)
+  const int ht = wv_id % hpq;
+  const int ds = wv_id / hpq;
+  const bool wave_active = wv_id < 2 * hpq;
+  const int r = blockIdx.x;                        // query row b * Lq + i
+  const int b = r / a.Lq;
+  // the idx row of (b, i) as in dsa_sparse_attn: one per query, or one per sequence
+  const int32_t* idx_row = a.idx_q_stride ? a.idx + (size_t)r * a.idx_q_stride : a.idx + (size_t)b * a.k;
+  const int nb = (a.k + kBlk2 - 1) / kBlk2;
+  const uint8_t* kvbase = static_cast<const uint8_t*>(a.kv) + (size_t)b * a.Lk * a.k_row_stride * 2;
+  const uint32_t row_bytes32 = (uint32_t)(a.k_row_stride * 2);
+  float* prow = a.P + (size_t)r * a.k;
+  const float wscale = a.alpha / (float)a.H;
+
+  // idx entries of block t into ring slot t % 4 (lanes 0..31; every wave issues the same
+  // load, so its own vmcnt covers them); entries past k are -1
+  auto issue_keys = [&](int t) {
+    int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
+    const int pos = t * kBlk2 + lane;
+    if (lane < kBlk2) {
+      if (pos < a.k) dma_4(idx_row + pos, lds_offset(slot));
+      else slot[lane] = -1;
+    }
+  };
+  // the 32 rows of block t: wave w loads key group w (rows 8 w + lane / 8), nine segments
+  const int dr = lane >> 3;
+  const uint32_t dchunk = 16u * (uint32_t)((lane & 7) ^ sw8(dr));
+  auto issue_rows = [&](int t, int buf) {
+    const uint32_t key = (uint32_t)keyring[t & (kKeyBufs2 - 1)][8 * wv_id + dr];
+    const uint8_t* src = kvbase + (uint64_t)(key < (uint32_t)a.Lk ? key : 0u) * row_bytes32 + dchunk;
+    dma_group_segs<0, 9>(src, lds_offset(lrows + buf * kBlk2Bytes + wv_id * kGroupBytes));
+  };
+
+  for (int t = 0; t < kKeyAhead && t < nb; ++t) issue_keys(t);
+  const int h = ht * 16 + r16;
+  bf16x8 qop[kQSteps];
+  {
+    const bf16x8* qrow = reinterpret_cast<const bf16x8*>(
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)r * a.H + (wave_active ? h : 0)) * kMlaD);
+#pragma unroll
+    for (int ks = 0; ks < kQSteps; ++ks) qop[ks] = qrow[4 * ks + g];
+  }
+  const float sl2 = a.sm_scale * kLog2e;
+  float lse2[4];                                   // heads 16 ht + 4 g + i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lse2[i] = a.lse[(size_t)r * a.H + (wave_active ? ht * 16 + 4 * g + i : 0)] * kLog2e;
+  int k_off0, k_off1;
+  {
+    const int w = 2 * ds + (r16 >> 3), rr = r16 & 7;
+    k_off0 = w * kGroupBytes + rr * 128 + 16 * (g ^ sw8(rr));
+    k_off1 = w * kGroupBytes + rr * 128 + 16 * ((4 + g) ^ sw8(rr));
+  }
+  // lanes 0..15 of head tile 0 own slot 16 ds + r16 of every block: its P entry is the
+  // loaded old value plus the wave's head sum and, with 32 heads, head tile 1's from LDS
+  const bool owner = wave_active && ht == 0 && g == 0;
+  const int sl = 16 * ds + r16;
+  auto put = [&](int t, float own, float old) {
+    float v = own;
+    if (hpq == 2) v += xsum[t & 1][ds][r16];
+    const int key = keyring[t & (kKeyBufs2 - 1)][sl];
+    const int pos = t * kBlk2 + sl;
+    if (pos < a.k && (uint32_t)key < (uint32_t)a.Lk) prow[pos] = old + wscale * v;
+  };
+  __builtin_amdgcn_s_waitcnt(0);                   // operands and the first idx entries
+  if (nb > 0) {
+    __syncthreads();
+    issue_rows(0, 0);
+  }
+  float held = 0.f, pold = 0.f;                     // owners: the previous block's sum and old P
+  for (int j = 0; j < nb; ++j) {
+    const int buf = j & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // rows of j, idx of j+1, P of j-1
+    __syncthreads();                                     // landed for all; buffer of j-1 free
+    if (owner && j > 0) put(j - 1, held, pold);
+    if (owner) pold = j * kBlk2 + sl < a.k ? prow[j * kBlk2 + sl] : 0.f;
+    if (j + kKeyAhead < nb) issue_keys(j + kKeyAhead);
+    if (j + 1 < nb) issue_rows(j + 1, buf ^ 1);
+    if (wave_active) {
+      const uint8_t* kb = lrows + buf * kBlk2Bytes;
+      bf16x8 kop[kQSteps];
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ++ks)
+        kop[ks] = *reinterpret_cast<const bf16x8*>(kb + (ks & 1 ? k_off1 : k_off0) + kSegBytes * (ks >> 1));
+      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kQSteps; ks += 2) {
+        s0 = mfma_bf16_16x16x32(qop[ks], kop[ks], s0);
+        s1 = mfma_bf16_16x16x32(qop[ks + 1], kop[ks + 1], s1);
+      }
+      const f32x4 s = s0 + s1;
+      // lane: key 16 ds + r16, heads 16 ht + 4 g + i
+      float e = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e += __builtin_amdgcn_exp2f(s[i] * sl2 - lse2[i]);
+      const float mine = wave_sum16x4(e);              // the 16 heads of the tile
+      if (g == 0) {
+        if (ht == 1) xsum[j & 1][ds][r16] = mine;
+        else held = mine;
+      }
+    }
+  }
+  __syncthreads();                                       // head tile 1's sums of the last block
+  if (owner && nb > 0) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // P of the last block
+    put(nb - 1, held, pold);
+  }
+}
+
+hipError_t launch_attn_probs(const AttnProbsArgs& a, hipStream_t s) {
+  attn_probs32_kernel<<<a.B * a.Lq, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 template <int HB>

@@ -359,8 +359,10 @@ int dsa_linear_bf16(const void* x, int64_t x_row_stride, const void* w, int64_t 
  * for idx entries S_r[i] in [0, Lk) (other entries are left unchanged).  in is the
  * layer's dsa_attn_in as given to dsa_sparse_attn (MLA: Hkv = 1, Dqk = 576, bf16, H = 16
  * or 32; K is the whole latent row); lse [B, Lq, H] is what dsa_sparse_attn wrote for the
- * same idx (natural-log sum of exp(sm_scale q . K) over the row); idx row r at idx + r *
- * idx_q_stride (k, or 0 to share row 0), k entries; P [B, Lq, k] fp32, caller-owned.
+ * same idx (natural-log sum of exp(sm_scale q . K) over the row); the idx row of (b, i) is
+ * that of dsa_sparse_attn, idx + b * (idx_q_stride ? Lq * idx_q_stride : k) + i *
+ * idx_q_stride (idx_q_stride = k: one row per query; 0: the Lq queries of a sequence share
+ * one row), k entries; P [B, Lq, k] fp32, caller-owned.
  * Returns DSA_OK, DSA_ERR_ARG, DSA_ERR_DTYPE, DSA_ERR_SHAPE, DSA_ERR_ALIGN or DSA_ERR_HIP.
  */
 int dsa_attn_probs(const dsa_attn_in* in, const float* lse, int B, int Lq, int Lk, const int32_t* idx,

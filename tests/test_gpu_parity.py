@@ -892,6 +892,30 @@ def test_attention_centroid_parity(H):
         assert np.all(pbar[b][idx_h[b] < 0] == 0)
 
 
+@pytest.mark.parametrize("H,L,Lq,k,shared", [(32, 300, 300, 100, False), (16, 260, 260, 72, False),
+                                              (32, 900, 4, 96, True), (16, 700, 3, 40, True)])
+def test_attention_centroid_ragged_and_shared_rows(H, L, Lq, k, shared):
+    """The centroid on index rows whose length is not a multiple of the 32-key block, with
+    -1 padding on the early rows, and on one index row shared by the queries of a sequence
+    (idx_q_stride 0, the MTP-draft case), against the oracle (relative 1e-4)."""
+    cfg = synth.get_config("prefill16k", L=L, Lq=Lq, B=2, topk=k, H=H, H_I=64)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k)
+    if shared:
+        idx = idx[:, -1:].contiguous()               # the last query's row, causal for all
+    layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(2)]
+    lses = [dsa.sparse_attn(lay, idx, return_lse=True)[1] for lay in layers]
+    pbar = dsa.attention_centroid(layers, idx, lses).cpu().numpy()
+    idx_h = idx.cpu().numpy()
+    for b in range(cfg.B):
+        rows_idx = np.repeat(idx_h[b][:1], Lq, axis=0) if shared else idx_h[b]
+        ora_layers = [{"q": to_f64(lay["q"][b]), "k": to_f64(lay["kv"][b])[:, None, :], "sm_scale": lay["sm_scale"]}
+                      for lay in layers]
+        ref = oracle.attention_centroid_rows(ora_layers, rows_idx, list(range(Lq)))
+        np.testing.assert_allclose(pbar[b], ref, rtol=1e-4, atol=1e-7)
+        assert np.all(pbar[b][rows_idx < 0] == 0)
+
+
 def test_indexer_kl_backward_dk_is_deterministic():
     """dk sums each key's contributions in 64-bit fixed point, so repeated calls give the
     same bits whatever order the rows arrive in, and a given dk is added to exactly once
