@@ -559,6 +559,13 @@ void mla_attn32_kernel(MlaParams P) {
     float sv[4];
     f32x4 kscale4 = {1.f, 1.f, 1.f, 1.f};           // KV8: the scales of this lane's keys
     float own_max = -INFINITY;
+    // Issue priority of the waves sharing a SIMD (two workgroups per CU in prefill):
+    // the score -> block maximum -> probabilities chain, whose steps end in the
+    // exchange barriers, goes first (2 for the K reads, score MFMAs and maximum, 1 for
+    // the probabilities); the value MFMAs (16 independent accumulators) and the row
+    // loads of the next block fill the issue slots left over (0).  Timed at 128K:
+    // 3% faster per layer than equal priorities, identical output.
+    __builtin_amdgcn_s_setprio(2);
     if (wave_active) {
       // S^T of sub-block ds: two independent chains (even and odd steps)
       constexpr int kKAhead = 4;
@@ -604,6 +611,7 @@ void mla_attn32_kernel(MlaParams P) {
       own_max = wave_max16x4(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
       xm[wv_id][lane] = own_max;
     }
+    __builtin_amdgcn_s_setprio(1);
     if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C3{}, C6{});
     __syncthreads();                                     // B2: block maxima exchanged
     if (wave_active) {
@@ -630,6 +638,7 @@ void mla_attn32_kernel(MlaParams P) {
       const uint32_t l23 = pack_bf16x2(pj[2] - __uint_as_float(h23 << 16), pj[3] - __uint_as_float(h23 & 0xffff0000u));
       xp[wv_id][lane] = i32x4{(int)h01, (int)h23, (int)l01, (int)l23};
     }
+    __builtin_amdgcn_s_setprio(0);
     if (j + NB - 1 < nb) issue_rows(j + NB - 1, nbuf, C6{}, C9{});
     __syncthreads();                                     // B3: probabilities exchanged
     if (wave_active) {

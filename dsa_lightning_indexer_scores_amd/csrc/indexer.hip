@@ -1139,9 +1139,16 @@ void indexer_topk_kernel(FusedParams P) {
       if (kBufs == 3 && it + 1 < n_tiles) wait_vm_at_most<kDmaPerWave + 1>(tile_loads);
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();   // ... for every wave; the buffer of tile it - 1 is free
+      // Issue priority among the waves sharing a SIMD (two workgroups per CU): a wave's
+      // admission step (ballots, staging writes, list flushes), which ends at the next
+      // tile barrier that the other waves of its workgroup wait on, goes before another
+      // wave's scoring (2 over 1), and the scoring before the row loads of the next tile
+      // (0).  Timed at 128K: 2% faster than equal priorities, identical index sets.
+      __builtin_amdgcn_s_setprio(0);
       const int nxt = cur == 0 ? kBufs - 1 : cur - 1;   // (it + kBufs - 1) % kBufs
       if (it + kBufs - 1 < n_tiles) issue_tile(s0 + (kBufs - 1) * kTileKeys, nxt);
 
+      __builtin_amdgcn_s_setprio(1);
       Op<DT> Bk[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) Bk[kb] = load_op_tile<DT>(ktile[cur], kb * 16 + (lane & 15), g);
@@ -1160,6 +1167,7 @@ void indexer_topk_kernel(FusedParams P) {
       }
       float sc[TW];
       tile_scores<DT, HB, TW>(A, Bk, W, sc);
+      __builtin_amdgcn_s_setprio(2);
       // Admission: val > theta_f is key > theta (the order-key map is strictly increasing
       // on floats with -0 = +0).  Positions are checked only in a tile that crosses a
       // token's causal edge or the segment end (a separate copy of the loop body, so the
@@ -1196,6 +1204,7 @@ void indexer_topk_kernel(FusedParams P) {
       cur = cur + 1 == kBufs ? 0 : cur + 1;
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // finalize this wave's rows
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt)
