@@ -352,14 +352,22 @@ void mla_attn_kernel(MlaParams P) {
 // buffer that the unchanged QK and PV code reads.  The scale of key s factors out of its
 // dot products: it multiplies the key's score, and the key's probability enters the value
 // product as p * scale (the denominator l sums p).
-template <bool SPLIT, int NB, bool KV8>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NB == 2 ? 2 : 1)))
+//
+// NQ = queries per workgroup that share one idx row (the MTP draft queries of a sequence,
+// idx_q_stride 0): 4 NQ waves, four per query.  The rows of a block are gathered once, by
+// the four waves of query slot 0, and every query's waves compute from the same buffers;
+// with NQ = 2 the two queries' chains share each SIMD (two waves per SIMD) instead of
+// running in two workgroups that gather the same rows.
+template <bool SPLIT, int NB, bool KV8, int NQ>
+__global__ __launch_bounds__(256 * NQ) __attribute__((amdgpu_waves_per_eu(NB == 2 || NQ == 2 ? 2 : 1)))
 void mla_attn32_kernel(MlaParams P) {
-  constexpr int NW = 4;
+  constexpr int NW = 4 * NQ;                     // waves per workgroup
+  constexpr int NWL = 4;                         // waves that gather the rows (query slot 0)
+  constexpr int NT = 64 * NW;                    // threads per workgroup
   constexpr int kDt = 16;                        // 16-dim output tiles per wave (256 dims)
   constexpr int kQSteps = 18;                    // 32-dim QK steps over the 576 latent dims
   constexpr int kDma = KV8 ? kDmaPerBlk2 / 2 : kDmaPerBlk2;   // 1 KB loads per block (18 / 36)
-  constexpr int kSlots = (kDma + NW - 1) / NW;   // per wave (5, 5, 4, 4 / 9)
+  constexpr int kSlots = (kDma + NWL - 1) / NWL; // per loading wave (5, 5, 4, 4 / 9)
   constexpr int kKeyAhead = 2 * NB - 2;          // idx blocks requested ahead of compute
   constexpr int kKeyBufs2 = NB == 2 ? 4 : 8;     // ring slots (j .. j + kKeyAhead in use)
   static_assert((NB & (NB - 1)) == 0 && kKeyBufs2 > kKeyAhead, "ring sizes");
@@ -373,6 +381,8 @@ void mla_attn32_kernel(MlaParams P) {
   const AttnArgs& a = P.a;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wv_id = uniform(tid >> 6);
+  const int qs = wv_id >> 2;                     // query slot
+  const int wq = wv_id & 3;                      // wave within the query
   const int hpq = a.H / 16;                      // head tiles per query (1 or 2)
   const int ng = P.n_groups;
   int grp;
@@ -382,12 +392,13 @@ void mla_attn32_kernel(MlaParams P) {
     grp = (xcd < rem) ? xcd * (per + 1) + jj : rem * (per + 1) + (xcd - rem) * per + jj;
   }
   const int split = blockIdx.y;
-  const int b = grp / a.Lq;
-  const int i = grp - b * a.Lq;                  // one query per workgroup
-  const int ht = wv_id % hpq;                    // head tile
-  const int ds = wv_id / hpq;                    // sub-block scored, value half accumulated
-  const bool wave_active = wv_id < 2 * hpq;
-  const int partner = ds == 0 ? wv_id + hpq : wv_id - hpq;
+  const int gps = a.Lq / NQ;                     // query groups per sequence
+  const int b = grp / gps;
+  const int i = (grp - b * gps) * NQ + qs;       // this wave's query
+  const int ht = wq % hpq;                       // head tile
+  const int ds = wq / hpq;                       // sub-block scored, value half accumulated
+  const bool wave_active = wq < 2 * hpq;
+  const int partner = 4 * qs + (ds == 0 ? wq + hpq : wq - hpq);   // wave index
   const int32_t* idx_row = a.idx_q_stride ? a.idx + (size_t)b * a.Lq * a.idx_q_stride + (size_t)i * a.idx_q_stride
                                           : a.idx + (size_t)b * a.topk;
   const int n_blk_total = (a.topk + kBlk2 - 1) / kBlk2;
@@ -401,7 +412,7 @@ void mla_attn32_kernel(MlaParams P) {
   // DMA target of block t's rows (buffer t % NB), and the bf16 block the math reads
   auto dma_buf = [&](int buf) { return lrows + buf * (KV8 ? kStgBytes : kBlk2Bytes); };
   auto math_buf = [&](int buf) -> const uint8_t* { return KV8 ? lrows + NB * kStgBytes : lrows + buf * kBlk2Bytes; };
-  const int my_loads = KV8 ? (wv_id + (kSlots - 1) * NW < kDma ? kSlots : kSlots - 1) + 1 : kSlots;
+  const int my_loads = qs != 0 ? 0 : KV8 ? (wq + (kSlots - 1) * NWL < kDma ? kSlots : kSlots - 1) + 1 : kSlots;
 
   // idx entries of the t-th block of this range into ring slot t % 4 (lanes 0..31; every
   // wave issues the same load); positions past topk are -1
@@ -413,16 +424,17 @@ void mla_attn32_kernel(MlaParams P) {
       else slot[lane] = -1;
     }
   };
-  // the block's 32 latent rows.  bf16: this wave loads key group wv_id (rows 8 wv_id +
-  // lane / 8) in the layout above, nine segment loads per block.  E4M3: the code rows land
-  // unswizzled at r * 576 (36 chunks per row) in 1 KB pieces, for the conversion to bf16.
+  // the block's 32 latent rows, loaded by the waves of query slot 0.  bf16: wave wq loads
+  // key group wq (rows 8 wq + lane / 8) in the layout above, nine segment loads per block.
+  // E4M3: the code rows land unswizzled at r * 576 (36 chunks per row) in 1 KB pieces, for
+  // the conversion to bf16.
   constexpr int kRowChunks = KV8 ? kChunks / 2 : kChunks;
   int dma_row[KV8 ? kSlots : 1];
   uint32_t dma_off[KV8 ? kSlots : 1];
   if constexpr (KV8) {
 #pragma unroll
     for (int u = 0; u < kSlots; ++u) {
-      const int piece = (wv_id + u * NW) * 64 + lane;
+      const int piece = (wq + u * NWL) * 64 + lane;
       const int r = min(piece / kRowChunks, kBlk2 - 1);   // loads past the block are skipped
       dma_row[u] = r;
       dma_off[u] = 16 * (piece - r * kRowChunks);
@@ -436,6 +448,7 @@ void mla_attn32_kernel(MlaParams P) {
   auto issue_rows = [&](int t, int buf, auto u0c, auto u1c) {
     constexpr int u0 = decltype(u0c)::value, u1 = decltype(u1c)::value;
     const int* slot = &keyring[t & (kKeyBufs2 - 1)][0];
+    if (qs != 0) return;                             // wave-uniform
     if constexpr (KV8) {
       if constexpr (u0 == 0) {
         if (lane < kBlk2) {
@@ -448,17 +461,17 @@ void mla_attn32_kernel(MlaParams P) {
       for (int u = u0; u < u1; ++u) key[u - u0] = slot[dma_row[u]];
 #pragma unroll
       for (int u = u0; u < u1; ++u) {
-        if (wv_id + u * NW < kDma) {                     // wave-uniform
+        if (wq + u * NWL < kDma) {                       // wave-uniform
           const uint32_t kk = (uint32_t)key[u - u0] < (uint32_t)a.Lk ? (uint32_t)key[u - u0] : 0u;
-          dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(dma_buf(buf) + (wv_id + u * NW) * 1024));
+          dma_16(kvbase + (uint64_t)kk * row_bytes32 + dma_off[u], lds_offset(dma_buf(buf) + (wq + u * NWL) * 1024));
         }
       }
     } else {
       if constexpr (u0 == 0) {
-        const uint32_t key = (uint32_t)slot[8 * wv_id + dr];
+        const uint32_t key = (uint32_t)slot[8 * wq + dr];
         row_src = kvbase + (uint64_t)(key < (uint32_t)a.Lk ? key : 0u) * row_bytes32 + dchunk;   // invalid: masked later
       }
-      dma_group_segs<u0, u1>(row_src, lds_offset(dma_buf(buf) + wv_id * kGroupBytes));
+      dma_group_segs<u0, u1>(row_src, lds_offset(dma_buf(buf) + wq * kGroupBytes));
     }
   };
   using C0 = Phase<0>;
@@ -534,8 +547,8 @@ void mla_attn32_kernel(MlaParams P) {
       const uint8_t* stg = dma_buf(buf);
       uint8_t* dst = lrows + NB * kStgBytes;
 #pragma unroll
-      for (int u = 0; u < (kStgBytes / 16 + 255) / 256; ++u) {
-        const int pc = tid + 256 * u;
+      for (int u = 0; u < (kStgBytes / 16 + NT - 1) / NT; ++u) {
+        const int pc = tid + NT * u;
         if (pc < kStgBytes / 16) {
           const int r = pc / kRowChunks, c = pc - r * kRowChunks;
           const i32x4 w = *reinterpret_cast<const i32x4*>(stg + 16 * pc);
@@ -822,6 +835,8 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   if (idx_q_stride == 0 && !p.k32) {  // queries of a sequence share one row: batch them per workgroup
     p.nq = Lq;
     while (p.nq > 1 && (p.nq * (H / 16) * 2 > 8 || Lq % p.nq)) --p.nq;
+  } else if (idx_q_stride == 0 && Lq % 2 == 0 && (int64_t)B * (Lq / 2) <= 256) {
+    p.nq = 2;               // pairs of queries gather their shared rows once (four-buffer grid)
   }
   // each wave holds 16 heads x 256 value dims; at most 8 waves per workgroup
   p.dvs = 2;
@@ -834,7 +849,9 @@ static MlaPlan plan_mla(int B, int Lq, int k, int H, int64_t idx_q_stride) {
   p.deep = p.k32 && p.n_groups <= 256;
   const int target = p.deep ? 256 : 1024;
   if (p.n_groups < target) {
-    split = (target + p.n_groups - 1) / p.n_groups;
+    // paired queries: at most one grid of 256 workgroups, so the partials (128 KB per
+    // workgroup at 32 heads) stay within 32 MiB
+    split = p.nq == 2 ? target / p.n_groups : (target + p.n_groups - 1) / p.n_groups;
     if (split > kMaxSplit) split = kMaxSplit;
     if (split > n_blk) split = n_blk;
   }
@@ -876,19 +893,25 @@ hipError_t launch_sparse_attn(const AttnArgs& a, void* ws, size_t ws_bytes, hipS
   dim3 grid(pl.n_groups, pl.n_split);
   const bool split = pl.n_split > 1;
   if (a.kv8) {   // E4M3 latent rows: the 32-key kernel only (checked by the caller)
-    if (pl.deep) {
-      if (split) mla_attn32_kernel<true, 4, true><<<grid, 256, 0, s>>>(P);
-      else mla_attn32_kernel<false, 4, true><<<grid, 256, 0, s>>>(P);
+    if (pl.deep && pl.nq == 2) {
+      if (split) mla_attn32_kernel<true, 4, true, 2><<<grid, 512, 0, s>>>(P);
+      else mla_attn32_kernel<false, 4, true, 2><<<grid, 512, 0, s>>>(P);
+    } else if (pl.deep) {
+      if (split) mla_attn32_kernel<true, 4, true, 1><<<grid, 256, 0, s>>>(P);
+      else mla_attn32_kernel<false, 4, true, 1><<<grid, 256, 0, s>>>(P);
     } else {
-      if (split) mla_attn32_kernel<true, 2, true><<<grid, 256, 0, s>>>(P);
-      else mla_attn32_kernel<false, 2, true><<<grid, 256, 0, s>>>(P);
+      if (split) mla_attn32_kernel<true, 2, true, 1><<<grid, 256, 0, s>>>(P);
+      else mla_attn32_kernel<false, 2, true, 1><<<grid, 256, 0, s>>>(P);
     }
+  } else if (pl.k32 && pl.deep && pl.nq == 2) {
+    if (split) mla_attn32_kernel<true, 4, false, 2><<<grid, 512, 0, s>>>(P);
+    else mla_attn32_kernel<false, 4, false, 2><<<grid, 512, 0, s>>>(P);
   } else if (pl.k32 && pl.deep) {
-    if (split) mla_attn32_kernel<true, 4, false><<<grid, 256, 0, s>>>(P);
-    else mla_attn32_kernel<false, 4, false><<<grid, 256, 0, s>>>(P);
+    if (split) mla_attn32_kernel<true, 4, false, 1><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 4, false, 1><<<grid, 256, 0, s>>>(P);
   } else if (pl.k32) {
-    if (split) mla_attn32_kernel<true, 2, false><<<grid, 256, 0, s>>>(P);
-    else mla_attn32_kernel<false, 2, false><<<grid, 256, 0, s>>>(P);
+    if (split) mla_attn32_kernel<true, 2, false, 1><<<grid, 256, 0, s>>>(P);
+    else mla_attn32_kernel<false, 2, false, 1><<<grid, 256, 0, s>>>(P);
   } else if (pl.nw <= 4) {
     if (split) mla_attn_kernel<4, 2, 3, true, 2><<<grid, 256, 0, s>>>(P);
     else mla_attn_kernel<4, 2, 3, false, 2><<<grid, 256, 0, s>>>(P);

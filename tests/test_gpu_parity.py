@@ -612,6 +612,43 @@ def test_mla_fp8_latent_equals_bf16_on_decoded_rows(B, Lq, Lk, k):
     assert torch.equal(got, ref)
 
 
+
+# Draft queries sharing one idx row per sequence (idx_q_stride 0, the MTP case).  With an
+# even number per sequence and at most 256 pairs, two queries share a workgroup and the
+# rows it gathers (eight waves); an odd number keeps one query per workgroup.  Against the
+# oracle on bf16 rows, and on FP8 latent rows bit-exact against the bf16 path on the
+# decoded rows (power-of-two scales, as in the test above).
+@pytest.mark.parametrize("B,Lq,Lk,k,H", [
+    (3, 4, 3000, 2048, 32),     # paired: 6 groups, keys split 8 ways
+    (3, 3, 3000, 2048, 32),     # odd count: one query per workgroup
+    (127, 2, 700, 300, 32),     # paired: 127 groups, split rounded down to 2
+    (2, 4, 900, 520, 16),       # paired, 16 heads: two waves of each query idle
+])
+def test_mla_shared_row_queries(B, Lq, Lk, k, H):
+    cfg = synth.get_config("decode200k", L=Lk, B=B, H=H)
+    lay = synth.attention_inputs(cfg, layer=1, device=DEV, Lq=Lq)
+    rng = np.random.default_rng(10 * B + Lq)
+    idx = np.stack([np.sort(rng.permutation(Lk)[:k]) for _ in range(B)])[:, None].astype(np.int32)
+    idx[0, 0, ::13] = -1
+    idx[-1, 0, 5::17] = Lk + 3                     # out of range: skipped
+    idx_t = torch.from_numpy(idx).to(DEV)
+    out, lse = dsa.sparse_attn(lay, idx_t, idx_q_stride=0, return_lse=True,
+                               out=poisoned((B, Lq, H, 512), torch.float32))
+    assert all_written(out)
+    ol_idx = idx.copy()
+    ol_idx[ol_idx >= Lk] = -1
+    for b in sorted({0, B // 2, B - 1}):
+        _attn_check(lay, None, out, lse, list(range(Lq)), b=b, idx_rows_override=np.repeat(ol_idx[b], Lq, axis=0))
+    assert torch.equal(dsa.sparse_attn(lay, idx_t, idx_q_stride=0), out.to(torch.bfloat16))
+    codes = torch.from_numpy((rng.integers(0, 0x41, (B, Lk, 576)) | (rng.integers(0, 2, (B, Lk, 576)) << 7))
+                             .astype(np.uint8))
+    scale = torch.from_numpy(2.0 ** rng.integers(-3, 2, (B, Lk)).astype(np.float32))
+    dec = (codes.view(torch.float8_e4m3fn).float() * scale[..., None]).to(torch.bfloat16)
+    got = dsa.sparse_attn(dict(lay, kv=codes.to(DEV), kv_scale=scale.to(DEV)), idx_t, idx_q_stride=0,
+                          out_dtype=torch.float32)
+    ref = dsa.sparse_attn(dict(lay, kv=dec.to(DEV)), idx_t, idx_q_stride=0, out_dtype=torch.float32)
+    assert torch.equal(got, ref)
+
 def test_tiny_mha_fp32_attention_parity():
     cfg = synth.get_config("tiny")
     ind = synth.indexer_inputs(cfg, device=DEV)
