@@ -7,7 +7,10 @@
 // compressed KV + 64-d RoPE key); K is the whole row, V its first 512 dims, and the
 // query heads are already absorbed to 576-d.
 //
-// MLA kernel: one workgroup per (query row group, key split); a row group is the nq
+// Two MLA kernels: mla_attn32_kernel (32-key blocks, below) serves 16 and 32 heads;
+// mla_attn_kernel (16-key blocks, first) serves 48 and 64 heads.
+//
+// mla_attn_kernel: one workgroup per (query row group, key split); a row group is the nq
 // queries that share one idx row (nq = 1, or the MTP draft queries).  Each wave owns
 // 16 heads of one query.  Keys are processed in blocks of 16 selected positions: the
 // block's 16 latent rows (18 KB) are gathered straight into LDS with direct-to-LDS loads
@@ -823,7 +826,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 struct MlaPlan {
   int nq, dvs, nw, n_groups, n_split, bps;
-  bool k32;           // mla_attn32_kernel (32-key blocks, one query per workgroup)
+  bool k32;           // mla_attn32_kernel (32-key blocks, one query or one pair sharing an idx row per workgroup)
   bool deep;          // its four-buffer form: one workgroup per CU, three blocks in flight
   size_t off_o, off_ml, total;
 };
