@@ -497,6 +497,38 @@ def test_mla_decode_split_and_mtp_shared_rows():
                     idx_rows_override=np.repeat(shared[b][None], 4, axis=0))
 
 
+
+# The other direction of the attention check: the oracle's own index sets (exact top-k of
+# its fp64 scores) fed to dsa_sparse_attn, against the oracle's attention over the same
+# sets.  Prefill (bf16 indexer inputs, the two-buffer kernel) and decode (one query per
+# sequence, keys split over workgroups).  Rows not checked keep the GPU's index rows.
+@pytest.mark.parametrize("case", ["prefill", "decode"])
+def test_attention_on_oracle_index_sets(case):
+    if case == "prefill":
+        L, k, B = 1500, 256, 1
+        cfg = _cfg("bf16", L, k)
+        rows = [0, 255, 256, 900, 1499]
+    else:
+        L, k, B = 3000, 2048, 2
+        cfg = synth.get_config("decode200k", L=L, B=B)
+        rows = [0]
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    lay = synth.attention_inputs(cfg, layer=2, device=DEV)
+    Lq = cfg.Lq
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind)).cpu().numpy()
+    ora = indexer_to_oracle(ind)
+    ref_idx = {}
+    for b in range(B):
+        sc = _oracle_rows(ora, b, rows, Lq, L)
+        nv = [L - Lq + r + 1 for r in rows]
+        ref_idx[b] = oracle.topk_rows(sc, nv, k)
+        idx[b][rows] = ref_idx[b]
+    out, lse = dsa.sparse_attn(lay, torch.from_numpy(idx).to(DEV), return_lse=True,
+                               out=poisoned((B, Lq, cfg.H, cfg.Dv), torch.float32))
+    assert all_written(out)
+    for b in range(B):
+        _attn_check(lay, None, out, lse, rows, b=b, idx_rows_override=ref_idx[b])
+
 # 48 and 64 query heads take the 16-key kernel (up to eight waves per workgroup): prefill
 # rows, decode rows split over several workgroups, and MTP draft queries sharing one row
 # (batched per workgroup), against the oracle with the GPU's index rows.
