@@ -185,6 +185,37 @@ def test_indexer_scores_parity(dtype, L, Lq, B):
     print(f"[scores] {dtype}: worst error / element bound = {worst:.3f}")
 
 
+
+# Indexer head counts below 64 (one, two and three 16-head blocks; the bf16 score schedule
+# pairs dot products, and with an odd count a pair spans two key blocks): materialised
+# scores within the element bound, the fused index sets against the oracle's exact top-k
+# within the tolerance band, and the fused kernel equal to the top-k of the materialised
+# scores.  Prefill rows and a few-query (chunk list) call.
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("H_I", [16, 32, 48])
+@pytest.mark.parametrize("Lq,Lk", [(700, 700), (2, 20000)])
+def test_indexer_fewer_heads(dtype, H_I, Lq, Lk):
+    k = 128
+    cfg = _cfg(dtype, Lk, k, Lq=Lq, B=1, H_I=H_I)
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    sc = dsa.indexer_scores(ind["q"], ind["k"], ind["w"], **_ind_args(ind))
+    idx = dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, **_ind_args(ind))
+    nv = torch.arange(Lq, device=DEV, dtype=torch.int32) + (Lk - Lq + 1)
+    assert torch.equal(idx[0], dsa.topk(sc[0], k, n_valid=nv))
+    ora = indexer_to_oracle(ind)
+    ora["dtype"] = dtype
+    rows = sorted({0, Lq // 2, Lq - 1})
+    ref = _oracle_rows(ora, 0, rows, Lq, Lk)
+    g = sc[0].cpu().numpy()[rows].astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isneginf(g), np.isneginf(ref))
+    bound = _score_bounds(ora, 0, rows, Lq, Lk)
+    assert np.all(np.abs(g[fin] - ref[fin]) <= bound[fin])
+    nvr = [Lk - Lq + r + 1 for r in rows]
+    ok, _, msg = index_sets_agree(idx.cpu().numpy()[0][rows], oracle.topk_rows(ref, nvr, k), ref, nvr, k,
+                                  1e-3 if dtype == "bf16" else 2e-2)
+    assert ok, msg
+
 # ---------------------------------------------------------------------------
 # fused indexer + top-k
 # ---------------------------------------------------------------------------
