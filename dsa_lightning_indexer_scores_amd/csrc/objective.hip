@@ -22,7 +22,8 @@
 // softmax, the loss and g = pi - pbar follow.  Pass 2 rescores each tile, forms c (rounded
 // to bf16 for the matrix cores), accumulates dw in fp32 and runs two more contractions:
 // dq (heads x dims over the tile's keys) in registers, and dk (keys x dims over the heads),
-// added to the global dk with fp32 atomics.
+// added in 64-bit fixed point to a workspace (dk_fix_add_kernel adds it to dk), so that dk
+// does not depend on the order in which rows arrive.
 #include "dsa_common.hpp"
 #include "dsa_launch.hpp"
 #include "mla_blocks.hpp"
@@ -75,7 +76,15 @@ void attn_probs32_kernel(AttnProbsArgs a) {
   const int ht = wv_id % hpq;
   const int ds = wv_id / hpq;
   const bool wave_active = wv_id < 2 * hpq;
-  const int r = blockIdx.x;                        // query row b * Lq + i
+  int r;                                           // query row b * Lq + i
+  {
+    // contiguous query ranges per XCD: neighbouring queries, whose index rows overlap,
+    // share an L2 (16K, 4 layers: 10.26 -> 10.15 ms)
+    const int nr = a.B * a.Lq;
+    const int bid = blockIdx.x, xcd = bid & 7, jj = bid >> 3;
+    const int per = nr >> 3, rem = nr & 7;
+    r = (xcd < rem) ? xcd * (per + 1) + jj : rem * (per + 1) + (xcd - rem) * per + jj;
+  }
   const int b = r / a.Lq;
   // the idx row of (b, i) as in dsa_sparse_attn: one per query, or one per sequence
   const int32_t* idx_row = a.idx_q_stride ? a.idx + (size_t)r * a.idx_q_stride : a.idx + (size_t)b * a.k;
