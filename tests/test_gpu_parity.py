@@ -560,6 +560,48 @@ def test_attention_on_oracle_index_sets(case):
     for b in range(B):
         _attn_check(lay, None, out, lse, rows, b=b, idx_rows_override=ref_idx[b])
 
+
+def test_decode_step_graph_replays_match_eager():
+    """A decode step (fused indexer + top-k, then four layers of sparse attention, one
+    workspace) captured as a graph: every kernel is a stream launch (no copies, no memsets,
+    no host synchronisation), so each replay, with eager steps in between, reproduces the
+    eager step's index rows and outputs bit for bit."""
+    cfg = synth.get_config("decode200k", L=20000, B=4)
+    k = cfg.topk
+    ind = synth.indexer_inputs(cfg, device=DEV)
+    layers = [synth.attention_inputs(cfg, layer=l, device=DEV) for l in range(cfg.n_layers)]
+    idx = torch.empty((cfg.B, 1, k), dtype=torch.int32, device=DEV)
+    outs = [torch.empty((cfg.B, 1, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=DEV) for _ in layers]
+    ws = dsa.Workspace()
+
+    def step():
+        dsa.indexer_topk(ind["q"], ind["k"], ind["w"], k, ws=ws, out=idx, **_ind_args(ind))
+        for lay, o in zip(layers, outs):
+            dsa.sparse_attn(lay, idx, ws=ws, out=o)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref_idx, ref_outs = idx.clone(), [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        idx.fill_(-7)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx)
+        assert all(torch.equal(o, r) for o, r in zip(outs, ref_outs))
+        step()                                   # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx)
+
 # 48 and 64 query heads take the 16-key kernel (up to eight waves per workgroup): prefill
 # rows, decode rows split over several workgroups, and MTP draft queries sharing one row
 # (batched per workgroup), against the oracle with the GPU's index rows.
