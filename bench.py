@@ -31,6 +31,10 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0                 # MI355X HBM3E
 MFMA_PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+# what bounds each compute dtype of the path, and its datasheet peak: fp8 and bf16 run on the
+# matrix cores; the fp32 reference-size path (the Tiny config) runs on the vector ALU, whose
+# fp32 peak is 256 CUs x 4 SIMDs x 64 flops per clock (32 FMA lanes) x 2.4 GHz = 157.3 TFLOP/s
+COMPUTE_PEAK = {"fp8": ("mfma", 5000.0), "bf16": ("mfma", 2500.0), "f32": ("alu", 157.3)}
 
 # Memory traffic per launch comes from two rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE)
 # summarised under profiles/.  Both count the L2's requests to the memory side (its misses
@@ -371,7 +375,8 @@ def main():
     ind = synth.indexer_inputs(cfg, device=dev)
     layers = [synth.attention_inputs(cfg, layer=l, device=dev) for l in range(cfg.n_layers)]
     idx = torch.empty((cfg.B, cfg.Lq, k), dtype=torch.int32, device=dev)
-    outs = [torch.empty((cfg.B, cfg.Lq, cfg.H, cfg.Dv), dtype=torch.bfloat16, device=dev)
+    out_dtype = torch.float32 if cfg.attn_dtype == "f32" else torch.bfloat16
+    outs = [torch.empty((cfg.B, cfg.Lq, cfg.H, cfg.Dv), dtype=out_dtype, device=dev)
             for _ in range(cfg.n_layers)]
     ws = dsa.Workspace()
     torch.cuda.synchronize()
@@ -420,13 +425,15 @@ def main():
     attn_tfs = attn_flop / (attn_ms * 1e-3) / 1e12
     # gathered latent rows (algorithmic bytes of the attention: each selected row once per query)
     attn_gather_gb = sel * cfg.Dqk * 2 / 1e9
+    idx_bound, idx_peak = COMPUTE_PEAK[cfg.idx_dtype]
+    attn_bound, attn_peak = COMPUTE_PEAK[cfg.attn_dtype]
     kernels = {
         "indexer_topk": {"ms": round(idx_ms, 4), "algorithmic_tflop": round(idx_flop / 1e12, 3),
-                         "tflops": round(idx_tfs, 1), "bound": "mfma", "peak_tflops": MFMA_PEAK_TFLOPS[cfg.idx_dtype],
-                         "frac": round(idx_tfs / MFMA_PEAK_TFLOPS[cfg.idx_dtype], 4)},
+                         "tflops": round(idx_tfs, 1), "bound": idx_bound, "peak_tflops": idx_peak,
+                         "frac": round(idx_tfs / idx_peak, 4)},
         "sparse_attn": {"ms_per_layer": round(attn_ms, 4), "algorithmic_tflop": round(attn_flop / 1e12, 3),
-                        "tflops": round(attn_tfs, 1), "bound": "mfma", "peak_tflops": MFMA_PEAK_TFLOPS["bf16"],
-                        "frac": round(attn_tfs / MFMA_PEAK_TFLOPS["bf16"], 4),
+                        "tflops": round(attn_tfs, 1), "bound": attn_bound, "peak_tflops": attn_peak,
+                        "frac": round(attn_tfs / attn_peak, 4),
                         "gathered_gb": round(attn_gather_gb, 2),
                         "gather_gbs": round(attn_gather_gb / (attn_ms * 1e-3), 1)},
     }
@@ -447,14 +454,25 @@ def main():
         del lay8
         torch.cuda.empty_cache()
     # roofline object: the kernel with the larger share of the step
-    if idx_ms >= attn_ms * cfg.n_layers:
-        roof = {"kernel": "indexer_topk", "bound": "mfma", "achieved": round(idx_tfs, 2),
-                "peak": MFMA_PEAK_TFLOPS[cfg.idx_dtype], "unit": "TFLOP/s",
-                "frac": round(idx_tfs / MFMA_PEAK_TFLOPS[cfg.idx_dtype], 4)}
+    if cfg.Lq < 16:
+        # few queries per sequence (decode): no key reuse, both parts stream bytes from HBM
+        # (the k^I cache with its scales; the gathered latent rows of each layer)
+        kI_gb = cfg.B * L * (cfg.d_I * (1 if cfg.idx_dtype == "fp8" else 2 if cfg.idx_dtype == "bf16" else 4)
+                             + (4 if cfg.idx_dtype == "fp8" else 0)) / 1e9
+        idx_gbs, attn_gbs = kI_gb / (idx_ms * 1e-3), attn_gather_gb / (attn_ms * 1e-3)
+        kernels["indexer_topk"].update({"hbm_gb": round(kI_gb, 3), "hbm_gbs": round(idx_gbs, 1)})
+        if idx_ms >= attn_ms * cfg.n_layers:
+            roof = {"kernel": "indexer_topk", "bound": "hbm", "achieved": round(idx_gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(idx_gbs / HBM_PEAK_GBS, 4)}
+        else:
+            roof = {"kernel": "sparse_attn", "bound": "hbm", "achieved": round(attn_gbs, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
+    elif idx_ms >= attn_ms * cfg.n_layers:
+        roof = {"kernel": "indexer_topk", "bound": idx_bound, "achieved": round(idx_tfs, 2),
+                "peak": idx_peak, "unit": "TFLOP/s", "frac": round(idx_tfs / idx_peak, 4)}
     else:
-        roof = {"kernel": "sparse_attn", "bound": "mfma", "achieved": round(attn_tfs, 2),
-                "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                "frac": round(attn_tfs / MFMA_PEAK_TFLOPS["bf16"], 4)}
+        roof = {"kernel": "sparse_attn", "bound": attn_bound, "achieved": round(attn_tfs, 2),
+                "peak": attn_peak, "unit": "TFLOP/s", "frac": round(attn_tfs / attn_peak, 4)}
     # measured HBM bytes per launch (counters), only for the workload they were taken on
     roof["traffic"] = recorded_traffic(roof["kernel"]) if cfg.name == "prefill128k" else None
 
@@ -472,7 +490,7 @@ def main():
         "dtype": "fp8-indexer/bf16-attention" if cfg.idx_dtype == "fp8" else cfg.idx_dtype,
         "data": "synthetic (seeded Gaussian, 5% planted 3x keys)",
         "config": {"workload": cfg.name, "L": L, "B": cfg.B, "topk": k, "H_I": cfg.H_I, "d_I": cfg.d_I,
-                   "indexer_dtype": cfg.idx_dtype, "attention": f"MLA {cfg.H} heads, {cfg.Dqk}/{cfg.Dv}",
+                   "indexer_dtype": cfg.idx_dtype, "attention": f"{cfg.attn.upper()} {cfg.H} heads, {cfg.Dqk}/{cfg.Dv}",
                    "group": "1 Full + 3 Shared", "parallelism": "single GPU"},
         "kernels": kernels,
         "roofline": roof,
