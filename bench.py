@@ -308,6 +308,32 @@ def summarize_pmc(csvs, kernel, template, workload, command):
     return "\n".join(lines)
 
 
+def main_roofline(cfg, L, idx_ms, attn_ms, idx_flop, attn_flop, attn_gather_gb):
+    """Roofline object of the main line: the kernel with the larger share of the step
+    (the indexer once against the attention of every layer), priced by what bounds it.
+    With fewer than 16 queries per sequence (decode) neither part reuses keys, so both are
+    priced in HBM bytes: the k^I cache with its scales, the gathered latent rows.  Otherwise
+    both are dense contractions priced against the peak of their arithmetic type.  Returns
+    (roofline, extra indexer fields or None)."""
+    idx_tfs = idx_flop / (idx_ms * 1e-3) / 1e12
+    attn_tfs = attn_flop / (attn_ms * 1e-3) / 1e12
+    idx_first = idx_ms >= attn_ms * cfg.n_layers
+    if cfg.Lq < 16:
+        code_bytes = {"fp8": 1, "bf16": 2, "f32": 4}[cfg.idx_dtype]
+        kI_gb = cfg.B * L * (cfg.d_I * code_bytes + (4 if cfg.idx_dtype == "fp8" else 0)) / 1e9
+        idx_gbs, attn_gbs = kI_gb / (idx_ms * 1e-3), attn_gather_gb / (attn_ms * 1e-3)
+        name, gbs = ("indexer_topk", idx_gbs) if idx_first else ("sparse_attn", attn_gbs)
+        roof = {"kernel": name, "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        return roof, {"hbm_gb": round(kI_gb, 3), "hbm_gbs": round(idx_gbs, 1)}
+    if idx_first:
+        (bound, peak), name, tfs = COMPUTE_PEAK[cfg.idx_dtype], "indexer_topk", idx_tfs
+    else:
+        (bound, peak), name, tfs = COMPUTE_PEAK[cfg.attn_dtype], "sparse_attn", attn_tfs
+    return {"kernel": name, "bound": bound, "achieved": round(tfs, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(tfs / peak, 4)}, None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -454,25 +480,9 @@ def main():
         del lay8
         torch.cuda.empty_cache()
     # roofline object: the kernel with the larger share of the step
-    if cfg.Lq < 16:
-        # few queries per sequence (decode): no key reuse, both parts stream bytes from HBM
-        # (the k^I cache with its scales; the gathered latent rows of each layer)
-        kI_gb = cfg.B * L * (cfg.d_I * (1 if cfg.idx_dtype == "fp8" else 2 if cfg.idx_dtype == "bf16" else 4)
-                             + (4 if cfg.idx_dtype == "fp8" else 0)) / 1e9
-        idx_gbs, attn_gbs = kI_gb / (idx_ms * 1e-3), attn_gather_gb / (attn_ms * 1e-3)
-        kernels["indexer_topk"].update({"hbm_gb": round(kI_gb, 3), "hbm_gbs": round(idx_gbs, 1)})
-        if idx_ms >= attn_ms * cfg.n_layers:
-            roof = {"kernel": "indexer_topk", "bound": "hbm", "achieved": round(idx_gbs, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(idx_gbs / HBM_PEAK_GBS, 4)}
-        else:
-            roof = {"kernel": "sparse_attn", "bound": "hbm", "achieved": round(attn_gbs, 1),
-                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4)}
-    elif idx_ms >= attn_ms * cfg.n_layers:
-        roof = {"kernel": "indexer_topk", "bound": idx_bound, "achieved": round(idx_tfs, 2),
-                "peak": idx_peak, "unit": "TFLOP/s", "frac": round(idx_tfs / idx_peak, 4)}
-    else:
-        roof = {"kernel": "sparse_attn", "bound": attn_bound, "achieved": round(attn_tfs, 2),
-                "peak": attn_peak, "unit": "TFLOP/s", "frac": round(attn_tfs / attn_peak, 4)}
+    roof, idx_hbm = main_roofline(cfg, L, idx_ms, attn_ms, idx_flop, attn_flop, attn_gather_gb)
+    if idx_hbm is not None:
+        kernels["indexer_topk"].update(idx_hbm)
     # measured HBM bytes per launch (counters), only for the workload they were taken on
     roof["traffic"] = recorded_traffic(roof["kernel"]) if cfg.name == "prefill128k" else None
 

@@ -55,3 +55,28 @@ def test_counter_summary_leaves_out_dispatches_that_do_no_work(tmp_path):
     fields = dict(l.split(":", 1) for l in text.splitlines() if ":" in l and not l.startswith("#"))
     assert int(fields["dispatches"]) == 2 and int(fields["launches"]) == 1
     assert int(fields["traffic_bytes_per_launch"]) == 4000 * 1024 * 2 + 100 * 1024
+
+
+def test_main_roofline_follows_the_workload():
+    import synth
+    # prefill128k: the attention of four layers outweighs the indexer; bf16 MFMA peak
+    cfg = synth.get_config("prefill128k")
+    roof, extra = bench.main_roofline(cfg, cfg.L, 55.0, 28.0, 140.7e12, 18.5e12, 306.8)
+    assert (roof["kernel"], roof["bound"], roof["unit"], roof["peak"]) == ("sparse_attn", "mfma", "TFLOP/s", 2500.0)
+    assert abs(roof["achieved"] - 18.5e12 / 28e-3 / 1e12) < 0.01 and extra is None
+    # an indexer that outweighs the layers is priced on its own type's peak (fp8)
+    roof, _ = bench.main_roofline(cfg, cfg.L, 200.0, 28.0, 140.7e12, 18.5e12, 306.8)
+    assert (roof["kernel"], roof["bound"], roof["peak"]) == ("indexer_topk", "mfma", 5000.0)
+    # decode: HBM bytes, the k^I codes plus one fp32 scale per key
+    cfg = synth.get_config("decode200k")
+    roof, extra = bench.main_roofline(cfg, cfg.L, 0.35, 0.046, 2.1e11, 9e9, 0.151)
+    kI = 64 * 200001 * (128 + 4) / 1e9
+    assert (roof["kernel"], roof["bound"], roof["unit"], roof["peak"]) == ("indexer_topk", "hbm", "GB/s", 8000.0)
+    assert abs(roof["achieved"] - kI / 0.35e-3) < 0.1 and extra["hbm_gb"] == round(kI, 3)
+    roof, _ = bench.main_roofline(cfg, cfg.L, 0.10, 0.046, 2.1e11, 9e9, 0.151)
+    assert (roof["kernel"], roof["bound"]) == ("sparse_attn", "hbm")
+    assert abs(roof["achieved"] - 0.151 / 0.046e-3) < 0.1
+    # fp32 MHA: the vector ALU peak
+    cfg = synth.get_config("tiny")
+    roof, _ = bench.main_roofline(cfg, cfg.L, 0.01, 0.06, 1e9, 2e9, 0.01)
+    assert (roof["kernel"], roof["bound"], roof["peak"]) == ("sparse_attn", "alu", 157.3)
