@@ -80,3 +80,14 @@ def test_main_roofline_follows_the_workload():
     cfg = synth.get_config("tiny")
     roof, _ = bench.main_roofline(cfg, cfg.L, 0.01, 0.06, 1e9, 2e9, 0.01)
     assert (roof["kernel"], roof["bound"], roof["peak"]) == ("sparse_attn", "alu", 157.3)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import json, os, subprocess, sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for argv, env in ((["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), *argv], capture_output=True, text=True,
+                           env={**os.environ, **env}, timeout=120)
+        assert r.returncode == 2
+        msg = json.loads(r.stdout.strip().splitlines()[-1])
+        assert "one GPU" in msg["error"]
